@@ -1,0 +1,227 @@
+/*
+ * eagletree.h -- C ABI of libeagletree: the data-parallel core of EAGLE-2
+ * dynamic draft trees on one AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the method (the pages this library follows):
+ *   [P1] "EAGLE-2: Faster Inference of Language Models with Dynamic Draft
+ *        Trees", summary page (paperlayer.ai, arXiv 2406.16858v2):
+ *        s2.1 speculative sampling, s4.1 expansion phase, s4.2 reranking
+ *        phase, App. A implementation details.
+ *   [P2] "EAGLE-2: Dynamic Draft Trees" explainer (stable-lab specdec
+ *        notes): the path-product value equation, expand/rerank, and the
+ *        "Common misconception" chain example.
+ *   [P3] EAGLE notes (garden.houmin.site/infra/eagle), section "EAGLE 2 /
+ *        方法": Expand stage (threshold stop) and ReRank stage (shallower
+ *        node wins ties).
+ *   [P4] EAGLE-3 review (xllm-io paper-review), section 五: all reported
+ *        speedups are at temperature 0 (greedy decoding).
+ *
+ * One decode cycle of a batch of B independent sequences is:
+ *     et_draft_step(step = 1 .. D)   -- expand the tree layer by layer
+ *     et_rerank                      -- keep the global top-N nodes
+ *     et_tree_mask                   -- flatten: ancestor mask, depth, pos
+ *     et_tree_attention              -- tree-masked attention (verify)
+ *     et_accept                      -- greedy longest accepted path
+ * Between draft steps the caller runs its draft model on `next_tokens`
+ * and hands the resulting vocab logits to the next step.
+ *
+ * Conventions
+ *   - Every pointer argument named as device memory must be a device
+ *     pointer (e.g. torch.empty(..., device="cuda").data_ptr()).  The
+ *     library never allocates or frees device memory on these calls; the
+ *     caller owns every buffer, including the workspace.
+ *   - `stream` is a hipStream_t passed as void* (NULL = legacy default
+ *     stream).  All calls are asynchronous and stream-ordered; none of them
+ *     synchronises the host.  Host-side argument validation happens before
+ *     any launch; on failure nothing is launched.
+ *   - Return value: ET_OK (0) or a negative et_status; et_last_error()
+ *     gives a message for the calling thread.
+ *   - Device-side preconditions (not checked, documented instead): logits
+ *     are finite or -inf with at least one finite entry per row; no NaN;
+ *     n_kept / parent_slot / tokens are the values written by et_rerank.
+ *   - T = N + 1 tree slots per sequence: slot 0 is the root (the last
+ *     committed token), slots 1..n hold the kept draft tokens, slots
+ *     n+1..N are padding.  W = ceil(T / 64) mask words per slot.
+ *   - A plan + workspace pair carries the tree from et_draft_step(1)
+ *     through et_rerank of the same cycle; use one workspace per stream
+ *     that runs cycles concurrently.
+ */
+#ifndef EAGLETREE_H
+#define EAGLETREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ET_OK = 0,
+  ET_EINVAL = -1,        /* null pointer, shape, stride or range error      */
+  ET_EUNSUPPORTED = -2,  /* dtype, head_dim, top-k or size outside support  */
+  ET_ESTATE = -3,        /* calls out of order for this plan and workspace  */
+  ET_EHIP = -4           /* a HIP launch or runtime call failed             */
+} et_status;
+
+typedef enum { ET_F32 = 0, ET_BF16 = 1 } et_dtype;
+
+typedef void* et_stream_t;              /* a hipStream_t                    */
+typedef struct et_plan_s* et_plan_t;    /* opaque, host-side metadata only  */
+
+/* Shapes of one cycle.  Limits (ET_EUNSUPPORTED / ET_EINVAL otherwise):
+ *   1 <= batch <= 65535; 2 <= vocab <= 2^24; 1 <= topk <= 16;
+ *   1 <= depth <= 15; 1 <= budget_n <= 255 (so T <= 256, W <= 4);
+ *   expand_threshold >= 0 (0 disables the stop rule);
+ *   head_dim in {64, 128}; n_q_heads % n_kv_heads == 0;
+ *   1 <= n_kv_heads, n_q_heads / n_kv_heads <= 16; prefix_cap >= 1.
+ * topk is both the number of children drawn per expanded node and the
+ * number of nodes expanded per layer ([P1] s4.1: the k most valuable
+ * nodes of the current layer are expanded; [P3] Expand stage: each node
+ * contributes its top 2 children when k = 2). */
+typedef struct {
+  int32_t batch;            /* B independent sequences                     */
+  int32_t vocab;            /* V                                           */
+  int32_t topk;             /* k                                           */
+  int32_t depth;            /* D draft layers below the root               */
+  int32_t budget_n;         /* N draft tokens kept by the rerank           */
+  float expand_threshold;   /* nodes whose value is below it are not
+                               expanded ([P3] Expand stage)                */
+  int32_t logits_dtype;     /* et_dtype of draft and target logits         */
+  int32_t n_q_heads;        /* Hq                                          */
+  int32_t n_kv_heads;       /* Hkv (grouped-query attention, G = Hq/Hkv)   */
+  int32_t head_dim;         /* d                                           */
+  int32_t prefix_cap;       /* P_cap: allocated prefix length of the cache */
+  int32_t qkv_dtype;        /* et_dtype of q, K/V cache, tree K/V and out  */
+} et_config;
+
+/* Validate `cfg` and create a plan (host memory only).  *out receives the
+ * plan on success. */
+int et_plan_create(const et_config* cfg, et_plan_t* out);
+int et_plan_destroy(et_plan_t plan);
+
+/* Bytes of device workspace the plan needs (256-byte aligned base
+ * required).  The workspace holds the candidate pool, the frontier,
+ * per-chunk partial results and arrival counters. */
+size_t et_workspace_bytes(et_plan_t plan);
+
+/* Pool capacity per sequence: topk + (depth - 1) * topk^2 nodes. */
+int32_t et_pool_capacity(et_plan_t plan);
+
+/* Clear the workspace's arrival counters with a fill kernel on `stream`.
+ * Must run once after the workspace is allocated and before its first
+ * use; afterwards every call leaves the counters cleared again. */
+int et_workspace_init(et_plan_t plan, void* ws, et_stream_t stream);
+
+/* One expansion layer ([P1] s4.1; [P2] value equation; [P3] Expand).
+ *
+ * step 1 starts a new tree: the root of sequence b is root_tokens[b]
+ * (device int32 [B]) with value 1; its single frontier row is row 0.
+ * For step s in 1..D, frontier slot j of sequence b (j < frontier count
+ * F_b, in the order of the previous call's next_tokens) reads the vocab
+ * logits row at
+ *     logits + b * batch_stride + j * row_stride      (elements)
+ * (dtype = logits_dtype; rows j >= F_b are not read).  For each row the
+ * call computes the full-vocab softmax at temperature 1, takes the topk
+ * largest logits (ties: lower token id first) as children, with
+ *     conf  = softmax probability of the child token,
+ *     value = value(parent) * conf          (one fp32 multiply),
+ * appends them to the sequence's candidate pool, and -- if s < D --
+ * selects the next frontier: the topk children of this layer with the
+ * largest value (ties: lower token id, then creation order), minus those
+ * whose value < expand_threshold.  next_tokens (device int32 [B][topk])
+ * receives the frontier's tokens in frontier order, padded with -1, and
+ * next_count (device int32 [B]) its size (0 at s = D or once the tree
+ * stopped).  Row alignment: 16-byte aligned rows take the vector path.
+ * Errors: ET_EINVAL (null pointer, step outside 1..D, stride < vocab or
+ * negative), ET_ESTATE (step != 1 and not the step after the last call on
+ * this plan and workspace). */
+int et_draft_step(et_plan_t plan, void* ws, int32_t step,
+                  const int32_t* root_tokens, const void* logits,
+                  int64_t batch_stride, int64_t row_stride,
+                  int32_t* next_tokens, int32_t* next_count,
+                  et_stream_t stream);
+
+/* Rerank ([P1] s4.2; [P2] expand/rerank; [P3] ReRank stage).
+ * Keeps the n = min(N, pool size) pool nodes with the largest value, with
+ * ties broken by shallower depth, then lower token id, then creation
+ * order, and flattens them in that rank order behind the root:
+ *   tokens      device int32 [B][T]  slot 0 = root token, pads = -1
+ *   parent_slot device int32 [B][T]  slot 0 = -1, pads = -1
+ *   conf, value device f32   [B][T]  slot 0 = 1, pads = 0
+ *   n_kept      device int32 [B]     n
+ * Rank order is topological (a parent always ranks before its child), so
+ * parent_slot[s] < s.  Requires et_draft_step(D) as the last call on this
+ * plan and workspace (ET_ESTATE otherwise). */
+int et_rerank(et_plan_t plan, void* ws, int32_t* tokens, int32_t* parent_slot,
+              float* conf, float* value, int32_t* n_kept, et_stream_t stream);
+
+/* Flatten ([P1] s4.2: the kept tokens become one sequence whose attention
+ * mask keeps branches apart): for slot s <= n_kept[b]
+ *   mask[b][s][w]  bit t of word w (t = 64 w + bit) is set iff slot t is
+ *                  slot s or one of its ancestors; device uint64 [B][T][W]
+ *   depth[b][s]    0 for the root, depth(parent) + 1 otherwise
+ *   pos_ids[b][s]  prefix_len[b] + depth[b][s]
+ * Pad slots get mask 0, depth -1, pos_ids -1.  prefix_len: device int32
+ * [B] with 0 <= prefix_len[b] <= prefix_cap (not checked on device). */
+int et_tree_mask(et_plan_t plan, const int32_t* parent_slot,
+                 const int32_t* n_kept, const int32_t* prefix_len,
+                 uint64_t* mask, int32_t* depth, int32_t* pos_ids,
+                 et_stream_t stream);
+
+/* Tree attention, the verify pass ([P1] s4.2; [P2]: the tree is checked
+ * in one tree-attention pass; [P3]: Medusa-style tree attention).
+ * For sequence b, query head h (kv head h / G) and slot s <= n_kept[b]:
+ *     scores over the prefix keys k_cache[b][h/G][0 .. prefix_len[b]) and
+ *     the tree keys k_tree[b][h/G][t] for every t with bit t of
+ *     mask[b][s] set; p = softmax(scale * q . k); out = sum p * v.
+ * Layouts (dtype = qkv_dtype, contiguous, row-major):
+ *     q, out           [B][T][Hq][d]
+ *     k_cache, v_cache [B][Hkv][prefix_cap][d]
+ *     k_tree, v_tree   [B][Hkv][T][d]
+ * Pad slots (s > n_kept[b]) get out = 0.  bf16 inputs are multiplied on
+ * the matrix cores with fp32 accumulation; softmax runs in fp32. */
+int et_tree_attention(et_plan_t plan, void* ws, const void* q,
+                      const void* k_cache, const void* v_cache,
+                      const void* k_tree, const void* v_tree,
+                      const int32_t* prefix_len, const uint64_t* mask,
+                      const int32_t* n_kept, float scale, void* out,
+                      et_stream_t stream);
+
+/* Greedy acceptance at temperature 0 ([P1] s2.1: tokens are accepted in
+ * order along the draft; [P4] s五: greedy decoding).  Target row s of
+ * sequence b is at target_logits + b * batch_stride + s * row_stride
+ * (dtype = logits_dtype), for s = 0 .. n_kept[b].  With a_s = argmax of
+ * row s (ties: lowest id), the walk starts at slot 0 and moves to the
+ * child c of the current slot whose token equals a_current, while one
+ * exists.  Outputs (device int32):
+ *   accept_len [B]        number of accepted draft tokens L
+ *   path_slots [B][D+1]   0, then the accepted slots; -1 after L + 1
+ *   out_tokens [B][D+1]   the L accepted tokens, then the bonus token
+ *                         a_(last accepted slot); -1 after L + 1 */
+int et_accept(et_plan_t plan, void* ws, const void* target_logits,
+              int64_t batch_stride, int64_t row_stride,
+              const int32_t* tokens, const int32_t* parent_slot,
+              const int32_t* n_kept, int32_t* accept_len,
+              int32_t* path_slots, int32_t* out_tokens, et_stream_t stream);
+
+/* Inspection: copy the workspace's candidate pool (after any draft step)
+ * into caller device buffers, for tests and debugging.  Pool arrays are
+ * [B][capacity] (capacity = et_pool_capacity); entries past
+ * pool_count[b] are unspecified.  parent is the pool index of the
+ * parent, -1 for the root.  frontier ([B][topk], pool indices) and
+ * frontier_count ([B]) describe the frontier the next draft step reads.
+ * Any output pointer may be NULL to skip it. */
+int et_pool_export(et_plan_t plan, const void* ws, int32_t* token,
+                   int32_t* parent, int32_t* depth, float* conf, float* value,
+                   int32_t* pool_count, int32_t* frontier,
+                   int32_t* frontier_count, et_stream_t stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* et_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EAGLETREE_H */

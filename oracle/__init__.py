@@ -1,0 +1,208 @@
+"""CPU oracle of the EAGLE-2 draft-tree cycle -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, the smoke check and the CPU-baseline leg of bench.py may use
+this package.  It marshals numpy arrays into liboracle_eagletree.so (plain
+C in eagletree_ref.c, fp64) and shares no code with the HIP library.
+
+Every function here is pinned by tests/test_oracle_pins.py against facts
+the pages or the mathematics fix (library routines on special cases,
+closed forms, the explainer's chain example, brute force, invariants);
+none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "eagletree_ref.c")
+_SO = os.path.join(_HERE, "liboracle_eagletree.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_SO):
+        tmp = _SO + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
+             "-ffp-contract=off", "-fno-fast-math", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        _lib = ctypes.CDLL(_SO)
+        _lib.etref_attention_row.restype = None
+        _lib.etref_tree_attention.restype = None
+    return _lib
+
+
+_DT = {"f32": 0, "bf16": 1}
+
+
+def _p(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+class TreeState:
+    """Pool and frontier of every sequence between draft steps."""
+
+    def __init__(self, w):
+        B, cap, k = w.batch, w.pool_cap, w.topk
+        self.w = w
+        self.token = np.full((B, cap), -1, np.int32)
+        self.parent = np.full((B, cap), -1, np.int32)
+        self.depth = np.full((B, cap), -1, np.int32)
+        self.conf = np.zeros((B, cap), np.float32)
+        self.value = np.zeros((B, cap), np.float32)
+        self.count = np.zeros(B, np.int32)
+        self.root = np.zeros(B, np.int32)
+        self.frontier = np.full((B, k), -1, np.int32)
+        self.frontier_count = np.zeros(B, np.int32)
+
+    def copy(self) -> "TreeState":
+        c = TreeState.__new__(TreeState)
+        c.w = self.w
+        for name in ("token", "parent", "depth", "conf", "value", "count",
+                     "root", "frontier", "frontier_count"):
+            setattr(c, name, getattr(self, name).copy())
+        return c
+
+
+def _rows(a: np.ndarray):
+    """(pointer, batch stride, row stride) in elements of a [B][rows][V]
+    array whose last axis is contiguous."""
+    if a.strides[-1] != a.itemsize:
+        raise ValueError("last axis must be contiguous")
+    return _p(a), a.strides[0] // a.itemsize, a.strides[1] // a.itemsize
+
+
+def draft_step(w, st: TreeState, step: int, root_tokens, logits):
+    """One expansion layer.  logits: [B][rows>=F][V] (f32 or bf16 bits)."""
+    root_tokens = _i32(root_tokens)
+    ptr, bs, rs = _rows(logits)
+    nt = np.full((w.batch, w.topk), -1, np.int32)
+    nc = np.zeros(w.batch, np.int32)
+    rc = lib().etref_draft_step(
+        w.batch, w.vocab, w.topk, w.depth, ctypes.c_float(w.threshold),
+        _DT[w.logits_dtype], step, _p(root_tokens), ptr, ctypes.c_int64(bs),
+        ctypes.c_int64(rs), w.pool_cap, _p(st.token), _p(st.parent),
+        _p(st.depth), _p(st.conf), _p(st.value), _p(st.count), _p(st.root),
+        _p(st.frontier), _p(st.frontier_count), _p(nt), _p(nc))
+    if rc != 0:
+        raise RuntimeError(f"etref_draft_step failed: {rc}")
+    return nt, nc
+
+
+def build_tree(w, root_tokens, draft, st: TreeState | None = None):
+    """Run steps 1..D with draft[b][step-1][j] as frontier row j."""
+    st = TreeState(w) if st is None else st
+    for step in range(1, w.depth + 1):
+        draft_step(w, st, step, root_tokens, draft[:, step - 1])
+    return st
+
+
+def rerank(w, st: TreeState):
+    B, T = w.batch, w.T
+    tokens = np.empty((B, T), np.int32)
+    parent = np.empty((B, T), np.int32)
+    conf = np.empty((B, T), np.float32)
+    value = np.empty((B, T), np.float32)
+    n_kept = np.empty(B, np.int32)
+    rc = lib().etref_rerank(
+        B, w.topk, w.depth, w.budget_n, w.pool_cap, _p(st.token),
+        _p(st.parent), _p(st.depth), _p(st.conf), _p(st.value), _p(st.count),
+        _p(st.root), _p(tokens), _p(parent), _p(conf), _p(value), _p(n_kept))
+    if rc != 0:
+        raise RuntimeError(f"etref_rerank failed: {rc}")
+    return dict(tokens=tokens, parent_slot=parent, conf=conf, value=value,
+                n_kept=n_kept)
+
+
+def tree_mask(w, parent_slot, n_kept, prefix_len):
+    B, T, W = w.batch, w.T, w.W
+    parent_slot, n_kept, prefix_len = map(_i32, (parent_slot, n_kept,
+                                                 prefix_len))
+    mask = np.zeros((B, T, W), np.uint64)
+    depth = np.empty((B, T), np.int32)
+    pos = np.empty((B, T), np.int32)
+    rc = lib().etref_tree_mask(B, w.budget_n, _p(parent_slot), _p(n_kept),
+                               _p(prefix_len), _p(mask), _p(depth), _p(pos))
+    if rc != 0:
+        raise RuntimeError(f"etref_tree_mask failed: {rc}")
+    return dict(mask=mask, depth=depth, pos_ids=pos)
+
+
+def _attn_args(w, inp, prefix_len, mask, n_kept):
+    arrs = [np.ascontiguousarray(inp[n]) for n in
+            ("q", "k_cache", "v_cache", "k_tree", "v_tree")]
+    prefix_len, n_kept = _i32(prefix_len), _i32(n_kept)
+    mask = np.ascontiguousarray(mask, dtype=np.uint64)
+    keep = arrs + [prefix_len, mask, n_kept]
+    head = (w.batch, w.T, w.n_q_heads, w.n_kv_heads, w.head_dim,
+            w.prefix_cap, _DT[w.qkv_dtype])
+    ptrs = [_p(a) for a in arrs] + [_p(prefix_len), _p(mask), _p(n_kept)]
+    return head, ptrs, keep
+
+
+def tree_attention(w, inp, prefix_len, mask, n_kept, scale=None):
+    """All rows, fp64 [B][T][Hq][d]."""
+    scale = w.scale if scale is None else scale
+    head, ptrs, keep = _attn_args(w, inp, prefix_len, mask, n_kept)
+    out = np.zeros((w.batch, w.T, w.n_q_heads, w.head_dim), np.float64)
+    lib().etref_tree_attention(*head, *ptrs, ctypes.c_double(scale), _p(out))
+    del keep
+    return out
+
+
+def attention_rows(w, inp, prefix_len, mask, n_kept, rows, scale=None):
+    """Selected (b, s, h) rows only, fp64 [len(rows)][d]."""
+    scale = w.scale if scale is None else scale
+    head, ptrs, keep = _attn_args(w, inp, prefix_len, mask, n_kept)
+    out = np.zeros((len(rows), w.head_dim), np.float64)
+    for i, (b, s, h) in enumerate(rows):
+        lib().etref_attention_row(*head, *ptrs, ctypes.c_double(scale),
+                                  int(b), int(s), int(h),
+                                  _p(out[i:i + 1]))
+    del keep
+    return out
+
+
+def accept(w, target, tokens, parent_slot, n_kept):
+    B, D = w.batch, w.depth
+    ptr, bs, rs = _rows(target)
+    tokens, parent_slot, n_kept = map(_i32, (tokens, parent_slot, n_kept))
+    alen = np.empty(B, np.int32)
+    path = np.empty((B, D + 1), np.int32)
+    otok = np.empty((B, D + 1), np.int32)
+    rc = lib().etref_accept(B, w.T, w.vocab, D, _DT[w.logits_dtype], ptr,
+                            ctypes.c_int64(bs), ctypes.c_int64(rs),
+                            _p(tokens), _p(parent_slot), _p(n_kept),
+                            _p(alen), _p(path), _p(otok))
+    if rc != 0:
+        raise RuntimeError(f"etref_accept failed: {rc}")
+    return dict(accept_len=alen, path_slots=path, out_tokens=otok)
+
+
+def cycle(w, inputs: dict):
+    """One whole cycle on generated inputs (see synth.gen)."""
+    st = build_tree(w, inputs["root_tokens"], inputs["draft"])
+    rr = rerank(w, st)
+    mk = tree_mask(w, rr["parent_slot"], rr["n_kept"], inputs["prefix_len"])
+    att = tree_attention(w, inputs["attn"], inputs["prefix_len"], mk["mask"],
+                         rr["n_kept"])
+    acc = accept(w, inputs["target"], rr["tokens"], rr["parent_slot"],
+                 rr["n_kept"])
+    return dict(state=st, rerank=rr, mask=mk, attention=att, accept=acc)

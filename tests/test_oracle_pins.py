@@ -1,0 +1,521 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each test ties one oracle function to something other than its own code:
+a library routine on a special case, a closed form, the explainer's chain
+example (tests/golden/chain_example.json), brute force on tiny inputs, or
+an invariant the pages state.  Chosen so that a plausible slip (a dropped
+term, a wrong sign, a swapped tie rule, an off-by-one slot) fails one.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import WORKLOADS, gen
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+TINY = WORKLOADS["tiny"]
+
+
+def _small(**kw):
+    base = dict(batch=1, vocab=64, topk=2, depth=3, budget_n=6, threshold=0.0,
+                logits_dtype="f32", sharpness=(1.5,), n_q_heads=1,
+                n_kv_heads=1, head_dim=64, prefix_cap=16,
+                prefix_range=(16, 16), qkv_dtype="f32", seed=0)
+    base.update(kw)
+    if "sharpness" not in kw:
+        base["sharpness"] = tuple([1.5] * base["batch"])
+    return TINY.with_(**base)
+
+
+def _np_softmax64(row):
+    x = row.astype(np.float64)
+    e = np.exp(x - x.max())
+    return e / e.sum()
+
+
+def _rows_of(logits, dtype):
+    return gen.bf16_bits_to_f32(logits) if dtype == "bf16" else logits
+
+
+# ---------------------------------------------------------------- draft step
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_topk_softmax_match_numpy(dtype):
+    """Children and conf of step 1 == numpy fp64 softmax + lexsort top-k
+    (library routine), including rows with many exactly equal logits."""
+    V, k, B = 300, 7, 6
+    w = _small(batch=B, vocab=V, topk=k, depth=1, budget_n=7,
+               logits_dtype=dtype)
+    g = np.random.default_rng(11)
+    x = (g.standard_normal((B, 1, V)) * 2).astype(np.float32)
+    x[0:3] = np.round(x[0:3])            # heavy ties: integer logits
+    x[5, 0, :] = 0.0                      # all equal: ids 0..k-1 win
+    x[4, 0, 17] = -np.inf                 # -inf is allowed (conf 0)
+    logits = gen.f32_to_bf16_bits(x) if dtype == "bf16" else x
+    roots = np.arange(B, dtype=np.int32)
+    st = oracle.TreeState(w)
+    oracle.draft_step(w, st, 1, roots, logits)
+    xf = _rows_of(logits, dtype)
+    for b in range(B):
+        row = xf[b, 0]
+        order = np.lexsort((np.arange(V), -row.astype(np.float64)))[:k]
+        assert list(st.token[b, :k]) == list(order)
+        p = _np_softmax64(row)[order].astype(np.float32)
+        np.testing.assert_allclose(st.conf[b, :k], p, rtol=2e-7, atol=0)
+        np.testing.assert_array_equal(st.value[b, :k], st.conf[b, :k])
+        assert (st.parent[b, :k] == -1).all() and (st.depth[b, :k] == 1).all()
+    assert list(st.token[5, :k]) == list(range(k))
+
+
+def test_closed_form_single_peak():
+    """One logit a, V-1 zeros: conf(peak) = e^a / (e^a + V - 1), the other
+    children are the lowest ids with conf 1 / (e^a + V - 1)."""
+    V, k, a, peak = 1000, 4, 5.0, 500
+    w = _small(vocab=V, topk=k, depth=1, budget_n=4)
+    x = np.zeros((1, 1, V), np.float32)
+    x[0, 0, peak] = a
+    st = oracle.TreeState(w)
+    oracle.draft_step(w, st, 1, np.array([7], np.int32), x)
+    den = math.exp(a) + V - 1
+    assert list(st.token[0, :k]) == [peak, 0, 1, 2]
+    assert st.conf[0, 0] == pytest.approx(math.exp(a) / den, rel=1e-7)
+    for r in range(1, k):
+        assert st.conf[0, r] == pytest.approx(1.0 / den, rel=1e-7)
+
+
+def _peak_logit(c, V):
+    """Logit a that gives the peak conf c in a row of V-1 zeros."""
+    return math.log(c * (V - 1) / (1.0 - c))
+
+
+def _chain_draft(conf_steps, V=512):
+    D = len(conf_steps)
+    draft = np.zeros((1, D, 1, V), np.float64)
+    for l, c in enumerate(conf_steps):
+        draft[0, l, 0, 10 + l] = _peak_logit(c, V)
+    return draft.astype(np.float32)
+
+
+def test_chain_example_values():
+    """Explainer, 'Common misconception': path products 0.9, 0.72, 0.55,
+    0.40 sum to 2.57 expected accepted tokens."""
+    gold = json.load(open(os.path.join(HERE, "golden", "chain_example.json")))
+    vals = gold["path_products"]
+    steps = [vals[0]] + [vals[i] / vals[i - 1] for i in range(1, len(vals))]
+    w = _small(vocab=512, topk=1, depth=4, budget_n=4)
+    st = oracle.build_tree(w, np.array([3], np.int32), _chain_draft(steps))
+    rr = oracle.rerank(w, st)
+    np.testing.assert_allclose(rr["value"][0, 1:5], vals, rtol=2e-6)
+    assert abs(float(rr["value"][0, 1:5].astype(np.float64).sum())
+               - gold["expected_accepted"]) < 1e-5
+    assert list(rr["parent_slot"][0]) == [-1, 0, 1, 2, 3]
+    assert list(rr["tokens"][0, 1:]) == [10, 11, 12, 13]
+
+
+def _calibrated_chain_targets(w, rr, steps, trials, rng):
+    """Target rows whose argmax at slot s is the chain child with
+    probability steps[s] (the child's conf), else another token."""
+    T, V = w.T, w.vocab
+    planted = np.empty((trials, T), np.int64)
+    for s in range(T):
+        child = rr["tokens"][0, s + 1] if s + 1 < T else 0
+        hit = rng.random(trials) < (steps[s] if s < len(steps) else 0.0)
+        other = rng.integers(0, V - 1, trials)
+        other = np.where(other >= child, other + 1, other)
+        planted[:, s] = np.where(hit, child, other)
+    return planted
+
+
+def test_chain_example_accept_statistics():
+    """Greedy walk on calibrated targets: mean accept length -> 2.57 and
+    full-sweep rate -> 0.40 (explainer chain example), each within a 99%
+    interval of its Monte Carlo error."""
+    gold = json.load(open(os.path.join(HERE, "golden", "chain_example.json")))
+    vals = gold["path_products"]
+    steps = [vals[0]] + [vals[i] / vals[i - 1] for i in range(1, len(vals))]
+    w1 = _small(vocab=512, topk=1, depth=4, budget_n=4)
+    st = oracle.build_tree(w1, np.array([3], np.int32), _chain_draft(steps))
+    rr = oracle.rerank(w1, st)
+    trials = 20000
+    rng = np.random.default_rng(5)
+    planted = _calibrated_chain_targets(w1, rr, steps, trials, rng)
+    target = np.zeros((trials, w1.T, w1.vocab), np.float32)
+    target[np.arange(trials)[:, None], np.arange(w1.T)[None, :], planted] = 1.0
+    wt = w1.with_(batch=trials)
+    rep = {k: np.repeat(rr[k], trials, axis=0) for k in ("tokens",
+                                                         "parent_slot",
+                                                         "n_kept")}
+    acc = oracle.accept(wt, target, rep["tokens"], rep["parent_slot"],
+                        rep["n_kept"])
+    L = acc["accept_len"].astype(np.float64)
+    z = 2.576
+    assert abs(L.mean() - gold["expected_accepted"]) < z * L.std() / math.sqrt(trials)
+    p = gold["full_sweep_probability"]
+    sweep = (L == 4).mean()
+    assert abs(sweep - p) < z * math.sqrt(p * (1 - p) / trials)
+
+
+# ---------------------------------------------------------------- rerank
+def _random_tree(w, seed, sharp=None):
+    sharp = sharp if sharp is not None else w.sharpness
+    ww = w.with_(sharpness=tuple(sharp), seed=seed)
+    draft = gen.draft_logits(ww)
+    roots = gen.root_tokens(ww)
+    return ww, oracle.build_tree(ww, roots, draft), draft, roots
+
+
+def _closed(subset, parent):
+    s = set(subset)
+    return all(parent[i] < 0 or parent[i] in s for i in subset)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_rerank_brute_force_optimal(seed):
+    """Greedy rerank maximises the sum of values over all connected
+    (ancestor-closed) n-subsets of the pool, and is that subset when the
+    maximum is unique (explainer: the objective is additive over nodes)."""
+    sharp = [0.6, 1.0, 1.5, 2.5][seed % 4]
+    w = _small(vocab=48, topk=2, depth=4, budget_n=5, sharpness=(sharp,))
+    w, st, _, _ = _random_tree(w, seed)
+    P = int(st.count[0])
+    assert P <= 20
+    n = min(w.budget_n, P)
+    val = st.value[0, :P].astype(np.float64)
+    par = st.parent[0, :P]
+    sums = []
+    for sub in itertools.combinations(range(P), n):
+        if _closed(sub, par):
+            sums.append((val[list(sub)].sum(), sub))
+    sums.sort(key=lambda t: -t[0])
+    rr = oracle.rerank(w, st)
+    got = rr["value"][0, 1:n + 1].astype(np.float64).sum()
+    assert abs(got - sums[0][0]) <= 1e-6
+    if len(sums) == 1 or sums[0][0] - sums[1][0] > 1e-5:
+        kept = set()
+        for s in range(1, n + 1):
+            # identify pool nodes by (token, depth-consistent parent chain)
+            kept.add((int(rr["tokens"][0, s]), float(rr["value"][0, s])))
+        best = {(int(st.token[0, i]), float(st.value[0, i])) for i in sums[0][1]}
+        assert kept == best
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_rerank_invariants(seed):
+    """Kept set connected, parent before child, values non-increasing along
+    paths, conf in [0, 1] ([P2]: ancestors always outscore a node)."""
+    w = _small(vocab=200, topk=3, depth=4, budget_n=12,
+               sharpness=([0.8, 2.5, 1.5][seed % 3],))
+    w, st, _, _ = _random_tree(w, seed)
+    rr = oracle.rerank(w, st)
+    n = int(rr["n_kept"][0])
+    assert n == min(w.budget_n, int(st.count[0]))
+    ps, v, c = rr["parent_slot"][0], rr["value"][0], rr["conf"][0]
+    for s in range(1, n + 1):
+        assert 0 <= ps[s] < s
+        assert v[s] <= v[ps[s]]
+        assert 0.0 <= c[s] <= 1.0
+    for s in range(n + 1, w.T):
+        assert rr["tokens"][0, s] == -1 and ps[s] == -1
+    # kept values are the n largest of the pool
+    pool_sorted = np.sort(st.value[0, :st.count[0]])[::-1]
+    np.testing.assert_array_equal(np.sort(v[1:n + 1])[::-1], pool_sorted[:n])
+
+
+def test_tie_goes_to_shallower_node():
+    """[P3] ReRank: on equal values the shallower node ranks first.  A row
+    with one logit 200 above the rest has conf == 1.0f exactly, so a chain
+    of such rows gives parent and child the same value."""
+    V = 64
+    w = _small(vocab=V, topk=2, depth=4, budget_n=6)
+    draft = np.full((1, 4, 2, V), -200.0, np.float32)
+    for l in range(4):
+        draft[0, l, :, 40 - l] = 0.0      # peak token 40, 39, 38, 37
+    st = oracle.build_tree(w, np.array([1], np.int32), draft)
+    rr = oracle.rerank(w, st)
+    assert (rr["value"][0, 1:5] == 1.0).all()
+    assert list(rr["tokens"][0, 1:5]) == [40, 39, 38, 37]
+    assert list(rr["parent_slot"][0, 1:5]) == [0, 1, 2, 3]
+
+
+def test_value_tie_then_lower_token():
+    """Equal value and depth: lower token id first (exact logit ties inside
+    one row give bit-identical conf)."""
+    V = 32
+    w = _small(vocab=V, topk=3, depth=1, budget_n=3)
+    x = np.zeros((1, 1, V), np.float32)
+    x[0, 0, [9, 4, 20]] = 3.0
+    st = oracle.build_tree(w, np.array([0], np.int32), x[:, None])
+    rr = oracle.rerank(w, st)
+    assert list(rr["tokens"][0, 1:4]) == [4, 9, 20]
+
+
+# ---------------------------------------------------------------- frontier
+@pytest.mark.parametrize("seed", range(40))
+def test_frontier_and_threshold_rule(seed):
+    """Expansion ([P1] s4.1, [P3] Expand): each layer's expanded nodes are
+    its top-k by value; no expanded node is below the threshold; every
+    unexpanded node above depth D is below the threshold or ranked >= k."""
+    w = _small(vocab=128, topk=2, depth=3, budget_n=8, threshold=0.1,
+               sharpness=([1.5, 2.5, 3.5][seed % 3],))
+    w, st, _, _ = _random_tree(w, seed)
+    P = int(st.count[0])
+    par = st.parent[0, :P]
+    expanded = set(int(p) for p in par if p >= 0)
+    for layer in range(1, w.depth):
+        idx = [i for i in range(P) if st.depth[0, i] == layer]
+        ranked = sorted(idx, key=lambda i: (-float(st.value[0, i]),
+                                            int(st.token[0, i]), i))
+        for r, i in enumerate(ranked):
+            if i in expanded:
+                assert st.value[0, i] >= w.threshold and r < w.topk
+            else:
+                assert st.value[0, i] < w.threshold or r >= w.topk
+    for i in range(P):
+        if st.depth[0, i] == w.depth:
+            assert i not in expanded
+    # children of one parent are that parent's row top-k (k per parent)
+    for p in expanded:
+        assert (par == p).sum() == w.topk
+
+
+def test_stop_when_frontier_empty():
+    """All values below the threshold after layer 1: nothing is expanded
+    again and the pool keeps only the root's children."""
+    w = _small(vocab=1000, topk=2, depth=3, budget_n=8, threshold=0.5,
+               sharpness=(0.5,))
+    w, st, _, _ = _random_tree(w, 3)
+    assert st.count[0] == 2 and st.frontier_count[0] == 0
+
+
+# ---------------------------------------------------------------- mask
+@pytest.mark.parametrize("N", [6, 63, 64, 130, 255])
+def test_mask_matches_parent_walk(N):
+    """Mask bits == the slots met walking parent pointers to the root;
+    popcount == depth + 1; pos = prefix + depth; pads are empty."""
+    g = np.random.default_rng(N)
+    B = 3
+    w = _small(batch=B, budget_n=N)
+    T = N + 1
+    parent = np.full((B, T), -1, np.int32)
+    n_kept = np.array([N, N // 2, 0], np.int32)
+    for b in range(B):
+        for s in range(1, n_kept[b] + 1):
+            parent[b, s] = g.integers(0, s)
+    prefix = np.array([5, 0, 17], np.int32)
+    mk = oracle.tree_mask(w, parent, n_kept, prefix)
+    for b in range(B):
+        for s in range(T):
+            bits = {t for t in range(T)
+                    if (int(mk["mask"][b, s, t // 64]) >> (t % 64)) & 1}
+            if s > n_kept[b]:
+                assert not bits and mk["depth"][b, s] == -1
+                assert mk["pos_ids"][b, s] == -1
+                continue
+            walk, cur = set(), s
+            while cur >= 0:
+                walk.add(cur)
+                cur = parent[b, cur] if cur > 0 else -1
+            assert bits == walk
+            assert mk["depth"][b, s] == len(walk) - 1
+            assert mk["pos_ids"][b, s] == prefix[b] + len(walk) - 1
+
+
+# ---------------------------------------------------------------- attention
+def _attn_case(seed, B=2, N=9, Hq=4, Hkv=2, d=64, Pcap=24, dtype="f32"):
+    w = _small(batch=B, budget_n=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d,
+               prefix_cap=Pcap, prefix_range=(3, Pcap), qkv_dtype=dtype,
+               seed=seed)
+    inp = gen.attention_inputs(w)
+    prefix = gen.prefix_lens(w)
+    g = np.random.default_rng(seed)
+    parent = np.full((B, w.T), -1, np.int32)
+    n_kept = g.integers(1, N + 1, B).astype(np.int32)
+    for b in range(B):
+        for s in range(1, n_kept[b] + 1):
+            parent[b, s] = g.integers(0, s)
+    mk = oracle.tree_mask(w, parent, n_kept, prefix)
+    return w, inp, prefix, parent, n_kept, mk
+
+
+def _f64(a, dtype):
+    return (gen.bf16_bits_to_f32(a) if dtype == "bf16" else a).astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_attention_equals_per_path_causal(dtype):
+    """Verify ([P2] one tree-attention pass, exactly as in the static-tree
+    scheme): row s equals dense causal attention over prefix ++ the path
+    root->s at its last position (torch fp64 SDPA)."""
+    w, inp, prefix, parent, n_kept, mk = _attn_case(1, dtype=dtype)
+    out = oracle.tree_attention(w, inp, prefix, mk["mask"], n_kept)
+    q, kc, vc, kt, vt = (_f64(inp[n], dtype) for n in
+                         ("q", "k_cache", "v_cache", "k_tree", "v_tree"))
+    for b in range(w.batch):
+        for s in range(w.T):
+            if s > n_kept[b]:
+                assert (out[b, s] == 0).all()
+                continue
+            path, cur = [], s
+            while cur >= 0:
+                path.append(cur)
+                cur = parent[b, cur] if cur > 0 else -1
+            path = path[::-1]
+            for h in range(w.n_q_heads):
+                kv = h // w.G
+                K = np.concatenate([kc[b, kv, :prefix[b]], kt[b, kv, path]])
+                Vv = np.concatenate([vc[b, kv, :prefix[b]], vt[b, kv, path]])
+                L = K.shape[0]
+                qs = np.zeros((L, w.head_dim))
+                qs[-1] = q[b, s, h]
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    torch.from_numpy(qs)[None], torch.from_numpy(K)[None],
+                    torch.from_numpy(Vv)[None], is_causal=True,
+                    scale=w.scale)[0, -1].numpy()
+                np.testing.assert_allclose(out[b, s, h], ref, rtol=0,
+                                           atol=1e-12)
+
+
+def test_attention_equal_keys_is_mean_of_visible_values():
+    """Closed form: with every key equal the softmax is uniform, so the
+    output is the mean of the visible values (prefix + ancestors + self)."""
+    w, inp, prefix, parent, n_kept, mk = _attn_case(2)
+    inp = dict(inp)
+    inp["k_cache"] = np.ones_like(inp["k_cache"])
+    inp["k_tree"] = np.ones_like(inp["k_tree"])
+    out = oracle.tree_attention(w, inp, prefix, mk["mask"], n_kept)
+    for b in range(w.batch):
+        for s in range(n_kept[b] + 1):
+            vis = [t for t in range(w.T)
+                   if (int(mk["mask"][b, s, 0]) >> t) & 1]
+            for h in range(w.n_q_heads):
+                kv = h // w.G
+                vals = np.concatenate([inp["v_cache"][b, kv, :prefix[b]],
+                                       inp["v_tree"][b, kv, vis]]).astype(np.float64)
+                np.testing.assert_allclose(out[b, s, h], vals.mean(0),
+                                           atol=1e-12)
+
+
+def test_attention_rows_match_full():
+    w, inp, prefix, parent, n_kept, mk = _attn_case(3, dtype="bf16")
+    full = oracle.tree_attention(w, inp, prefix, mk["mask"], n_kept)
+    rows = [(0, 0, 0), (1, int(n_kept[1]), 3), (0, 1, 2), (1, w.T - 1, 1)]
+    part = oracle.attention_rows(w, inp, prefix, mk["mask"], n_kept, rows)
+    for i, (b, s, h) in enumerate(rows):
+        np.testing.assert_array_equal(part[i], full[b, s, h])
+
+
+# ---------------------------------------------------------------- accept
+@pytest.mark.parametrize("seed", range(30))
+def test_accept_brute_force(seed):
+    """[P1] s2.1 greedy: the walk ends at the deepest slot all of whose
+    path edges match the target argmax at the parent (numpy argmax, first
+    maximum = lowest id); the bonus is that slot's argmax."""
+    w = _small(vocab=40, topk=3, depth=4, budget_n=12, sharpness=(2.0,))
+    w, st, _, _ = _random_tree(w, seed)
+    rr = oracle.rerank(w, st)
+    g = np.random.default_rng(seed)
+    n = int(rr["n_kept"][0])
+    # integer-valued targets (ties common), with a random kept path planted
+    target = np.round(g.standard_normal((1, w.T, w.vocab)) * 2).astype(np.float32)
+    leaf = int(g.integers(0, n + 1))
+    path, cur = [], leaf
+    while cur > 0:
+        path.append(cur)
+        cur = rr["parent_slot"][0, cur]
+    for c in path:
+        if g.random() < 0.85:
+            target[0, rr["parent_slot"][0, c], rr["tokens"][0, c]] = 50.0
+    acc = oracle.accept(w, target, rr["tokens"], rr["parent_slot"],
+                        rr["n_kept"])
+    am = np.argmax(target[0], axis=1)
+    best, best_depth = 0, 0
+    for s in range(1, n + 1):
+        ok, cur, dep = True, s, 0
+        while cur > 0:
+            p = rr["parent_slot"][0, cur]
+            ok &= rr["tokens"][0, cur] == am[p]
+            cur, dep = p, dep + 1
+        if ok and dep > best_depth:
+            best, best_depth = s, dep
+    L = int(acc["accept_len"][0])
+    assert L == best_depth
+    assert acc["path_slots"][0, L] == best
+    assert acc["out_tokens"][0, L] == am[best]
+    assert (acc["path_slots"][0, L + 1:] == -1).all()
+    for i in range(1, L + 1):
+        assert acc["out_tokens"][0, i - 1] == rr["tokens"][0, acc["path_slots"][0, i]]
+
+
+def test_expected_accept_equals_sum_of_values():
+    """Explainer value equation: E[#accepted] = sum of kept values when the
+    target's choice at each slot is drawn from that slot's draft softmax
+    (calibrated drafter).  Monte Carlo over 20000 targets, 99% interval."""
+    w = _small(vocab=24, topk=2, depth=3, budget_n=5, sharpness=(1.0,))
+    w, st, draft, roots = _random_tree(w, 7)
+    rr = oracle.rerank(w, st)
+    n = int(rr["n_kept"][0])
+    # which draft row produced each slot's children: slot -> (layer, row)
+    row_of = {}
+    T = w.T
+    P = int(st.count[0])
+    order = sorted(range(P), key=lambda i: (-float(st.value[0, i]),
+                                            int(st.depth[0, i]),
+                                            int(st.token[0, i]), i))
+    slot_of_pool = {order[s - 1]: s for s in range(1, n + 1)}
+    assert [int(st.token[0, order[s - 1]]) for s in range(1, n + 1)] == \
+        list(rr["tokens"][0, 1:n + 1])
+    row_of[0] = (0, 0)
+    # frontier order of layer l is the order of parents among layer-l+1 nodes
+    for l in range(1, w.depth):
+        parents = []
+        for i in range(P):
+            if st.depth[0, i] == l + 1 and st.parent[0, i] not in parents:
+                parents.append(int(st.parent[0, i]))
+        for j, p in enumerate(parents):
+            if p in slot_of_pool:
+                row_of[slot_of_pool[p]] = (l, j)
+    trials = 20000
+    rng = np.random.default_rng(1)
+    planted = rng.integers(0, w.vocab, (trials, T))
+    for s, (l, j) in row_of.items():
+        p = _np_softmax64(draft[0, l, j])
+        planted[:, s] = rng.choice(w.vocab, size=trials, p=p)
+    target = np.zeros((trials, T, w.vocab), np.float32)
+    target[np.arange(trials)[:, None], np.arange(T)[None, :], planted] = 1000.0
+    wt = w.with_(batch=trials)
+    rep = {k: np.repeat(rr[k], trials, axis=0) for k in ("tokens",
+                                                         "parent_slot",
+                                                         "n_kept")}
+    acc = oracle.accept(wt, target, rep["tokens"], rep["parent_slot"],
+                        rep["n_kept"])
+    L = acc["accept_len"].astype(np.float64)
+    expect = rr["value"][0, 1:n + 1].astype(np.float64).sum()
+    assert abs(L.mean() - expect) < 2.576 * L.std() / math.sqrt(trials) + 1e-3
+
+
+# ---------------------------------------------------------------- generator
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, -2.5, 3.0e38],
+                 np.float32)
+    h = gen.f32_to_bf16_bits(x)
+    back = gen.bf16_bits_to_f32(h)
+    np.testing.assert_array_equal(back[:4], [1.0, 1.0, 1.0 + 2**-6, -2.5])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(back, ref)
+
+
+def test_generator_is_seeded_and_shaped():
+    w = WORKLOADS["tiny"]
+    a, b = gen.draft_logits(w), gen.draft_logits(w)
+    np.testing.assert_array_equal(a, b)
+    assert a.shape == (1, w.depth, w.topk, w.vocab)
+    inp = gen.attention_inputs(w)
+    assert inp["q"].shape == (1, w.T, 1, 64)
+    w64 = WORKLOADS["llama8b_b64"]
+    p = gen.prefix_lens(w64)
+    assert p.min() >= 512 and p.max() <= 4096 and len(set(p)) > 10
