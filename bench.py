@@ -1,0 +1,260 @@
+"""Throughput of one EAGLE-2 draft-tree build + verify cycle on one MI355X.
+
+A step is one whole cycle over one batch: D x et_draft_step, et_rerank,
+et_tree_mask, et_tree_attention (one attention layer) and et_accept, on
+synthetic inputs already resident in HBM.  The default workload is the
+Llama-3.1-8B shape at batch 1 (vocab 128256, top-k 10, depth 8, N 60,
+GQA 32/8 x 128, prefix 4096, bf16).  Input sets rotate so the working set
+exceeds the 256 MB MALL and every cycle reads HBM.
+
+Prints one JSON line: cycles/s, the roofline of the dominant kernel
+(algorithmic bytes / its average duration, HIP events on the launch
+stream) and the CPU oracle timed on this host as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama8b")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch every call eagerly instead of replaying "
+                         "one HIP graph per input set")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget for the CPU oracle baseline (0 = skip)")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="input sets to rotate (0 = enough to pass the MALL)")
+    return ap.parse_args()
+
+
+def algorithmic(w, n_kept, frontier_rows):
+    """Bytes (and flops) each call must move, per launch, from the shapes:
+    logits rows read once, K/V read once, Q/O/tree K/V once."""
+    esz = 2 if w.logits_dtype == "bf16" else 4
+    qsz = 2 if w.qkv_dtype == "bf16" else 4
+    draft = [rows * w.vocab * esz for rows in frontier_rows]
+    accept = float(np.sum(n_kept + 1)) * w.vocab * esz
+    P = w.prefix_range[0]  # fixed-prefix workloads
+    kv = w.batch * w.n_kv_heads * (P + w.T) * w.head_dim * 2 * qsz
+    qo = 2 * w.batch * w.T * w.n_q_heads * w.head_dim * qsz
+    flops = 4.0 * w.batch * w.n_q_heads * w.T * P * w.head_dim
+    return dict(draft=draft, accept=accept, attention=kv + qo,
+                attention_flops=flops)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is "
+              "not supported (the batch would shard by sequence with no "
+              "exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dynamic_draft_tree_amd as d
+    from synth import WORKLOADS, gen
+
+    d.lib()  # fail loudly if the HIP library is missing
+    w = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    # ---- resident input sets ---------------------------------------------
+    t0 = time.time()
+    sets = []
+    set_bytes = 0
+    n_sets = args.sets
+    seed = w.seed
+    while True:
+        s = dict(draft=gen.draft_logits(w, seed), target=gen.target_logits(w, seed),
+                 roots=gen.root_tokens(w, seed), prefix=gen.prefix_lens(w, seed),
+                 attn=gen.attention_inputs(w, seed))
+        ds = dict(draft=dev(s["draft"]), target=dev(s["target"]),
+                  roots=dev(s["roots"]), prefix=dev(s["prefix"]),
+                  attn={k: dev(v) for k, v in s["attn"].items()})
+        if not sets:
+            host0 = s
+            set_bytes = sum(t.numel() * t.element_size() for t in
+                            [ds["draft"], ds["target"], *ds["attn"].values()])
+        sets.append(ds)
+        seed += 1000
+        want = n_sets or max(2, -(-2 * MALL_BYTES // set_bytes))
+        if len(sets) >= min(want, 64):
+            break
+    gen_s = time.time() - t0
+    plan = d.Plan(w)
+    stream = torch.cuda.current_stream()
+
+    def cycle(ds):
+        plan.cycle(ds["roots"], ds["draft"], ds["prefix"], ds["attn"],
+                   ds["target"], stream)
+
+    # ---- graphs: one per input set ---------------------------------------
+    graphs = None
+    if not args.no_graph:
+        cycle(sets[0])  # warm the code objects before capture
+        torch.cuda.synchronize()
+        graphs = []
+        for ds in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                plan.cycle(ds["roots"], ds["draft"], ds["prefix"], ds["attn"],
+                           ds["target"], torch.cuda.current_stream())
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i):
+        if graphs is not None:
+            graphs[i % len(sets)].replay()
+        else:
+            cycle(sets[i % len(sets)])
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        run(i)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+
+    # ---- per-call durations (instrumented pass, eager, same stream) -------
+    names = ["draft", "rerank", "mask", "attention", "accept"]
+    acc = {n: 0.0 for n in names}
+    cnt = {n: 0 for n in names}
+    K = max(10, min(args.steps, 200))
+    evs = []
+    for i in range(K):
+        ds = sets[i % len(sets)]
+        row = []
+        for step in range(1, w.depth + 1):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            plan.draft_step(step, ds["roots"], ds["draft"][:, step - 1], stream)
+            e1.record(stream)
+            row.append(("draft", e0, e1))
+        for n, fn in (("rerank", lambda: plan.rerank(stream)),
+                      ("mask", lambda: plan.tree_mask(ds["prefix"], stream)),
+                      ("attention", lambda: plan.tree_attention(
+                          ds["attn"]["q"], ds["attn"]["k_cache"],
+                          ds["attn"]["v_cache"], ds["attn"]["k_tree"],
+                          ds["attn"]["v_tree"], ds["prefix"], stream=stream)),
+                      ("accept", lambda: plan.accept(ds["target"], stream))):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            row.append((n, e0, e1))
+        evs.append(row)
+    torch.cuda.synchronize()
+    for row in evs:
+        for n, e0, e1 in row:
+            acc[n] += e0.elapsed_time(e1) * 1e3  # us
+            cnt[n] += 1
+    avg_us = {n: acc[n] / cnt[n] for n in names}
+    per_cycle_us = {n: acc[n] / K for n in names}
+
+    # algorithmic bytes of the last cycle's shapes
+    n_kept = plan.n_kept.cpu().numpy()
+    # frontier rows per step: 1 at step 1; with the threshold off every
+    # later step reads k rows per sequence
+    fr = [w.batch] + [w.batch * w.topk] * (w.depth - 1)
+    alg = algorithmic(w, n_kept, fr)
+    dominant = max(names, key=lambda n: per_cycle_us[n])
+    if dominant == "draft":
+        bytes_per_launch = float(np.mean(alg["draft"]))
+        kernel = "draft_step_kernel"
+    elif dominant == "accept":
+        bytes_per_launch = alg["accept"]
+        kernel = "accept_kernel"
+    elif dominant == "attention":
+        bytes_per_launch = alg["attention"]
+        kernel = "tree_attn_bf16_kernel" if w.qkv_dtype == "bf16" else "tree_attn_f32_kernel"
+    else:
+        bytes_per_launch = 0.0
+        kernel = dominant
+    achieved = bytes_per_launch / (avg_us[dominant] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": kernel, "avg_us": round(avg_us[dominant], 3),
+                "bytes_per_launch": bytes_per_launch}
+
+    # ---- CPU oracle baseline ---------------------------------------------
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        inputs = dict(root_tokens=host0["roots"], draft=host0["draft"],
+                      prefix_len=host0["prefix"], attn=host0["attn"],
+                      target=host0["target"])
+        t1 = time.time()
+        n = 0
+        while True:
+            oracle.cycle(w, inputs)
+            n += 1
+            if time.time() - t1 >= args.cpu_seconds or n >= 50:
+                break
+        el = time.time() - t1
+        cpu = {"value": round(n / el, 4), "unit": "cycles/s",
+               "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"{n} full oracle cycle(s) of the {w.name} workload "
+                         f"(input set 0) in {el:.1f} s"}
+
+    line = {
+        "metric": "draft-tree build+verify cycles/sec at Llama-3.1-8B shape, "
+                  "N=60; % HBM roofline",
+        "value": round(1e3 / ms, 2),
+        "unit": "cycles/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.logits_dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "vocab": w.vocab,
+                   "topk": w.topk, "depth": w.depth, "budget_n": w.budget_n,
+                   "heads": f"{w.n_q_heads}/{w.n_kv_heads}x{w.head_dim}",
+                   "prefix": list(w.prefix_range), "input_sets": len(sets),
+                   "set_mb": round(set_bytes / 1e6, 1),
+                   "mode": "eager" if graphs is None else "hip_graph"},
+        "roofline": roofline,
+        "per_call_us": {n: round(avg_us[n], 3) for n in names},
+        "per_cycle_us": {n: round(per_cycle_us[n], 3) for n in names},
+        "cpu_baseline": cpu,
+        "gen_seconds": round(gen_s, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

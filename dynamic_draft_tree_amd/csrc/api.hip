@@ -1,0 +1,408 @@
+// api.hip -- the extern "C" boundary of libeagletree: argument validation,
+// plan creation, workspace layout and kernel launches.  Every check runs
+// on the host before anything is launched; kernels never allocate.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ET_OK;
+  return fail(ET_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define CHECK_PTR(p)                                                  \
+  do {                                                                \
+    if (!(p)) return fail(ET_EINVAL, "%s: %s is NULL", fn, #p);        \
+  } while (0)
+
+et::Plan* as_plan(et_plan_t p) { return reinterpret_cast<et::Plan*>(p); }
+
+// Region indices of Plan::off.
+enum {
+  R_DRAFT_ROW_TICKET, R_DRAFT_SEQ_TICKET, R_ACC_ROW_TICKET, R_ACC_SEQ_TICKET,
+  R_POOL_TOKEN, R_POOL_PARENT, R_POOL_DEPTH, R_POOL_CONF, R_POOL_VALUE,
+  R_POOL_COUNT, R_ROOT, R_FRONTIER, R_FRONTIER_COUNT, R_PART_M, R_PART_S,
+  R_PART_KEYS, R_ROW_M, R_ROW_S, R_ROW_KEYS, R_ACC_PART, R_ACC_AMAX,
+  R_ATT_O, R_ATT_M, R_ATT_L, R_COUNT
+};
+
+void layout(et::Plan& p) {
+  const size_t B = p.B, k = p.k, S = p.s_draft, T = p.T, cap = p.cap;
+  const size_t units = (size_t)p.B * p.Hkv * p.attn_nqb * p.attn_splits;
+  const size_t att_rows = p.attn_splits > 1 ? units * et::kAttnRows : 0;
+  size_t sz[R_COUNT] = {};
+  sz[R_DRAFT_ROW_TICKET] = B * k * 4;
+  sz[R_DRAFT_SEQ_TICKET] = B * 4;
+  sz[R_ACC_ROW_TICKET] = B * T * 4;
+  sz[R_ACC_SEQ_TICKET] = B * 4;
+  sz[R_POOL_TOKEN] = sz[R_POOL_PARENT] = sz[R_POOL_DEPTH] = B * cap * 4;
+  sz[R_POOL_CONF] = sz[R_POOL_VALUE] = B * cap * 4;
+  sz[R_POOL_COUNT] = sz[R_ROOT] = B * 4;
+  sz[R_FRONTIER] = 2 * B * k * 4;
+  sz[R_FRONTIER_COUNT] = 2 * B * 4;
+  sz[R_PART_M] = sz[R_PART_S] = B * k * S * 4;
+  sz[R_PART_KEYS] = B * k * S * et::kMaxTopk * 8;
+  sz[R_ROW_M] = B * k * 4;
+  sz[R_ROW_S] = B * k * 8;
+  sz[R_ROW_KEYS] = B * k * et::kMaxTopk * 8;
+  sz[R_ACC_PART] = B * T * S * 8;
+  sz[R_ACC_AMAX] = B * T * 4;
+  sz[R_ATT_O] = att_rows * p.HD * 4;
+  sz[R_ATT_M] = sz[R_ATT_L] = att_rows * 4;
+  size_t off = 0;
+  for (int r = 0; r < R_COUNT; ++r) {
+    p.off[r] = off;
+    off += align256(sz[r]);
+    if (r == R_ACC_SEQ_TICKET) {
+      p.off_counters = 0;
+      p.n_counters = off / 4;  // counters occupy the first regions
+    }
+  }
+  p.ws_bytes = off;
+}
+
+template <typename T>
+T* at(void* ws, const et::Plan& p, int r) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + p.off[r]);
+}
+
+}  // namespace
+
+namespace et {
+
+DraftWs draft_ws(const Plan& p, void* ws) {
+  DraftWs w;
+  w.row_ticket = at<uint32_t>(ws, p, R_DRAFT_ROW_TICKET);
+  w.seq_ticket = at<uint32_t>(ws, p, R_DRAFT_SEQ_TICKET);
+  w.pool_token = at<int32_t>(ws, p, R_POOL_TOKEN);
+  w.pool_parent = at<int32_t>(ws, p, R_POOL_PARENT);
+  w.pool_depth = at<int32_t>(ws, p, R_POOL_DEPTH);
+  w.pool_conf = at<float>(ws, p, R_POOL_CONF);
+  w.pool_value = at<float>(ws, p, R_POOL_VALUE);
+  w.pool_count = at<int32_t>(ws, p, R_POOL_COUNT);
+  w.root_token = at<int32_t>(ws, p, R_ROOT);
+  w.frontier = at<int32_t>(ws, p, R_FRONTIER);
+  w.frontier_count = at<int32_t>(ws, p, R_FRONTIER_COUNT);
+  w.part_m = at<float>(ws, p, R_PART_M);
+  w.part_s = at<float>(ws, p, R_PART_S);
+  w.part_keys = at<uint64_t>(ws, p, R_PART_KEYS);
+  w.row_m = at<float>(ws, p, R_ROW_M);
+  w.row_s = at<double>(ws, p, R_ROW_S);
+  w.row_keys = at<uint64_t>(ws, p, R_ROW_KEYS);
+  return w;
+}
+
+AcceptWs accept_ws(const Plan& p, void* ws) {
+  AcceptWs w;
+  w.row_ticket = at<uint32_t>(ws, p, R_ACC_ROW_TICKET);
+  w.seq_ticket = at<uint32_t>(ws, p, R_ACC_SEQ_TICKET);
+  w.part = at<uint64_t>(ws, p, R_ACC_PART);
+  w.amax = at<int32_t>(ws, p, R_ACC_AMAX);
+  return w;
+}
+
+AttnWs attn_ws(const Plan& p, void* ws) {
+  AttnWs w;
+  w.o = at<float>(ws, p, R_ATT_O);
+  w.m = at<float>(ws, p, R_ATT_M);
+  w.l = at<float>(ws, p, R_ATT_L);
+  return w;
+}
+
+}  // namespace et
+
+extern "C" {
+
+const char* et_last_error(void) { return g_err; }
+
+int et_plan_create(const et_config* cfg, et_plan_t* out) {
+  const char* fn = "et_plan_create";
+  CHECK_PTR(cfg);
+  CHECK_PTR(out);
+  const et_config& c = *cfg;
+  if (c.logits_dtype != ET_F32 && c.logits_dtype != ET_BF16)
+    return fail(ET_EUNSUPPORTED, "%s: logits_dtype %d", fn, c.logits_dtype);
+  if (c.qkv_dtype != ET_F32 && c.qkv_dtype != ET_BF16)
+    return fail(ET_EUNSUPPORTED, "%s: qkv_dtype %d", fn, c.qkv_dtype);
+  if (c.batch < 1 || c.batch > 65535)
+    return fail(ET_EINVAL, "%s: batch %d outside 1..65535", fn, c.batch);
+  if (c.vocab < 2 || c.vocab > et::kMaxVocab)
+    return fail(ET_EUNSUPPORTED, "%s: vocab %d outside 2..%d", fn, c.vocab,
+                et::kMaxVocab);
+  if (c.topk < 1 || c.topk > et::kMaxTopk)
+    return fail(ET_EUNSUPPORTED, "%s: topk %d outside 1..%d", fn, c.topk,
+                et::kMaxTopk);
+  if (c.topk > c.vocab)
+    return fail(ET_EINVAL, "%s: topk %d > vocab %d", fn, c.topk, c.vocab);
+  if (c.depth < 1 || c.depth > et::kMaxDepth)
+    return fail(ET_EUNSUPPORTED, "%s: depth %d outside 1..%d", fn, c.depth,
+                et::kMaxDepth);
+  if (c.budget_n < 1 || c.budget_n > et::kMaxBudget)
+    return fail(ET_EUNSUPPORTED, "%s: budget_n %d outside 1..%d", fn,
+                c.budget_n, et::kMaxBudget);
+  if (!(c.expand_threshold >= 0.0f) || c.expand_threshold > 1.0f)
+    return fail(ET_EINVAL, "%s: expand_threshold outside [0, 1]", fn);
+  if (c.head_dim != 64 && c.head_dim != 128)
+    return fail(ET_EUNSUPPORTED, "%s: head_dim %d not in {64, 128}", fn,
+                c.head_dim);
+  if (c.n_kv_heads < 1 || c.n_q_heads < c.n_kv_heads ||
+      c.n_q_heads % c.n_kv_heads != 0)
+    return fail(ET_EINVAL, "%s: heads %d / %d not grouped", fn, c.n_q_heads,
+                c.n_kv_heads);
+  if (c.n_q_heads / c.n_kv_heads > 16)
+    return fail(ET_EUNSUPPORTED, "%s: group size %d > 16", fn,
+                c.n_q_heads / c.n_kv_heads);
+  if (c.prefix_cap < 1)
+    return fail(ET_EINVAL, "%s: prefix_cap %d < 1", fn, c.prefix_cap);
+  const long long cap = c.topk + (long long)(c.depth - 1) * c.topk * c.topk;
+  if (cap > et::kMaxPool)
+    return fail(ET_EUNSUPPORTED, "%s: pool capacity %lld > %d", fn, cap,
+                et::kMaxPool);
+
+  et::Plan* p = new (std::nothrow) et::Plan();
+  if (!p) return fail(ET_EINVAL, "%s: out of host memory", fn);
+  p->cfg = c;
+  p->B = c.batch;
+  p->V = c.vocab;
+  p->k = c.topk;
+  p->D = c.depth;
+  p->N = c.budget_n;
+  p->T = c.budget_n + 1;
+  p->W = (p->T + 63) / 64;
+  p->cap = (int)cap;
+  p->Hq = c.n_q_heads;
+  p->Hkv = c.n_kv_heads;
+  p->G = c.n_q_heads / c.n_kv_heads;
+  p->HD = c.head_dim;
+  p->Pcap = c.prefix_cap;
+  p->ldt = c.logits_dtype;
+  p->qdt = c.qkv_dtype;
+  p->s_draft = (p->V + et::chunk_elems(p->ldt) - 1) / et::chunk_elems(p->ldt);
+  // Attention: 64-row query blocks of the G*T rows per kv head; split the
+  // prefix until the grid has about two blocks per compute unit.
+  p->attn_nqb = (p->T * p->G + et::kAttnRows - 1) / et::kAttnRows;
+  const long long units = (long long)p->B * p->Hkv * p->attn_nqb;
+  const int max_tiles = (p->Pcap + et::kAttnTile - 1) / et::kAttnTile;
+  long long splits = (512 + units - 1) / units;
+  if (splits > max_tiles) splits = max_tiles;
+  if (splits > 64) splits = 64;
+  if (splits < 1) splits = 1;
+  p->attn_splits = p->qdt == ET_F32 ? 1 : (int)splits;
+  p->last_ws = nullptr;
+  p->last_step = 0;
+  layout(*p);
+  *out = reinterpret_cast<et_plan_t>(p);
+  g_err[0] = 0;
+  return ET_OK;
+}
+
+int et_plan_destroy(et_plan_t plan) {
+  delete as_plan(plan);
+  return ET_OK;
+}
+
+size_t et_workspace_bytes(et_plan_t plan) {
+  return plan ? as_plan(plan)->ws_bytes : 0;
+}
+
+int32_t et_pool_capacity(et_plan_t plan) {
+  return plan ? as_plan(plan)->cap : 0;
+}
+
+int et_workspace_init(et_plan_t plan, void* ws, et_stream_t stream) {
+  const char* fn = "et_workspace_init";
+  CHECK_PTR(plan);
+  CHECK_PTR(ws);
+  if (((uintptr_t)ws & 255u) != 0)
+    return fail(ET_EINVAL, "%s: workspace not 256-byte aligned", fn);
+  et::Plan& p = *as_plan(plan);
+  p.last_ws = nullptr;
+  p.last_step = 0;
+  return hip_status(et::launch_clear_u32(static_cast<uint32_t*>(ws),
+                                         p.n_counters, (hipStream_t)stream),
+                    fn);
+}
+
+int et_draft_step(et_plan_t plan, void* ws, int32_t step,
+                  const int32_t* root_tokens, const void* logits,
+                  int64_t batch_stride, int64_t row_stride,
+                  int32_t* next_tokens, int32_t* next_count,
+                  et_stream_t stream) {
+  const char* fn = "et_draft_step";
+  CHECK_PTR(plan);
+  CHECK_PTR(ws);
+  CHECK_PTR(logits);
+  CHECK_PTR(next_tokens);
+  CHECK_PTR(next_count);
+  et::Plan& p = *as_plan(plan);
+  if (step < 1 || step > p.D)
+    return fail(ET_EINVAL, "%s: step %d outside 1..%d", fn, step, p.D);
+  if (step == 1) CHECK_PTR(root_tokens);
+  if (row_stride < p.V)
+    return fail(ET_EINVAL, "%s: row_stride %lld < vocab %d", fn,
+                (long long)row_stride, p.V);
+  if (batch_stride < 0)
+    return fail(ET_EINVAL, "%s: negative batch_stride", fn);
+  if (((uintptr_t)ws & 255u) != 0)
+    return fail(ET_EINVAL, "%s: workspace not 256-byte aligned", fn);
+  if (step != 1 && (p.last_ws != ws || p.last_step != step - 1))
+    return fail(ET_ESTATE, "%s: step %d does not follow step %d on this "
+                "workspace", fn, step, p.last_step);
+  const int per = p.ldt == ET_BF16 ? 8 : 4;
+  const bool vec = aligned16(logits) && batch_stride % per == 0 &&
+                   row_stride % per == 0;
+  int rc = hip_status(
+      et::launch_draft_step(p, et::draft_ws(p, ws), step, root_tokens, logits,
+                            batch_stride, row_stride, vec, next_tokens,
+                            next_count, (hipStream_t)stream),
+      fn);
+  if (rc == ET_OK) {
+    p.last_ws = ws;
+    p.last_step = step;
+  }
+  return rc;
+}
+
+int et_rerank(et_plan_t plan, void* ws, int32_t* tokens, int32_t* parent_slot,
+              float* conf, float* value, int32_t* n_kept,
+              et_stream_t stream) {
+  const char* fn = "et_rerank";
+  CHECK_PTR(plan);
+  CHECK_PTR(ws);
+  CHECK_PTR(tokens);
+  CHECK_PTR(parent_slot);
+  CHECK_PTR(conf);
+  CHECK_PTR(value);
+  CHECK_PTR(n_kept);
+  et::Plan& p = *as_plan(plan);
+  if (p.last_ws != ws || p.last_step != p.D)
+    return fail(ET_ESTATE, "%s: the tree is not complete (last step %d of "
+                "%d on this workspace)", fn, p.last_step, p.D);
+  return hip_status(et::launch_rerank(p, et::draft_ws(p, ws), tokens,
+                                      parent_slot, conf, value, n_kept,
+                                      (hipStream_t)stream),
+                    fn);
+}
+
+int et_tree_mask(et_plan_t plan, const int32_t* parent_slot,
+                 const int32_t* n_kept, const int32_t* prefix_len,
+                 uint64_t* mask, int32_t* depth, int32_t* pos_ids,
+                 et_stream_t stream) {
+  const char* fn = "et_tree_mask";
+  CHECK_PTR(plan);
+  CHECK_PTR(parent_slot);
+  CHECK_PTR(n_kept);
+  CHECK_PTR(prefix_len);
+  CHECK_PTR(mask);
+  CHECK_PTR(depth);
+  CHECK_PTR(pos_ids);
+  et::Plan& p = *as_plan(plan);
+  return hip_status(et::launch_tree_mask(p, parent_slot, n_kept, prefix_len,
+                                         mask, depth, pos_ids,
+                                         (hipStream_t)stream),
+                    fn);
+}
+
+int et_tree_attention(et_plan_t plan, void* ws, const void* q,
+                      const void* k_cache, const void* v_cache,
+                      const void* k_tree, const void* v_tree,
+                      const int32_t* prefix_len, const uint64_t* mask,
+                      const int32_t* n_kept, float scale, void* out,
+                      et_stream_t stream) {
+  const char* fn = "et_tree_attention";
+  CHECK_PTR(plan);
+  CHECK_PTR(ws);
+  CHECK_PTR(q);
+  CHECK_PTR(k_cache);
+  CHECK_PTR(v_cache);
+  CHECK_PTR(k_tree);
+  CHECK_PTR(v_tree);
+  CHECK_PTR(prefix_len);
+  CHECK_PTR(mask);
+  CHECK_PTR(n_kept);
+  CHECK_PTR(out);
+  et::Plan& p = *as_plan(plan);
+  if (!(scale > 0.0f) || scale != scale)
+    return fail(ET_EINVAL, "%s: scale must be positive", fn);
+  if (((uintptr_t)ws & 255u) != 0)
+    return fail(ET_EINVAL, "%s: workspace not 256-byte aligned", fn);
+  if (p.qdt == ET_BF16 &&
+      !(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) &&
+        aligned16(k_tree) && aligned16(v_tree) && aligned16(out)))
+    return fail(ET_EINVAL, "%s: bf16 q/k/v/out must be 16-byte aligned", fn);
+  return hip_status(et::launch_tree_attention(
+                        p, et::attn_ws(p, ws), q, k_cache, v_cache, k_tree,
+                        v_tree, prefix_len, mask, n_kept, scale, out,
+                        (hipStream_t)stream),
+                    fn);
+}
+
+int et_accept(et_plan_t plan, void* ws, const void* target_logits,
+              int64_t batch_stride, int64_t row_stride, const int32_t* tokens,
+              const int32_t* parent_slot, const int32_t* n_kept,
+              int32_t* accept_len, int32_t* path_slots, int32_t* out_tokens,
+              et_stream_t stream) {
+  const char* fn = "et_accept";
+  CHECK_PTR(plan);
+  CHECK_PTR(ws);
+  CHECK_PTR(target_logits);
+  CHECK_PTR(tokens);
+  CHECK_PTR(parent_slot);
+  CHECK_PTR(n_kept);
+  CHECK_PTR(accept_len);
+  CHECK_PTR(path_slots);
+  CHECK_PTR(out_tokens);
+  et::Plan& p = *as_plan(plan);
+  if (row_stride < p.V)
+    return fail(ET_EINVAL, "%s: row_stride %lld < vocab %d", fn,
+                (long long)row_stride, p.V);
+  if (batch_stride < 0)
+    return fail(ET_EINVAL, "%s: negative batch_stride", fn);
+  if (((uintptr_t)ws & 255u) != 0)
+    return fail(ET_EINVAL, "%s: workspace not 256-byte aligned", fn);
+  const int per = p.ldt == ET_BF16 ? 8 : 4;
+  const bool vec = aligned16(target_logits) && batch_stride % per == 0 &&
+                   row_stride % per == 0;
+  return hip_status(
+      et::launch_accept(p, et::accept_ws(p, ws), target_logits, batch_stride,
+                        row_stride, vec, tokens, parent_slot, n_kept,
+                        accept_len, path_slots, out_tokens,
+                        (hipStream_t)stream),
+      fn);
+}
+
+int et_pool_export(et_plan_t plan, const void* ws, int32_t* token,
+                   int32_t* parent, int32_t* depth, float* conf, float* value,
+                   int32_t* pool_count, int32_t* frontier,
+                   int32_t* frontier_count, et_stream_t stream) {
+  const char* fn = "et_pool_export";
+  CHECK_PTR(plan);
+  CHECK_PTR(ws);
+  et::Plan& p = *as_plan(plan);
+  return hip_status(
+      et::launch_pool_export(p, et::draft_ws(p, const_cast<void*>(ws)), token,
+                             parent, depth, conf, value, pool_count, frontier,
+                             frontier_count, (hipStream_t)stream),
+      fn);
+}
+
+}  // extern "C"

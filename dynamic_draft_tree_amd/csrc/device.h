@@ -1,0 +1,405 @@
+// device.h -- wave64 primitives and ordering keys shared by the kernels.
+#pragma once
+
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+namespace et {
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// Order-preserving map of a non-NaN float onto uint32 (-0 and +0 equal).
+__device__ __forceinline__ uint32_t ordered_f32(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unordered_f32(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Logit key: larger logit first, then lower token id.  0 = "no element".
+__device__ __forceinline__ uint64_t logit_key(float x, uint32_t id) {
+  return ((uint64_t)ordered_f32(x) << 32) | (uint64_t)(0xFFFFFFFFu - id);
+}
+__device__ __forceinline__ float logit_of(uint64_t key) {
+  return unordered_f32((uint32_t)(key >> 32));
+}
+__device__ __forceinline__ uint32_t id_of(uint64_t key) {
+  return 0xFFFFFFFFu - (uint32_t)key;
+}
+
+// Pool key: larger value, then shallower depth, then lower token, then
+// earlier creation.  value in [0, 1] needs 30 bits, depth <= 15 needs 4,
+// token < 2^18 needs 18, pool index <= 4095 needs 12: 64 in total.
+__device__ __forceinline__ uint64_t pool_key(float value, int depth,
+                                             int token, int idx) {
+  return ((uint64_t)__float_as_uint(value) << 34) |
+         ((uint64_t)(15 - depth) << 30) |
+         ((uint64_t)((1 << 18) - 1 - token) << 12) | (uint64_t)(4095 - idx);
+}
+__device__ __forceinline__ int pool_index_of(uint64_t key) {
+  return 4095 - (int)(key & 0xFFFu);
+}
+__device__ __forceinline__ float pool_value_of(uint64_t key) {
+  return __uint_as_float((uint32_t)(key >> 34));
+}
+
+// ---- cross-lane exchange without LDS traffic -----------------------------
+// xor_lane<M>(v) returns the value of lane (lane ^ M).  Within a 16-lane
+// row: DPP quad_perm (M = 1, 2), row_ror (M = 8; M = 4 picks row_ror:4 or
+// row_ror:12 by lane bit 2, since row_ror:n reads lane (i - n) mod 16).
+// Across rows: v_permlane16_swap / v_permlane32_swap, whose two results
+// hold the lower / upper partner row or half; lane bit 4 / 5 picks one.
+// All lanes of the wave must be active.
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  const int iv = (int)v;
+  if constexpr (M == 1) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, iv, 0xB1, 0xF, 0xF, false);
+  } else if constexpr (M == 2) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, iv, 0x4E, 0xF, 0xF, false);
+  } else if constexpr (M == 4) {
+    const uint32_t dn = (uint32_t)__builtin_amdgcn_update_dpp(0, iv, 0x124, 0xF, 0xF, false);
+    const uint32_t up = (uint32_t)__builtin_amdgcn_update_dpp(0, iv, 0x12C, 0xF, 0xF, false);
+    return (threadIdx.x & 4) ? dn : up;
+  } else if constexpr (M == 8) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, iv, 0x128, 0xF, 0xF, false);
+  } else if constexpr (M == 16) {
+    auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (threadIdx.x & 16) ? (uint32_t)r[0] : (uint32_t)r[1];
+  } else {
+    static_assert(M == 32, "xor distance");
+    auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & 32) ? (uint32_t)r[0] : (uint32_t)r[1];
+  }
+}
+template <int M>
+__device__ __forceinline__ float xor_lane(float v) {
+  return __uint_as_float(xor_lane<M>(__float_as_uint(v)));
+}
+template <int M>
+__device__ __forceinline__ int xor_lane(int v) {
+  return (int)xor_lane<M>((uint32_t)v);
+}
+template <int M>
+__device__ __forceinline__ uint64_t xor_lane(uint64_t v) {
+  const uint32_t lo = xor_lane<M>((uint32_t)v);
+  const uint32_t hi = xor_lane<M>((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+template <int M>
+__device__ __forceinline__ double xor_lane(double v) {
+  return __longlong_as_double((long long)xor_lane<M>((uint64_t)__double_as_longlong(v)));
+}
+// Runtime distance (a compile-time constant after unrolling).
+template <typename T>
+__device__ __forceinline__ T xor_lane_rt(T v, int m) {
+  switch (m) {
+    case 1: return xor_lane<1>(v);
+    case 2: return xor_lane<2>(v);
+    case 4: return xor_lane<4>(v);
+    case 8: return xor_lane<8>(v);
+    case 16: return xor_lane<16>(v);
+    default: return xor_lane<32>(v);
+  }
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int src) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, src);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ float readlane_f32(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
+// Butterfly reductions: every lane ends with the same result.
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, xor_lane_rt(v, m));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += xor_lane_rt(v, m);
+  return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += xor_lane_rt(v, m);
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += xor_lane_rt(v, m);
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint64_t o = xor_lane_rt(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Rank of this lane among the lanes whose `pred` is set, and their count.
+__device__ __forceinline__ int ballot_rank(bool pred, int* count) {
+  const uint64_t m = __ballot(pred);
+  *count = __popcll(m);
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Bitonic sort across the 64 lanes, descending (lane 0 = largest).
+template <typename T>
+__device__ __forceinline__ T wave_sort_desc(T v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const T o = xor_lane_rt(v, j);
+      const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
+      v = take_max ? (o > v ? o : v) : (o < v ? o : v);
+    }
+  return v;
+}
+__device__ __forceinline__ float wave_sort_desc_f32(float v) {
+  return wave_sort_desc<float>(v);
+}
+__device__ __forceinline__ uint64_t wave_sort_desc_u64(uint64_t v) {
+  return wave_sort_desc<uint64_t>(v);
+}
+
+// Make this wave's LDS writes visible to its own later LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __threadfence_block();
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Top-k (k <= 16) of N keys per lane (distinct, 0 = empty) across the
+// wave; lanes 0..k-1 return the result in descending order, other lanes
+// and missing entries return 0.  scratch: 64 u64 of LDS owned by the wave.
+// Fast path: keep only keys >= the k-th largest lane maximum (a lower
+// bound of the k-th largest key) and sort those if they fit one wave;
+// otherwise k rounds of wave-wide maximum.
+template <int N>
+__device__ uint64_t wave_topk_u64(const uint64_t (&keys)[N], int k,
+                                  uint64_t* scratch) {
+  const int lane = lane_id();
+  uint64_t lmax = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) lmax = keys[i] > lmax ? keys[i] : lmax;
+  const uint64_t sorted = wave_sort_desc_u64(lmax);
+  uint64_t L = readlane_u64(sorted, k - 1);
+  if (L == 0) L = 1;  // fewer than k lanes hold keys: take every key
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) c += keys[i] >= L;
+  const int total = wave_sum_i32(c);
+  if (total <= 64) {
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      int cnt;
+      const bool pred = keys[i] >= L;
+      const int r = ballot_rank(pred, &cnt);
+      if (pred) scratch[base + r] = keys[i];
+      base += cnt;
+    }
+    wave_lds_sync();
+    uint64_t v = lane < total ? scratch[lane] : 0;
+    wave_lds_sync();
+    v = wave_sort_desc_u64(v);
+    return lane < k ? v : 0;
+  }
+  uint64_t res = 0, prev = ~0ull;
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (keys[i] < prev && keys[i] > best) best = keys[i];
+    const uint64_t w = wave_max_u64(best);
+    if (lane == r) res = w;
+    prev = w;
+    if (w == 0) break;
+  }
+  return res;
+}
+
+// ---- block-wide selection -------------------------------------------------
+// Top-k (k <= 16) of n distinct keys held in LDS, written in descending
+// order to out[0..k) (0 where n < k).  n <= kRankMax: every thread ranks
+// its keys by counting the larger keys (LDS broadcast reads, no dependent
+// chains).  Larger n: k rounds of block-wide maximum.  All threads of the
+// block must call it; it starts and ends with a barrier.
+constexpr int kRankMax = 256;
+
+template <int NT>
+__device__ void block_topk(const uint64_t* keys, int n, int k, uint64_t* out,
+                           uint64_t* red /* >= NT / 64 entries */) {
+  __syncthreads();
+  const int tid = threadIdx.x;
+  if (n <= kRankMax) {
+    for (int t = tid; t < n; t += NT) {
+      const uint64_t me = keys[t];
+      int rank = 0;
+      int j = 0;
+      for (; j + 4 <= n; j += 4) {
+        rank += (keys[j] > me) + (keys[j + 1] > me) + (keys[j + 2] > me) +
+                (keys[j + 3] > me);
+      }
+      for (; j < n; ++j) rank += keys[j] > me;
+      if (rank < k) out[rank] = me;
+    }
+    for (int r = n + tid; r < k; r += NT) out[r] = 0;
+    __syncthreads();
+    return;
+  }
+  uint64_t prev = ~0ull;
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = 0;
+    for (int t = tid; t < n; t += NT) {
+      const uint64_t v = keys[t];
+      if (v < prev && v > best) best = v;
+    }
+    best = wave_max_u64(best);
+    if ((tid & 63) == 0) red[tid >> 6] = best;
+    __syncthreads();
+    uint64_t w = red[0];
+#pragma unroll
+    for (int q = 1; q < NT / 64; ++q) w = red[q] > w ? red[q] : w;
+    if (tid == 0) out[r] = w;
+    prev = w;
+    __syncthreads();
+  }
+}
+
+// ---- hand-off between blocks of one launch -------------------------------
+// Data that one block produces and a later-arriving block of the same
+// launch consumes is written and read with relaxed agent-scope atomic
+// accesses, which gfx950 performs coherently across the XCDs' separate L2
+// caches (sc1 loads/stores).  Ordering comes from waiting for the
+// producer's stores to complete before it takes its arrival ticket.  This
+// avoids agent-scope fences, which write back and invalidate the L2.
+__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(int32_t* p, int32_t v) {
+  st_agent(reinterpret_cast<uint32_t*>(p), (uint32_t)v);
+}
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  st_agent(reinterpret_cast<uint32_t*>(p), __float_as_uint(v));
+}
+__device__ __forceinline__ void st_agent(double* p, double v) {
+  st_agent(reinterpret_cast<uint64_t*>(p), (uint64_t)__double_as_longlong(v));
+}
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_agent(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_agent(const int32_t* p) {
+  return (int32_t)ld_agent(reinterpret_cast<const uint32_t*>(p));
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __uint_as_float(ld_agent(reinterpret_cast<const uint32_t*>(p)));
+}
+__device__ __forceinline__ double ld_agent(const double* p) {
+  return __longlong_as_double((long long)ld_agent(reinterpret_cast<const uint64_t*>(p)));
+}
+
+// Wait until this wave's stores have completed (s_waitcnt vmcnt(0)); the
+// signal fences keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void wait_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Block-level "last arrival" ticket.  Every wave waits for its own stores
+// (published with st_agent) to complete, the block synchronises, thread 0
+// takes a ticket, and the block whose ticket completes `total` resets the
+// counter.  Returns the same value in every thread of the block; the
+// winner then reads the published data with ld_agent.
+__device__ __forceinline__ bool block_arrive_last(uint32_t* ctr,
+                                                  uint32_t total,
+                                                  int* s_flag) {
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    int last = prev == total - 1;
+    if (last) st_agent(ctr, 0u);
+    *s_flag = last;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// ---- row chunk loader shared by the vocab scans ---------------------------
+constexpr int kLoadThreads = 256;
+// Element e of a thread's E lies at chunk offset elem_off(e): 16-byte
+// vectors of `per` elements, vector v of thread t at (v * 256 + t) * per.
+// The scalar path (rows not 16-byte aligned) uses the same mapping so the
+// per-thread sums, and hence every output bit, do not depend on alignment.
+template <bool BF16>
+__device__ __forceinline__ int elem_off(int e, int tid) {
+  constexpr int per = BF16 ? 8 : 4;
+  return ((e / per) * kLoadThreads + tid) * per + (e % per);
+}
+
+template <bool BF16, bool VEC, int E>
+__device__ __forceinline__ void load_chunk(const void* row, int base, int V,
+                                           int tid, float (&x)[E]) {
+  constexpr int per = BF16 ? 8 : 4;
+  if constexpr (VEC) {
+#pragma unroll
+    for (int i = 0; i < E / per; ++i) {
+      const int off = base + (i * kLoadThreads + tid) * per;
+      if (off + per <= V) {
+        const uint4 u = *(const uint4*)((const char*)row + (size_t)off * (BF16 ? 2 : 4));
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if constexpr (BF16) {
+            x[i * 8 + 2 * q] = __uint_as_float(w[q] << 16);
+            x[i * 8 + 2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+          } else {
+            x[i * 4 + q] = __uint_as_float(w[q]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < per; ++u)
+          x[i * per + u] = off + u < V
+              ? (BF16 ? bf16_bits_to_f32(((const uint16_t*)row)[off + u])
+                      : ((const float*)row)[off + u])
+              : -INFINITY;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int off = base + elem_off<BF16>(e, tid);
+      x[e] = off < V ? (BF16 ? bf16_bits_to_f32(((const uint16_t*)row)[off])
+                             : ((const float*)row)[off])
+                     : -INFINITY;
+    }
+  }
+}
+
+}  // namespace et

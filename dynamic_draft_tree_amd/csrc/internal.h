@@ -1,0 +1,126 @@
+// internal.h -- plan, workspace layout and kernel launchers of libeagletree.
+//
+// Workspace (device, caller-allocated, 256-byte aligned regions):
+//   counters     u32   arrival tickets of the last-block merges; cleared by
+//                      et_workspace_init and reset by every consumer
+//   pool         SoA   token/parent/depth i32, conf/value f32  [B][cap]
+//   pool_count, root_token                                     [B]
+//   frontier     i32   [2][B][k] pool indices, double-buffered by step
+//                      parity so a launch never reads what it writes
+//   frontier_count i32 [2][B]
+//   draft partials     per (row, chunk): max, sum, top-k logit keys
+//   draft rows         per row: max, fp64 sum, top-k logit keys
+//   accept partials    per (slot row, chunk): argmax key; per row argmax
+//   attention partials per (b, kv head, q block, split): O, m, l
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/eagletree.h"
+
+namespace et {
+
+constexpr int kMaxTopk = 16;
+constexpr int kMaxDepth = 15;
+constexpr int kMaxBudget = 255;
+constexpr int kMaxVocab = 1 << 18;       // token id fits the 18-bit key field
+constexpr int kMaxPool = 4095;           // pool index fits the 12-bit field
+constexpr int kScanThreads = 256;        // threads per row-scan block
+constexpr int kElemsBf16 = 32;           // bf16 elements per thread (4 x 16 B)
+constexpr int kElemsF32 = 16;            // fp32 elements per thread (4 x 16 B)
+// vocab elements per row-scan block for a logits dtype
+constexpr int chunk_elems(int dtype) {
+  return kScanThreads * (dtype == ET_BF16 ? kElemsBf16 : kElemsF32);
+}
+constexpr int kAttnRows = 64;            // query rows per attention block
+constexpr int kAttnTile = 64;            // keys per staged K/V tile
+
+struct DraftWs {
+  uint32_t* row_ticket;   // [B][k]
+  uint32_t* seq_ticket;   // [B]
+  int32_t* pool_token;    // [B][cap]
+  int32_t* pool_parent;
+  int32_t* pool_depth;
+  float* pool_conf;
+  float* pool_value;
+  int32_t* pool_count;    // [B]
+  int32_t* root_token;    // [B]
+  int32_t* frontier;      // [2][B][k]
+  int32_t* frontier_count;// [2][B]
+  float* part_m;          // [B][k][S]
+  float* part_s;          // [B][k][S]
+  uint64_t* part_keys;    // [B][k][S][kMaxTopk]
+  float* row_m;           // [B][k]
+  double* row_s;          // [B][k]
+  uint64_t* row_keys;     // [B][k][kMaxTopk]
+};
+
+struct AcceptWs {
+  uint32_t* row_ticket;   // [B][T]
+  uint32_t* seq_ticket;   // [B]
+  uint64_t* part;         // [B][T][S]
+  int32_t* amax;          // [B][T]
+};
+
+struct AttnWs {
+  float* o;               // [B*Hkv][nqb][S][kAttnRows][d]
+  float* m;               // [B*Hkv][nqb][S][kAttnRows]
+  float* l;
+};
+
+struct Plan {
+  et_config cfg;
+  int B, V, k, D, N, T, W, cap;
+  int Hq, Hkv, G, HD, Pcap;
+  int ldt, qdt;           // et_dtype of logits and q/k/v
+  int s_draft;            // vocab chunks per row
+  int attn_nqb, attn_splits;
+  // workspace layout
+  size_t off_counters, n_counters;
+  size_t off[32];
+  size_t ws_bytes;
+  // call-order check
+  const void* last_ws;
+  int last_step;
+};
+
+DraftWs draft_ws(const Plan& p, void* ws);
+AcceptWs accept_ws(const Plan& p, void* ws);
+AttnWs attn_ws(const Plan& p, void* ws);
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_clear_u32(uint32_t* p, size_t n, hipStream_t s);
+hipError_t launch_draft_step(const Plan& p, const DraftWs& w, int step,
+                             const int32_t* root_tokens, const void* logits,
+                             int64_t bstride, int64_t rstride, bool vec,
+                             int32_t* next_tokens, int32_t* next_count,
+                             hipStream_t s);
+hipError_t launch_rerank(const Plan& p, const DraftWs& w, int32_t* tokens,
+                         int32_t* parent_slot, float* conf, float* value,
+                         int32_t* n_kept, hipStream_t s);
+hipError_t launch_tree_mask(const Plan& p, const int32_t* parent_slot,
+                            const int32_t* n_kept, const int32_t* prefix_len,
+                            uint64_t* mask, int32_t* depth, int32_t* pos,
+                            hipStream_t s);
+hipError_t launch_tree_attention(const Plan& p, const AttnWs& w,
+                                 const void* q, const void* kc,
+                                 const void* vc, const void* kt,
+                                 const void* vt, const int32_t* prefix_len,
+                                 const uint64_t* mask, const int32_t* n_kept,
+                                 float scale, void* out, hipStream_t s);
+hipError_t launch_accept(const Plan& p, const AcceptWs& w, const void* target,
+                         int64_t bstride, int64_t rstride, bool vec,
+                         const int32_t* tokens, const int32_t* parent_slot,
+                         const int32_t* n_kept, int32_t* accept_len,
+                         int32_t* path_slots, int32_t* out_tokens,
+                         hipStream_t s);
+hipError_t launch_pool_export(const Plan& p, const DraftWs& w, int32_t* token,
+                              int32_t* parent, int32_t* depth, float* conf,
+                              float* value, int32_t* pool_count,
+                              int32_t* frontier, int32_t* frontier_count,
+                              hipStream_t s);
+
+}  // namespace et

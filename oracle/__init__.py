@@ -196,6 +196,10 @@ def accept(w, target, tokens, parent_slot, n_kept):
     return dict(accept_len=alen, path_slots=path, out_tokens=otok)
 
 
+def num_threads() -> int:
+    return int(lib().etref_num_threads())
+
+
 def cycle(w, inputs: dict):
     """One whole cycle on generated inputs (see synth.gen)."""
     st = build_tree(w, inputs["root_tokens"], inputs["draft"])

@@ -29,6 +29,9 @@
  */
 #include <math.h>
 #include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdlib.h>
 #include <string.h>
 
@@ -457,4 +460,13 @@ int etref_accept(int B, int T, int V, int D, int dtype, const void* target,
   }
   free(amax);
   return 0;
+}
+
+/* Threads the OpenMP loop above may use (1 without OpenMP). */
+int etref_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }

@@ -1,0 +1,111 @@
+"""Host-only checks of the C ABI (no GPU needed): the library loads,
+exports every entry point include/eagletree.h declares, and rejects bad
+arguments with the documented codes before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dynamic_draft_tree_amd as d
+from dynamic_draft_tree_amd import binding
+from synth import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            names |= set(re.findall(r"\b(et_[a-z_]+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    L = d.lib()
+    declared = _declared()
+    assert {"et_draft_step", "et_rerank", "et_tree_mask", "et_tree_attention",
+            "et_accept"} <= declared
+    for name in declared:
+        assert hasattr(L, name), name
+    assert declared <= set(binding.EXPORTS)
+
+
+def _cfg(**kw):
+    c = d.make_config(WORKLOADS["llama8b"])
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("topk", 0, binding.ET_EUNSUPPORTED), ("topk", 17, binding.ET_EUNSUPPORTED),
+    ("depth", 0, binding.ET_EUNSUPPORTED), ("depth", 16, binding.ET_EUNSUPPORTED),
+    ("budget_n", 0, binding.ET_EUNSUPPORTED),
+    ("budget_n", 256, binding.ET_EUNSUPPORTED),
+    ("vocab", 1, binding.ET_EUNSUPPORTED),
+    ("vocab", (1 << 18) + 1, binding.ET_EUNSUPPORTED),
+    ("head_dim", 96, binding.ET_EUNSUPPORTED),
+    ("n_kv_heads", 3, binding.ET_EINVAL),
+    ("n_kv_heads", 0, binding.ET_EINVAL),
+    ("logits_dtype", 7, binding.ET_EUNSUPPORTED),
+    ("qkv_dtype", 2, binding.ET_EUNSUPPORTED),
+    ("batch", 0, binding.ET_EINVAL),
+    ("prefix_cap", 0, binding.ET_EINVAL),
+    ("expand_threshold", -0.5, binding.ET_EINVAL),
+    ("expand_threshold", float("nan"), binding.ET_EINVAL),
+])
+def test_plan_rejects(field, value, code):
+    with pytest.raises(binding.EtError) as e:
+        d.et_plan_create(_cfg(**{field: value}))
+    assert e.value.code == code
+    assert field.split("_")[0] in str(e.value) or "heads" in str(e.value) \
+        or "pool" in str(e.value)
+
+
+def test_largest_supported_tree_is_accepted():
+    """k = 16, D = 15 gives the largest pool (16 + 14 * 256 = 3600)."""
+    h = d.et_plan_create(_cfg(topk=16, depth=15, budget_n=255))
+    assert d.et_pool_capacity(h) == 3600
+    d.et_plan_destroy(h)
+
+
+def test_plan_sizes():
+    for name, w in WORKLOADS.items():
+        h = d.et_plan_create(d.make_config(w))
+        assert d.et_pool_capacity(h) == w.pool_cap
+        assert d.et_workspace_bytes(h) % 256 == 0
+        d.et_plan_destroy(h)
+
+
+def test_calls_validate_before_launch():
+    """Null pointers, bad steps and out-of-order calls fail on the host."""
+    L = d.lib()
+    h = d.et_plan_create(d.make_config(WORKLOADS["tiny"]))
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced
+    nul = None
+    assert L.et_draft_step(h, fake, 1, fake, nul, 1024, 1024, fake, fake,
+                           nul) == binding.ET_EINVAL
+    assert L.et_draft_step(h, fake, 0, fake, fake, 1024, 1024, fake, fake,
+                           nul) == binding.ET_EINVAL
+    assert L.et_draft_step(h, fake, 4, fake, fake, 1024, 1024, fake, fake,
+                           nul) == binding.ET_EINVAL
+    assert L.et_draft_step(h, fake, 1, fake, fake, 1024, 1000, fake, fake,
+                           nul) == binding.ET_EINVAL
+    assert b"row_stride" in L.et_last_error()
+    assert L.et_draft_step(h, fake, 2, fake, fake, 1024, 1024, fake, fake,
+                           nul) == binding.ET_ESTATE
+    assert L.et_rerank(h, fake, fake, fake, fake, fake, fake,
+                       nul) == binding.ET_ESTATE
+    assert L.et_draft_step(h, ctypes.c_void_p((1 << 20) + 8), 1, fake, fake,
+                           1024, 1024, fake, fake, nul) == binding.ET_EINVAL
+    assert L.et_tree_attention(h, fake, fake, fake, fake, fake, fake, fake,
+                               fake, fake, ctypes.c_float(0.0), fake,
+                               nul) == binding.ET_EINVAL
+    assert L.et_accept(h, fake, fake, 0, 10, fake, fake, fake, fake, fake,
+                       fake, nul) == binding.ET_EINVAL
+    assert L.et_tree_mask(h, fake, nul, fake, fake, fake, fake,
+                          nul) == binding.ET_EINVAL
+    d.et_plan_destroy(h)

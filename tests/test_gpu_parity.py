@@ -1,0 +1,345 @@
+"""GPU parity: libeagletree (HIP, through the C ABI) against the CPU oracle.
+
+Protocol (stepwise replay): each GPU call is compared with the oracle run
+from the GPU's own input state, so a legitimate near-tie reorder (oracle
+values within 1e-5 relative) is accepted once and does not cascade; end-
+to-end outputs must then be bit-exact whenever no near-tie event occurred.
+Bars: token ids, topology, masks and accepted paths bit-exact; conf and
+value within 1e-5 relative; attention within 1e-2 max-abs of the fp64
+oracle on the same bf16 inputs (1e-4 for fp32 inputs).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import WORKLOADS, gen
+
+from gpu_util import (ATTN_TOL_BF16, ATTN_TOL_F32, bf16_dev_to_f64,
+                      check_draft_step, dev_inputs, make_inputs,
+                      random_path_targets, state_from_export, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import dynamic_draft_tree_amd as d
+    return d
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    _lib().lib()  # fail loudly if the library is missing
+
+
+TINY = WORKLOADS["tiny"]
+VARIANTS = {
+    "tiny": TINY,
+    "tiny_deep": TINY.with_(threshold=0.0, sharpness=(3.0,), seed=17),
+    "chain_k1": TINY.with_(topk=1, depth=6, budget_n=6, threshold=0.0,
+                           logits_dtype="bf16", qkv_dtype="bf16",
+                           head_dim=128, seed=5),
+    "small_bf16": TINY.with_(batch=3, vocab=5000, topk=4, depth=4,
+                             budget_n=20, threshold=0.0, logits_dtype="bf16",
+                             sharpness=(0.8, 1.5, 2.5), n_q_heads=8,
+                             n_kv_heads=2, head_dim=128, prefix_cap=300,
+                             prefix_range=(1, 300), qkv_dtype="bf16", seed=21),
+    "odd_vocab": TINY.with_(batch=2, vocab=4099, topk=5, depth=3,
+                            budget_n=12, threshold=0.05, logits_dtype="bf16",
+                            sharpness=(2.0, 2.5), n_q_heads=4, n_kv_heads=4,
+                            head_dim=64, prefix_cap=130,
+                            prefix_range=(65, 130), qkv_dtype="bf16", seed=8),
+    "wide_w3": TINY.with_(batch=2, vocab=3000, topk=16, depth=4,
+                          budget_n=150, threshold=0.0, logits_dtype="bf16",
+                          sharpness=(0.8, 1.2), n_q_heads=16, n_kv_heads=1,
+                          head_dim=64, prefix_cap=200,
+                          prefix_range=(100, 200), qkv_dtype="bf16", seed=9),
+    "max_pool": TINY.with_(batch=1, vocab=2048, topk=16, depth=15,
+                           budget_n=255, threshold=0.0, logits_dtype="bf16",
+                           sharpness=(1.0,), n_q_heads=2, n_kv_heads=1,
+                           head_dim=128, prefix_cap=64, prefix_range=(64, 64),
+                           qkv_dtype="bf16", seed=10),
+    "f32_gqa": TINY.with_(batch=2, vocab=1500, topk=3, depth=4, budget_n=10,
+                          threshold=0.0, sharpness=(2.0, 1.0), n_q_heads=4,
+                          n_kv_heads=2, head_dim=128, prefix_cap=100,
+                          prefix_range=(0, 100), seed=11),
+}
+FULL = ["vicuna7b_flat", "vicuna7b_sharp", "llama8b", "llama8b_b64",
+        "llama70b_b8"]
+ALL = list(VARIANTS) + FULL
+
+
+def _w(name):
+    return VARIANTS[name] if name in VARIANTS else WORKLOADS[name]
+
+
+_cache = {}
+
+
+def _run(name):
+    """GPU cycle step by step with pool exports, plus the oracle replay.
+    Cached per workload so later tests reuse one run."""
+    if name in _cache:
+        return _cache[name]
+    d = _lib()
+    w = _w(name)
+    print(f"[parity] {name}: generating inputs", flush=True)
+    inp = make_inputs(w)
+    dev = dev_inputs(inp)
+    plan = d.Plan(w)
+    roots = inp["root_tokens"]
+    before = oracle.TreeState(w)
+    events = 0
+    ora_indep = oracle.TreeState(w)
+    for step in range(1, w.depth + 1):
+        plan.draft_step(step, dev["root_tokens"], dev["draft"][:, step - 1])
+        torch.cuda.synchronize()
+        gpu_after = state_from_export(w, plan.export_pool(), roots)
+        gpu_next = (plan.next_tokens.cpu().numpy(), plan.next_count.cpu().numpy())
+        ora_after = before.copy()
+        ora_next = oracle.draft_step(w, ora_after, step, roots,
+                                     inp["draft"][:, step - 1])
+        events += check_draft_step(w, before, gpu_after, ora_after, gpu_next,
+                                   ora_next)
+        oracle.draft_step(w, ora_indep, step, roots, inp["draft"][:, step - 1])
+        before = gpu_after
+    plan.rerank()
+    torch.cuda.synchronize()
+    gpu_rr = dict(tokens=plan.tokens.cpu().numpy(),
+                  parent_slot=plan.parent_slot.cpu().numpy(),
+                  conf=plan.conf.cpu().numpy(), value=plan.value.cpu().numpy(),
+                  n_kept=plan.n_kept.cpu().numpy())
+    res = dict(w=w, inp=inp, dev=dev, plan=plan, gpu_state=before,
+               ora_indep=ora_indep, events=events, gpu_rr=gpu_rr)
+    _cache[name] = res
+    print(f"[parity] {name}: draft steps done, near-tie events {events}",
+          flush=True)
+    return res
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_draft_steps_replay(name):
+    r = _run(name)
+    w = r["w"]
+    if r["events"] == 0:
+        # no near tie anywhere: the independent oracle run must match
+        g, o = r["gpu_state"], r["ora_indep"]
+        np.testing.assert_array_equal(g.count, o.count)
+        for b in range(w.batch):
+            n = int(o.count[b])
+            for f in ("token", "parent", "depth"):
+                np.testing.assert_array_equal(getattr(g, f)[b, :n],
+                                              getattr(o, f)[b, :n])
+    else:
+        print(f"{name}: {r['events']} near-tie event(s) accepted")
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_rerank_and_mask_exact(name):
+    """Rerank and mask on the GPU pool equal the oracle's on that pool."""
+    r = _run(name)
+    w, plan = r["w"], r["plan"]
+    ora = oracle.rerank(w, r["gpu_state"])
+    g = r["gpu_rr"]
+    for f in ("tokens", "parent_slot", "n_kept"):
+        np.testing.assert_array_equal(g[f], ora[f], err_msg=f)
+    np.testing.assert_array_equal(g["conf"], ora["conf"])
+    np.testing.assert_array_equal(g["value"], ora["value"])
+    # independent oracle run: equal when no near-tie event happened
+    if r["events"] == 0:
+        ind = oracle.rerank(w, r["ora_indep"])
+        np.testing.assert_array_equal(g["tokens"], ind["tokens"])
+        np.testing.assert_array_equal(g["parent_slot"], ind["parent_slot"])
+    plan.tree_mask(r["dev"]["prefix_len"])
+    torch.cuda.synchronize()
+    om = oracle.tree_mask(w, g["parent_slot"], g["n_kept"],
+                          r["inp"]["prefix_len"])
+    np.testing.assert_array_equal(plan.mask.cpu().numpy().view(np.uint64),
+                                  om["mask"])
+    np.testing.assert_array_equal(plan.depth.cpu().numpy(), om["depth"])
+    np.testing.assert_array_equal(plan.pos_ids.cpu().numpy(), om["pos_ids"])
+
+
+def _attn_rows(w, n_kept, rng, limit):
+    rows = []
+    for b in range(w.batch):
+        n = int(n_kept[b])
+        for s in sorted({0, 1 if n >= 1 else 0, n, min(n + 1, w.T - 1),
+                         w.T - 1}):
+            for h in sorted({0, w.n_q_heads - 1, int(rng.integers(w.n_q_heads))}):
+                rows.append((b, s, h))
+    while len(rows) < limit:
+        rows.append((int(rng.integers(w.batch)), int(rng.integers(w.T)),
+                     int(rng.integers(w.n_q_heads))))
+    return rows
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_tree_attention_parity(name):
+    r = _run(name)
+    w, plan, dev, inp = r["w"], r["plan"], r["dev"], r["inp"]
+    a = dev["attn"]
+    plan.tree_mask(dev["prefix_len"])
+    plan.tree_attention(a["q"], a["k_cache"], a["v_cache"], a["k_tree"],
+                        a["v_tree"], dev["prefix_len"])
+    torch.cuda.synchronize()
+    out = bf16_dev_to_f64(plan.attn_out)
+    mask = plan.mask.cpu().numpy().view(np.uint64)
+    n_kept = plan.n_kept.cpu().numpy()
+    tol = ATTN_TOL_F32 if w.qkv_dtype == "f32" else ATTN_TOL_BF16
+    total_keys = w.batch * w.T * w.n_q_heads * (w.prefix_cap + w.T)
+    if total_keys <= 3e7:
+        ref = oracle.tree_attention(w, inp["attn"], inp["prefix_len"], mask,
+                                    n_kept)
+        err = np.abs(out - ref).max()
+        assert err <= tol, f"max abs err {err}"
+    else:
+        rng = np.random.default_rng(0)
+        rows = _attn_rows(w, n_kept, rng, 160)
+        ref = oracle.attention_rows(w, inp["attn"], inp["prefix_len"], mask,
+                                    n_kept, rows)
+        got = np.stack([out[b, s, h] for (b, s, h) in rows])
+        err = np.abs(got - ref).max()
+        assert err <= tol, f"max abs err {err}"
+        # pad slots are exactly zero everywhere
+        for b in range(w.batch):
+            assert (out[b, int(n_kept[b]) + 1:] == 0).all()
+    print(f"{name}: attention max abs err {err:.3e}")
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_accept_exact(name):
+    """Greedy walk on targets that follow a random kept path (long walks),
+    and on the plain generated targets."""
+    r = _run(name)
+    w, plan, dev, inp = r["w"], r["plan"], r["dev"], r["inp"]
+    g = r["gpu_rr"]
+    rng = np.random.default_rng(1)
+    planted = random_path_targets(w, g, rng)
+    for tgt in (inp["target"],
+                gen.target_logits(w, planted=planted, boost=300.0)):
+        td = to_dev(tgt)
+        plan.accept(td)
+        torch.cuda.synchronize()
+        ref = oracle.accept(w, tgt, g["tokens"], g["parent_slot"], g["n_kept"])
+        np.testing.assert_array_equal(plan.accept_len.cpu().numpy(),
+                                      ref["accept_len"])
+        np.testing.assert_array_equal(plan.path_slots.cpu().numpy(),
+                                      ref["path_slots"])
+        np.testing.assert_array_equal(plan.out_tokens.cpu().numpy(),
+                                      ref["out_tokens"])
+    print(f"{name}: accept_len {plan.accept_len.cpu().numpy()[:8]}")
+
+
+def test_cycle_is_deterministic():
+    """Two cycles (second on a fresh workspace) give identical bits."""
+    d = _lib()
+    w = VARIANTS["small_bf16"]
+    inp = make_inputs(w)
+    dev = dev_inputs(inp)
+    outs = []
+    for _ in range(2):
+        plan = d.Plan(w)
+        for _ in range(3):
+            plan.cycle(dev["root_tokens"], dev["draft"], dev["prefix_len"],
+                       dev["attn"], dev["target"])
+        torch.cuda.synchronize()
+        outs.append([t.cpu().clone() for t in (
+            plan.tokens, plan.parent_slot, plan.value, plan.mask,
+            plan.attn_out.view(torch.int16), plan.out_tokens)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_unaligned_rows_take_scalar_path():
+    """Row stride V+1 (rows not 16-byte aligned) gives the same tree."""
+    d = _lib()
+    w = VARIANTS["small_bf16"]
+    inp = make_inputs(w)
+    dev = dev_inputs(inp)
+    plan_a = d.Plan(w)
+    plan_b = d.Plan(w)
+    V = w.vocab
+    padded = torch.zeros((w.batch, w.depth, w.topk, V + 1), dtype=torch.bfloat16,
+                         device="cuda")
+    padded[..., :V] = dev["draft"]
+    for step in range(1, w.depth + 1):
+        plan_a.draft_step(step, dev["root_tokens"], dev["draft"][:, step - 1])
+        plan_b.draft_step(step, dev["root_tokens"], padded[:, step - 1, :, :V])
+    plan_a.rerank()
+    plan_b.rerank()
+    torch.cuda.synchronize()
+    assert torch.equal(plan_a.tokens, plan_b.tokens)
+    assert torch.equal(plan_a.parent_slot, plan_b.parent_slot)
+    assert torch.equal(plan_a.value, plan_b.value)
+
+
+def test_tree_stops_when_all_below_threshold():
+    """Threshold 0.9 with flat rows: step 1 expands nothing further; later
+    steps leave the pool unchanged and report an empty frontier."""
+    d = _lib()
+    w = TINY.with_(threshold=0.9, sharpness=(0.5,), seed=3)
+    inp = make_inputs(w)
+    dev = dev_inputs(inp)
+    plan = d.Plan(w)
+    for step in range(1, w.depth + 1):
+        plan.draft_step(step, dev["root_tokens"], dev["draft"][:, step - 1])
+        torch.cuda.synchronize()
+        assert int(plan.next_count[0]) == 0
+    ex = plan.export_pool()
+    assert int(ex["pool_count"][0]) == w.topk
+    plan.rerank()
+    torch.cuda.synchronize()
+    assert int(plan.n_kept[0]) == w.topk
+
+
+def test_attention_empty_prefix():
+    """prefix_len 0: each slot attends to its ancestors and itself only."""
+    d = _lib()
+    w = VARIANTS["small_bf16"]
+    inp = make_inputs(w)
+    dev = dev_inputs(inp)
+    plan = d.Plan(w)
+    plan.cycle(dev["root_tokens"], dev["draft"], dev["prefix_len"],
+               dev["attn"], dev["target"])
+    zero = torch.zeros_like(dev["prefix_len"])
+    plan.tree_mask(zero)
+    a = dev["attn"]
+    plan.tree_attention(a["q"], a["k_cache"], a["v_cache"], a["k_tree"],
+                        a["v_tree"], zero)
+    torch.cuda.synchronize()
+    mask = plan.mask.cpu().numpy().view(np.uint64)
+    ref = oracle.tree_attention(w, inp["attn"], np.zeros(w.batch, np.int32),
+                                mask, plan.n_kept.cpu().numpy())
+    err = np.abs(bf16_dev_to_f64(plan.attn_out) - ref).max()
+    assert err <= ATTN_TOL_BF16, err
+
+
+@pytest.mark.parametrize("name,reps", [("llama8b", 40), ("llama8b_b64", 8),
+                                       ("small_bf16", 100)])
+def test_repeated_cycles_bit_identical(name, reps):
+    """Blocks of one launch hand partial results to the last-arriving block
+    through agent-coherent accesses; repeated cycles over alternating input
+    sets must reproduce the first cycle's outputs bit for bit."""
+    d = _lib()
+    w = _w(name)
+    sets = [dev_inputs(make_inputs(w, seed=w.seed + i)) for i in range(2)]
+    plan = d.Plan(w)
+    ref = []
+    bufs = lambda: [t.clone() for t in (plan.tokens, plan.parent_slot,
+                                        plan.value, plan.conf, plan.mask,
+                                        plan.attn_out.view(torch.int16),
+                                        plan.out_tokens, plan.path_slots)]
+    for i in range(reps):
+        ds = sets[i % 2]
+        plan.cycle(ds["root_tokens"], ds["draft"], ds["prefix_len"],
+                   ds["attn"], ds["target"])
+        got = bufs()
+        if i < 2:
+            ref.append(got)
+        else:
+            for a, b in zip(ref[i % 2], got):
+                assert torch.equal(a, b), f"cycle {i} differs"
+    torch.cuda.synchronize()
