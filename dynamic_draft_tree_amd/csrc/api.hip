@@ -59,8 +59,10 @@ void layout(et::Plan& p) {
   sz[R_POOL_COUNT] = sz[R_ROOT] = B * 4;
   sz[R_FRONTIER] = 2 * B * k * 4;
   sz[R_FRONTIER_COUNT] = 2 * B * 4;
-  sz[R_PART_M] = sz[R_PART_S] = B * k * S * 4;
-  sz[R_PART_KEYS] = B * k * S * et::kMaxTopk * 8;
+  // draft partials: one per (row, chunk, wave of the scan block)
+  const size_t W4 = et::kScanThreads / 64;
+  sz[R_PART_M] = sz[R_PART_S] = B * k * S * W4 * 4;
+  sz[R_PART_KEYS] = B * k * S * W4 * et::kMaxTopk * 8;
   sz[R_ROW_M] = B * k * 4;
   sz[R_ROW_S] = B * k * 8;
   sz[R_ROW_KEYS] = B * k * et::kMaxTopk * 8;

@@ -158,6 +158,35 @@ __device__ __forceinline__ int ballot_rank(bool pred, int* count) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Exclusive prefix sum over the wave of small non-negative values (< 64),
+// from one ballot per bit plane; *total receives the wave sum.
+__device__ __forceinline__ int wave_excl_prefix_small(int v, int* total) {
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int bit = 0; bit < 6; ++bit) {
+    int cnt;
+    const int r = ballot_rank((v >> bit) & 1, &cnt);
+    pre += r << bit;
+    tot += cnt << bit;
+  }
+  *total = tot;
+  return pre;
+}
+
+// x[e] for a per-lane index e in [0, E) via a select tree (no dynamic
+// register indexing).
+template <int E>
+__device__ __forceinline__ float select_elem(const float (&x)[E], int e) {
+  float t[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) t[i] = x[i];
+#pragma unroll
+  for (int w = E / 2; w >= 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w; ++i) t[i] = (e & w) ? t[i + w] : t[i];
+  return t[0];
+}
+
 // Bitonic sort across the 64 lanes, descending (lane 0 = largest).
 template <typename T>
 __device__ __forceinline__ T wave_sort_desc(T v) {
@@ -174,6 +203,28 @@ __device__ __forceinline__ T wave_sort_desc(T v) {
 }
 __device__ __forceinline__ float wave_sort_desc_f32(float v) {
   return wave_sort_desc<float>(v);
+}
+// Bitonic sort inside each 16-lane row (DPP only), descending.
+__device__ __forceinline__ float row16_sort_desc_f32(float v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int k = 2; k <= 16; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const float o = xor_lane_rt(v, j);
+      const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
+      v = take_max ? fmaxf(v, o) : fminf(v, o);
+    }
+  return v;
+}
+// A value with at least k (<= 16) of the wave's 64 values >= it: the
+// minimum over the four 16-lane rows of each row's ceil(k/4)-th largest.
+__device__ __forceinline__ float wave_kth_lower_bound(float v, int k) {
+  const float srt = row16_sort_desc_f32(v);
+  const int q = (k + 3) / 4 - 1;
+  const float r0 = readlane_f32(srt, q), r1 = readlane_f32(srt, 16 + q);
+  const float r2 = readlane_f32(srt, 32 + q), r3 = readlane_f32(srt, 48 + q);
+  return fminf(fminf(r0, r1), fminf(r2, r3));
 }
 __device__ __forceinline__ uint64_t wave_sort_desc_u64(uint64_t v) {
   return wave_sort_desc<uint64_t>(v);
@@ -235,6 +286,30 @@ __device__ uint64_t wave_topk_u64(const uint64_t (&keys)[N], int k,
   return res;
 }
 
+// Block-wide max / sum of one float per thread (all threads get it).
+template <int NT>
+__device__ __forceinline__ float block_max_f32(float v, float* red) {
+  v = wave_max_f32(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) r = fmaxf(r, red[w]);
+  return r;
+}
+template <int NT>
+__device__ __forceinline__ float block_sum_f32(float v, float* red) {
+  v = wave_sum_f32(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) r += red[w];
+  return r;
+}
+
 // ---- block-wide selection -------------------------------------------------
 // Top-k (k <= 16) of n distinct keys held in LDS, written in descending
 // order to out[0..k) (0 where n < k).  n <= kRankMax: every thread ranks
@@ -251,13 +326,16 @@ __device__ void block_topk(const uint64_t* keys, int n, int k, uint64_t* out,
   if (n <= kRankMax) {
     for (int t = tid; t < n; t += NT) {
       const uint64_t me = keys[t];
-      int rank = 0;
+      int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
       int j = 0;
       for (; j + 4 <= n; j += 4) {
-        rank += (keys[j] > me) + (keys[j + 1] > me) + (keys[j + 2] > me) +
-                (keys[j + 3] > me);
+        r0 += keys[j] > me;
+        r1 += keys[j + 1] > me;
+        r2 += keys[j + 2] > me;
+        r3 += keys[j + 3] > me;
       }
-      for (; j < n; ++j) rank += keys[j] > me;
+      for (; j < n; ++j) r0 += keys[j] > me;
+      const int rank = (r0 + r1) + (r2 + r3);
       if (rank < k) out[rank] = me;
     }
     for (int r = n + tid; r < k; r += NT) out[r] = 0;

@@ -30,8 +30,12 @@ struct DraftArgs {
   float thr;
 };
 
-constexpr int kCandCap = 512;  // LDS candidate slots per block
-constexpr int kRowKeys = 64 * kMaxTopk;  // chunk-list keys of one row (S <= 64)
+constexpr int kCandCap = 512;            // LDS candidate slots per block
+constexpr int kWaves = kScanThreads / 64;  // waves per scan block
+// wave-list keys of one row: (max chunks per row) * waves * k
+constexpr int row_keys_cap(int E) {
+  return ((kMaxVocab + kScanThreads * E - 1) / (kScanThreads * E)) * kWaves * kMaxTopk;
+}
 
 template <bool BF16, bool VEC, int E>
 __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
@@ -41,16 +45,17 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
   const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k = a.k;
-  __shared__ uint64_t s_keys[kCandCap];
+  __shared__ uint64_t s_keys[kCandCap];  // also 4 x 128 wave scratch
+  constexpr int kRowKeys = row_keys_cap(E);
   __shared__ uint64_t s_aux[kRowKeys];
   __shared__ uint64_t s_top[kMaxTopk];
-  __shared__ uint64_t s_red[NT / 64];
-  __shared__ float s_m[NT / 64], s_s[NT / 64], s_L[NT / 64];
+  __shared__ uint64_t s_red[kWaves];
   __shared__ int s_count;
   __shared__ int s_flag;
 
   const int prev = (a.step - 1) & 1, cur = a.step & 1;
   const int F = a.step == 1 ? 1 : a.ws.frontier_count[prev * a.B + b];
+  // phase: frontier count read
   if (F == 0) {
     // The tree stopped growing earlier: no rows, empty next frontier.
     if (c == 0 && j == 0) {
@@ -64,57 +69,75 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
   }
   if (j >= F) return;
 
-  // ---- stream one chunk: max, sum of exp, top-k candidates -------------
+  // ---- stream one chunk: per wave max, sum of exp and top-k -------------
   const int64_t esz = BF16 ? 2 : 4;
   const char* row = (const char*)a.logits + (b * a.bstride + j * a.rstride) * esz;
   const int base = c * kChunkE;
-  if (tid == 0) s_count = 0;
   float x[E];
   load_chunk<BF16, VEC, E>(row, base, a.V, tid, x);
   // phase: chunk loaded
 
-  float lmax = -INFINITY;
+  // Lane max as a pairwise tree (short dependency chain).
+  float mx[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) lmax = fmaxf(lmax, x[e]);
+  for (int e = 0; e < E; ++e) mx[e] = x[e];
+#pragma unroll
+  for (int w = E / 2; w >= 1; w >>= 1)
+#pragma unroll
+    for (int e = 0; e < w; ++e) mx[e] = fmaxf(mx[e], mx[e + w]);
+  const float lmax = mx[0];
   const float mw = wave_max_f32(lmax);
   float sl = 0.f;
   if (mw > -INFINITY) {
-    // exp(x - m) = 2^(x log2 e - m log2 e): one FMA and v_exp_f32
+    // exp(x - m) = 2^(x log2 e - m log2 e): one FMA and v_exp_f32; four
+    // accumulators keep the add chain short.
     const float off = mw * kLog2e;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < E; ++e) sl += __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], kLog2e, -off));
+    for (int e = 0; e < E; ++e)
+      acc[e & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], kLog2e, -off));
+    sl = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   }
   const float sw = wave_sum_f32(sl);
   // phase: max and sum of exp
-  // Each wave's k-th largest lane maximum is a lower bound of the block's
-  // k-th largest element (those k lane maxima are k distinct elements), so
-  // the largest of the bounds is one too: only elements >= it can be in the
-  // block's top-k.
+  // The wave's k-th largest lane maximum Lw bounds its k-th largest
+  // element from below (those k maxima are k distinct elements), so every
+  // element of the wave's top-k is >= Lw.  Those elements are compacted
+  // into LDS with ballots (branch-free: non-candidates write a spare slot)
+  // and ranked by counting; each lands at its rank.
   const float Lw = readlane_f32(wave_sort_desc_f32(lmax), k - 1);
-  if (lane == 0) {
-    s_m[wave] = mw;
-    s_s[wave] = sw;
-    s_L[wave] = Lw;
-  }
-  __syncthreads();
-  float L = s_L[0];
-#pragma unroll
-  for (int w = 1; w < NT / 64; ++w) L = fmaxf(L, s_L[w]);
-  // phase: block threshold
+  // phase: wave threshold
+  uint64_t* scr = &s_keys[wave * 128];
+  int total = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int id = base + elem_off<BF16>(e, tid);
-    if (id < a.V && x[e] >= L) {
-      const int slot = atomicAdd(&s_count, 1);
-      if (slot < kCandCap) s_keys[slot] = logit_key(x[e], (uint32_t)id);
-    }
+    const bool pred = id < a.V && x[e] >= Lw;
+    int n_e;
+    const int r = ballot_rank(pred, &n_e);
+    if (n_e != 0 && pred && total + r < 64) scr[total + r] = logit_key(x[e], (uint32_t)id);
+    total += n_e;
   }
-  __syncthreads();
-  const int n_cand = s_count;
-  if (n_cand <= kCandCap) {
-    block_topk<NT>(s_keys, n_cand, k, s_top, s_red);
+  wave_lds_sync();
+  // phase: wave candidates
+  const int64_t rowid = (int64_t)b * k + j;
+  const int64_t pidx = (rowid * a.S + c) * kWaves + wave;
+  uint64_t* dst = &a.ws.part_keys[pidx * kMaxTopk];
+  if (total <= 64) {
+    // candidate q sits in lane q; compare against each by readlane
+    const uint64_t me = lane < total ? scr[lane] : 0;
+    int r0 = 0, r1 = 0;
+    int q = 0;
+    for (; q + 2 <= total; q += 2) {
+      r0 += readlane_u64(me, q) > me;
+      r1 += readlane_u64(me, q + 1) > me;
+    }
+    if (q < total) r0 += readlane_u64(me, q) > me;
+    const int rank = r0 + r1;
+    if (lane < total && rank < k) st_agent(&dst[rank], me);
+    if (lane >= total && lane < k) st_agent(&dst[lane], (uint64_t)0);
   } else {
-    // Many equal logits: exact selection over the registers, k rounds.
+    // Many equal logits: k rounds of wave-wide maximum over the registers.
     uint64_t prevk = ~0ull;
     for (int r = 0; r < k; ++r) {
       uint64_t best = 0;
@@ -124,71 +147,53 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
         const uint64_t key = id < a.V ? logit_key(x[e], (uint32_t)id) : 0;
         if (key < prevk && key > best) best = key;
       }
-      best = wave_max_u64(best);
-      if (lane == 0) s_red[wave] = best;
-      __syncthreads();
-      uint64_t w = s_red[0];
-#pragma unroll
-      for (int q = 1; q < NT / 64; ++q) w = s_red[q] > w ? s_red[q] : w;
-      if (tid == 0) s_top[r] = w;
+      const uint64_t w = wave_max_u64(best);
+      if (lane == 0) st_agent(&dst[r], w);
       prevk = w;
-      __syncthreads();
     }
   }
-  // phase: block top-k
-  const int64_t rowid = (int64_t)b * k + j;
-  const int64_t pidx = rowid * a.S + c;
-  if (tid < k) st_agent(&a.ws.part_keys[pidx * kMaxTopk + tid], s_top[tid]);
-  if (tid == 0) {
-    float m = s_m[0];
-#pragma unroll
-    for (int w = 1; w < NT / 64; ++w) m = fmaxf(m, s_m[w]);
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w)
-      if (s_m[w] > -INFINITY) s += s_s[w] * __builtin_amdgcn_exp2f((s_m[w] - m) * kLog2e);
-    st_agent(&a.ws.part_m[pidx], m);
-    st_agent(&a.ws.part_s[pidx], s);
+  // phase: wave top-k
+  if (lane == 0) {
+    st_agent(&a.ws.part_m[pidx], mw);
+    st_agent(&a.ws.part_s[pidx], sw);
   }
 
   // phase: partial published
   // ---- last block of this row: merge the S chunk partials --------------
   if (!block_arrive_last(&a.ws.row_ticket[rowid], (uint32_t)a.S, &s_flag)) return;
   {
-    const int64_t p0 = rowid * a.S;
-    const int nk = a.S * k;  // <= 64 * 16
+    const int nl = a.S * kWaves;  // sorted wave lists of this row (<= 256)
+    const int64_t p0 = rowid * a.S * kWaves;
+    const int nk = nl * k;        // <= kRowKeys
     for (int t = tid; t < nk; t += NT) {
-      const int ch = t / k, r = t - ch * k;
-      s_aux[t] = ld_agent(&a.ws.part_keys[(p0 + ch) * kMaxTopk + r]);
+      const int li = t / k, r = t - li * k;
+      s_aux[t] = ld_agent(&a.ws.part_keys[(p0 + li) * kMaxTopk + r]);
     }
-    float pm = -INFINITY, ps = 0.f;
-    if (tid < a.S) {
-      pm = ld_agent(&a.ws.part_m[p0 + tid]);
-      ps = ld_agent(&a.ws.part_s[p0 + tid]);
-    }
+    const float pm = tid < nl ? ld_agent(&a.ws.part_m[p0 + tid]) : -INFINITY;
+    const float ps = tid < nl ? ld_agent(&a.ws.part_s[p0 + tid]) : 0.f;
     // phase: row partials read
-    if (wave == 0) {
-      // S <= 64: one wave combines (max, sum) in fp32
-      const float m = wave_max_f32(pm);
-      const float sc = pm > -INFINITY ? ps * expf(pm - m) : 0.f;
-      const float s = wave_sum_f32(sc);
-      if (lane == 0) {
-        st_agent(&a.ws.row_m[rowid], m);
-        st_agent(&a.ws.row_s[rowid], s);
-      }
+    // (max, sum of exp) over the nl wave partials, in fp32
+    const float m = block_max_f32<NT>(pm, (float*)s_red);
+    const float sc = pm > -INFINITY ? ps * expf(pm - m) : 0.f;
+    const float srow = block_sum_f32<NT>(sc, (float*)s_red);
+    if (tid == 0) {
+      st_agent(&a.ws.row_m[rowid], m);
+      st_agent(&a.ws.row_s[rowid], srow);
     }
-    // Each chunk list is sorted, so with at least k lists the k-th largest
-    // chunk head bounds the row's k-th largest key from below; rank only
-    // the keys above it (with fewer lists every key is a candidate).
+    // Each wave list is sorted, so with at least k lists the k-th largest
+    // head bounds the row's k-th largest key from below; rank only the
+    // keys above it (with fewer lists every key is a candidate).
     __syncthreads();
-    if (tid < a.S) s_keys[tid] = s_aux[tid * k];
+    if (tid < nl) s_keys[tid] = s_aux[tid * k];
+    // phase: row sum published
     uint64_t Lh = 1;
-    if (a.S >= k) {
-      block_topk<NT>(s_keys, a.S, k, s_top, s_red);
+    if (nl >= k) {
+      block_topk<NT>(s_keys, nl, k, s_top, s_red);
       Lh = s_top[k - 1];
     }
     if (tid == 0) s_count = 0;
     __syncthreads();
+    // phase: row threshold
     for (int t = tid; t < nk; t += NT) {
       const uint64_t v = s_aux[t];
       if (v >= Lh && v != 0) {
@@ -248,6 +253,7 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
     }
     if (tid == 0) s_count = 0;
     __syncthreads();
+    // phase: frontier threshold
     if (tid < n_new && !(pool_value_of(s_aux[tid]) < vL))
       s_keys[atomicAdd(&s_count, 1)] = s_aux[tid];
     __syncthreads();

@@ -8,7 +8,7 @@
 //   frontier     i32   [2][B][k] pool indices, double-buffered by step
 //                      parity so a launch never reads what it writes
 //   frontier_count i32 [2][B]
-//   draft partials     per (row, chunk): max, sum, top-k logit keys
+//   draft partials     per (row, chunk, wave): max, sum, top-k logit keys
 //   draft rows         per row: max, fp64 sum, top-k logit keys
 //   accept partials    per (slot row, chunk): argmax key; per row argmax
 //   attention partials per (b, kv head, q block, split): O, m, l
@@ -50,9 +50,9 @@ struct DraftWs {
   int32_t* root_token;    // [B]
   int32_t* frontier;      // [2][B][k]
   int32_t* frontier_count;// [2][B]
-  float* part_m;          // [B][k][S]
-  float* part_s;          // [B][k][S]
-  uint64_t* part_keys;    // [B][k][S][kMaxTopk]
+  float* part_m;          // [B][k][S][waves]
+  float* part_s;          // [B][k][S][waves]
+  uint64_t* part_keys;    // [B][k][S][waves][kMaxTopk]
   float* row_m;           // [B][k]
   double* row_s;          // [B][k]
   uint64_t* row_keys;     // [B][k][kMaxTopk]
