@@ -28,6 +28,14 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True, capture_output=not verbose)
+    # a kernel template whose host-side instantiation failed leaves its
+    # launch stub undefined; refuse such a library here rather than at load
+    und = subprocess.run(["nm", "-D", "--undefined-only", tmp], check=True,
+                         capture_output=True, text=True).stdout
+    missing = [ln.split()[-1] for ln in und.splitlines() if "_ZN2et" in ln]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("libeagletree: undefined symbols " + ", ".join(missing))
     os.replace(tmp, LIB)
     return LIB
 

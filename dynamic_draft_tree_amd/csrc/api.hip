@@ -48,7 +48,7 @@ enum {
 void layout(et::Plan& p) {
   const size_t B = p.B, k = p.k, S = p.s_draft, T = p.T, cap = p.cap;
   const size_t units = (size_t)p.B * p.Hkv * p.attn_nqb * p.attn_splits;
-  const size_t att_rows = p.attn_splits > 1 ? units * et::kAttnRows : 0;
+  const size_t att_rows = p.attn_splits > 1 ? units * 64 * p.attn_wr : 0;
   size_t sz[R_COUNT] = {};
   sz[R_DRAFT_ROW_TICKET] = B * k * 4;
   sz[R_DRAFT_SEQ_TICKET] = B * 4;
@@ -199,14 +199,21 @@ int et_plan_create(const et_config* cfg, et_plan_t* out) {
   p->ldt = c.logits_dtype;
   p->qdt = c.qkv_dtype;
   p->s_draft = (p->V + et::chunk_elems(p->ldt) - 1) / et::chunk_elems(p->ldt);
-  // Attention: 64-row query blocks of the G*T rows per kv head; split the
-  // prefix until the grid has about two blocks per compute unit.
-  p->attn_nqb = (p->T * p->G + et::kAttnRows - 1) / et::kAttnRows;
+  // Attention: the G*T query rows of one kv head are cut into blocks of
+  // 64 or 128 rows (128 when that adds no padding rows: each K/V tile then
+  // serves twice the rows); the keys are split until the grid has about
+  // one block per compute unit.
+  {
+    const int R = p->T * p->G;
+    const int q1 = (R + 63) / 64, q2 = (R + 127) / 128;
+    p->attn_wr = q2 * 128 <= q1 * 64 ? 2 : 1;
+    p->attn_nqb = p->attn_wr == 2 ? q2 : q1;
+  }
   const long long units = (long long)p->B * p->Hkv * p->attn_nqb;
-  const int max_tiles = (p->Pcap + et::kAttnTile - 1) / et::kAttnTile;
-  long long splits = (512 + units - 1) / units;
+  const int max_tiles = (p->Pcap + p->T + et::kAttnTile - 1) / et::kAttnTile;
+  long long splits = (et::kAttnTargetBlocks + units - 1) / units;
   if (splits > max_tiles) splits = max_tiles;
-  if (splits > 64) splits = 64;
+  if (splits > et::kAttnMaxSplits) splits = et::kAttnMaxSplits;
   if (splits < 1) splits = 1;
   p->attn_splits = p->qdt == ET_F32 ? 1 : (int)splits;
   p->last_ws = nullptr;

@@ -8,18 +8,27 @@
 // keys of its ancestors and itself (bit t of mask[b][s]).
 //
 // bf16 path (matrix cores, gfx950 v_mfma_f32_16x16x32_bf16):
-//   grid (S splits, q blocks of 64 rows, B * Hkv); 4 waves, 16 rows each.
-//   The rows of one kv head are the G query heads of every slot, row
-//   r = slot * G + g, so the K/V tile staged in LDS serves G*T queries.
+//   A unit is one kv head of one sequence; its rows are the G query heads
+//   of every slot, row r = slot * G + g, so a K/V tile staged in LDS serves
+//   G*T queries.  Rows are cut into blocks of 64*WR (4 waves, 16*WR rows
+//   each) and the unit's key tiles (prefix tiles, then tree tiles) into S
+//   contiguous splits; one block per (unit, row block, split).  Block i
+//   runs on XCD i % 8, so the launch maps every block of a unit to one XCD
+//   and the unit's K/V and split partials stay in that XCD's L2.
 //   Scores are computed transposed, S^T = K . Q^T, which leaves each lane
 //   holding one query row (lane % 16) and 4 consecutive keys per 16-key
 //   sub-tile; that register layout is directly the B operand of
 //   O^T = V^T . P^T when the MFMA's k index is permuted to
-//   {4g..4g+3, 16+4g..16+4g+3} (the A operand V^T reads the same keys
-//   from a transposed V tile in LDS).  Online softmax in fp32 registers
-//   with exp2 and a pre-multiplied log2(e) scale; the ancestor bitmask is
-//   tested per key in registers.  With S > 1 each split writes (O, m, l)
-//   partials and a merge kernel combines them.
+//   {4g..4g+3, 16+4g..16+4g+3}.  The A operand V^T is read from the
+//   row-major V tile with the LDS transpose read (ds_read_b64_tr_b16: in
+//   each 16-lane group, lane j receives element j % 4 of the 8-byte words
+//   addressed by lanes j/4, 4+j/4, 8+j/4, 12+j/4), so no transposed copy
+//   of V is ever written.  K/V tiles are double-buffered in LDS with one
+//   barrier per tile; the next tile's global loads are in flight while the
+//   current one is computed.  Online softmax in fp32 registers with exp2
+//   and a pre-multiplied log2(e) scale; the ancestor bitmask word of a tree
+//   tile is tested per key in registers.  With S > 1 each split writes
+//   (O, m, l) partials and a merge kernel combines them.
 // fp32 path: plain per-row kernel (vector ALU), for fp32 inputs.
 #include "device.h"
 #include "internal.h"
@@ -28,6 +37,8 @@ namespace et {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 struct AttnArgs {
   const void* q;
@@ -46,6 +57,9 @@ struct AttnArgs {
   float scale, scale_log2;
 };
 
+// Growth of a row's max (log2 units) tolerated before O is rescaled.
+constexpr float kSlack = 8.0f;
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
@@ -56,74 +70,162 @@ __device__ __forceinline__ uint64_t pick_word(const uint64_t (&m)[4], int w) {
   return w == 0 ? m[0] : w == 1 ? m[1] : w == 2 ? m[2] : m[3];
 }
 
-template <int HD>
-__global__ __launch_bounds__(256) void tree_attn_bf16_kernel(AttnArgs a) {
-  constexpr int KSTEPS = HD / 32;
-  constexpr int DT = HD / 16;
-  constexpr int KPAD = HD + 8;
-  constexpr int VPAD = kAttnTile + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kAttnTile * KPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[HD * VPAD];
+// LDS byte address of a shared-memory pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 
-  const int split = blockIdx.x, qb = blockIdx.y, bh = blockIdx.z;
-  const int b = bh / a.Hkv, kvh = bh - b * a.Hkv;
+// ds_read_b64_tr_b16 at an LDS byte address, plus a fixed byte offset.
+// Plain (non-template) device functions: the host pass never sees the
+// assembly inside a kernel body.
+__device__ __forceinline__ u32x2_t ds_read_tr16(uint32_t addr) {
+  u32x2_t v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+__device__ __forceinline__ u32x2_t ds_read_tr16_off2k(uint32_t addr) {
+  u32x2_t v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:2048" : "=v"(v) : "v"(addr));
+  return v;
+}
+__device__ __forceinline__ u32x2_t ds_read_tr16_off4k(uint32_t addr) {
+  u32x2_t v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:4096" : "=v"(v) : "v"(addr));
+  return v;
+}
+
+// s_waitcnt lgkmcnt(0) that the compiler sees as producing the values of
+// the transpose reads issued before it.
+__device__ __forceinline__ void lds_wait_all(u32x2_t (&x)[8], u32x2_t (&y)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]),
+                 "+v"(x[5]), "+v"(x[6]), "+v"(x[7]), "+v"(y[0]), "+v"(y[1]),
+                 "+v"(y[2]), "+v"(y[3]), "+v"(y[4]), "+v"(y[5]), "+v"(y[6]),
+                 "+v"(y[7]));
+}
+__device__ __forceinline__ void lds_wait_all(u32x2_t (&x)[4], u32x2_t (&y)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(y[0]),
+                 "+v"(y[1]), "+v"(y[2]), "+v"(y[3]));
+}
+
+// 16 bytes per lane from global memory straight into a 1 KB LDS slab
+// (lane i writes bytes 16i..16i+15; `slab` must be wave-uniform).  A plain
+// device function, so that kernel templates calling it still instantiate
+// in the host pass.
+__device__ __forceinline__ void load_lds16(const void* src, void* slab) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)slab, 16, 0, 0);
+}
+
+// s_waitcnt immediate that waits until at most n vector memory loads are
+// outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
+
+// Block index -> (unit, row block, split) with every block of a unit on
+// XCD unit % 8.  Returns false for the padding blocks past the last unit.
+__device__ __forceinline__ bool attn_block_coords(int i, int units, int per_unit,
+                                                  int* unit, int* rem) {
+  const int xcd = i & 7, j = i >> 3;
+  const int u = xcd + 8 * (j / per_unit);
+  *unit = u;
+  *rem = j - (j / per_unit) * per_unit;
+  return u < units;
+}
+
+__device__ __forceinline__ void barrier_no_fence() {
+  // s_barrier alone: the direct loads still in flight into another buffer
+  // need no fence here (each wave waits for its own loads with an explicit
+  // vmcnt before the barrier that publishes them)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int HD, int WR>
+__global__ __launch_bounds__(512, 1) void tree_attn_bf16_kernel(AttnArgs a) {
+  constexpr int KSTEPS = HD / 32;  // 32-wide d steps of K . Q^T
+  constexpr int DT = HD / 16;      // 16-wide d tiles of O
+  constexpr int TE = kAttnTile * HD;  // elements of one K (or V) tile
+  constexpr int CPR = HD / 8;      // 16-byte chunks per key row
+  constexpr int CH = kAttnTile * CPR / 64 / 8;  // 1 KB slabs per wave per tile
+  constexpr int NB = 3;            // LDS tile buffers: prefetch distance 2
+  constexpr int BR = 64 * WR;      // query rows per block
+  __shared__ __attribute__((aligned(16))) uint16_t sKV[NB][2][TE];
+  __shared__ uint64_t sMask[4][BR];  // [tree tile][row of the block]
+
+  int unit, rem;
+  if (!attn_block_coords(blockIdx.x, a.B * a.Hkv, a.nqb * a.S, &unit, &rem)) return;
+  const int qb = rem / a.S, split = rem - qb * a.S;
+  const int b = unit / a.Hkv, kvh = unit - b * a.Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int rg = wave & 3, kh = wave >> 2;  // row group, key half of a tile
   const int r16 = lane & 15, g = lane >> 4;
   const int n = a.n_kept[b];
   const int R = (n + 1) * a.G;
   const int RT = a.T * a.G;
-  const int row0 = qb * kAttnRows;
+  const int row0 = qb * BR;
   uint16_t* out = (uint16_t*)a.out;
 
   if (row0 >= R) {
+    // rows of unkept slots: zero output (the merge does it when S > 1)
     if (a.S == 1) {
-      for (int e = tid; e < kAttnRows * HD; e += 256) {
-        int r = row0 + e / HD;
+      for (int e = tid; e < BR * (HD / 4); e += 512) {
+        const int r = row0 + e / (HD / 4);
         if (r >= RT) break;
-        int slot = r / a.G, gg = r - slot * a.G;
-        out[(((int64_t)b * a.T + slot) * a.Hq + kvh * a.G + gg) * HD + e % HD] = 0;
+        const int slot = r / a.G, gg = r - slot * a.G;
+        *(uint2*)(out + (((int64_t)b * a.T + slot) * a.Hq + kvh * a.G + gg) * HD +
+                  (e % (HD / 4)) * 4) = make_uint2(0u, 0u);
       }
     }
     return;
   }
 
   const int P = a.prefix_len[b];
-  const int ntiles = (P + kAttnTile - 1) / kAttnTile;
-  const int t_begin = (int)((int64_t)split * ntiles / a.S);
-  const int t_end = (int)((int64_t)(split + 1) * ntiles / a.S);
-  const int ntree = (a.T + kAttnTile - 1) / kAttnTile;
-  const int nprefix = t_end - t_begin;
-  const int total = nprefix + (split == a.S - 1 ? ntree : 0);
+  const int tp = (P + kAttnTile - 1) / kAttnTile;
+  const int tt = (n + 1 + kAttnTile - 1) / kAttnTile;
+  const int tot = tp + tt;
+  const int t_begin = (int)((int64_t)split * tot / a.S);
+  const int cnt = (int)((int64_t)(split + 1) * tot / a.S) - t_begin;
 
-  const int r = row0 + wave * 16 + r16;
-  const bool rvalid = r < R;
-  const int slot = r / a.G, gg = r - slot * a.G;
-  bf16x8_t qf[KSTEPS];
-  uint64_t mrow[4] = {0, 0, 0, 0};
+  // Prologue loads are unconditional (row and key indexes are clamped to
+  // valid data, whose results are then masked or never stored), so every
+  // path into the tile loop has the same loads outstanding and the
+  // compiler's wait counting adds no vmcnt(0) inside the loop.
+  const int me = min(tid, 4 * BR - 1);  // mask word staged by this thread
+  uint64_t mword;
   {
+    const int rc = min(row0 + me % BR, R - 1);
+    mword = a.mask[((int64_t)b * a.T + rc / a.G) * a.W + min(me / BR, a.W - 1)];
+  }
+  bf16x8_t qf[WR][KSTEPS];
+#pragma unroll
+  for (int w = 0; w < WR; ++w) {
+    const int rc = min(row0 + rg * 16 * WR + w * 16 + r16, R - 1);
+    const int slot = rc / a.G, gg = rc - slot * a.G;
     const uint16_t* qr = (const uint16_t*)a.q +
                          (((int64_t)b * a.T + slot) * a.Hq + kvh * a.G + gg) * HD;
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      if (rvalid) {
-        qf[kk] = *(const bf16x8_t*)(qr + kk * 32 + g * 8);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qf[kk][i] = (__bf16)0.0f;
-      }
-    }
-    if (rvalid) {
-      const uint64_t* mr = a.mask + ((int64_t)b * a.T + slot) * a.W;
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        if (w < a.W) mrow[w] = mr[w];
-    }
+    for (int kk = 0; kk < KSTEPS; ++kk) qf[w][kk] = *(const bf16x8_t*)(qr + kk * 32 + g * 8);
   }
 
-  f32x4_t oacc[DT];
+  f32x4_t oacc[WR][DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int w = 0; w < WR; ++w)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[w][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // Row sums l ride on the matrix cores as well: ones . P^T adds the bf16
+  // weights exactly as V^T . P^T uses them, replicated over the 16 d rows.
+  f32x4_t lacc[WR];
+  float m_run[WR];
+#pragma unroll
+  for (int w = 0; w < WR; ++w) {
+    lacc[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[w] = -INFINITY;
+  }
+  bf16x8_t ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+  const float c = a.scale_log2;
 
   const int64_t kvb = (int64_t)b * a.Hkv + kvh;
   const uint16_t* kcb = (const uint16_t*)a.kc + kvb * a.Pcap * HD;
@@ -131,158 +233,249 @@ __global__ __launch_bounds__(256) void tree_attn_bf16_kernel(AttnArgs a) {
   const uint16_t* ktb = (const uint16_t*)a.kt + kvb * a.T * HD;
   const uint16_t* vtb = (const uint16_t*)a.vt + kvb * a.T * HD;
 
-  // K/V tiles are staged global -> registers -> LDS; the loads of tile
-  // it+1 are issued before tile it is computed so their latency overlaps.
-  constexpr int CH = kAttnTile * (HD / 8) / 256;  // 16-byte chunks per thread
-  uint4 kreg[CH], vreg[CH];
-  auto load_tile = [&](int it) {
-    const bool tr = it >= nprefix;
-    const int k0 = (tr ? it - nprefix : t_begin + it) * kAttnTile;
-    const int km = tr ? a.T : P;
-    const uint16_t* Kg = tr ? ktb : kcb;
-    const uint16_t* Vg = tr ? vtb : vcb;
+  // Tiles go straight from global memory to LDS (global_load_lds_dwordx4:
+  // lane i of a wave writes bytes 16i..16i+15 of a 1 KB slab).  In LDS a
+  // tile is row-major [key][d] with the 16-byte chunk c of row r stored at
+  // chunk position c ^ (r % CPR): the direct loads cannot pad rows, and the
+  // XOR swizzle keeps the K reads and V transpose reads free of bank
+  // conflicts.  Keys past the end of the prefix, or past the last kept tree
+  // slot, load the last valid row instead: finite values whose scores are
+  // masked, so they add p = 0 times a finite V (tree rows past n_kept are
+  // the caller's unwritten memory and are never read).
+#define ET_ISSUE_TILE(T_, BUF_)                                               \
+  do {                                                                        \
+    const int t_ = (T_);                                                      \
+    const bool tr_ = t_ >= tp;                                                \
+    const int k0_ = (tr_ ? t_ - tp : t_) * kAttnTile;                         \
+    const int klast_ = (tr_ ? n + 1 : P) - 1;                                 \
+    const uint16_t* Kg_ = tr_ ? ktb : kcb;                                    \
+    const uint16_t* Vg_ = tr_ ? vtb : vcb;                                    \
+    _Pragma("unroll") for (int c_ = 0; c_ < CH; ++c_) {                       \
+      const int slab = c_ * 8 + wave;                                         \
+      const int q = slab * 64 + lane;                                         \
+      const int row = q / CPR, phys = q % CPR;                                \
+      const int64_t go = (int64_t)min(k0_ + row, klast_) * HD +               \
+                         ((phys ^ (row & (CPR - 1))) * 8);                    \
+      load_lds16(Kg_ + go, &sKV[(BUF_)][0][slab * 512]);                      \
+      load_lds16(Vg_ + go, &sKV[(BUF_)][1][slab * 512]);                      \
+    }                                                                         \
+  } while (0)
+
+  if (cnt > 0) ET_ISSUE_TILE(t_begin, 0);
+  if (cnt > 1) ET_ISSUE_TILE(t_begin + 1, 1);
+  // Q, the mask word and tile 0 have landed; tile 1 may still be in flight
+  if (cnt > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * CH));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  if (tid < 4 * BR) {
+    const int rr = me % BR, q = me / BR;
+    sMask[q][rr] = (row0 + rr < R && q < a.W) ? mword : 0ull;
+  }
+  __syncthreads();
+
+  const int sw = r16 & (CPR - 1);  // swizzle of the K rows this lane reads
+  for (int it = 0; it < cnt; ++it) {
+    const int cur = it % NB;
+    // buffer (it+2) % NB was last read in iteration it-1, before its barrier
+    if (it + 2 < cnt) ET_ISSUE_TILE(t_begin + it + 2, (it + 2) % NB);
+
+    const int t = t_begin + it;
+    const bool tree = t >= tp;
+    const int key0 = (tree ? t - tp : t) * kAttnTile;
+    const uint16_t* Ks = sKV[cur][0];
+    const uint16_t* Vs = sKV[cur][1];
+
+    // S^T = K . Q^T over this wave's 32 keys: lane holds row r16 and keys
+    // kh*32 + s2*16 + 4g + e.  kk outermost for independent accumulators.
+    f32x4_t sacc[WR][2];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + 256 * i;
-      const int kk = c / (HD / 8), d0 = (c % (HD / 8)) * 8;
-      kreg[i] = make_uint4(0u, 0u, 0u, 0u);
-      vreg[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (k0 + kk < km) {
-        kreg[i] = *(const uint4*)(Kg + (int64_t)(k0 + kk) * HD + d0);
-        vreg[i] = *(const uint4*)(Vg + (int64_t)(k0 + kk) * HD + d0);
-      }
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int w = 0; w < WR; ++w) sacc[w][s2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      bf16x8_t af[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        af[s2] = *(const bf16x8_t*)&Ks[(kh * 32 + s2 * 16 + r16) * HD + (((kk * 4 + g) ^ sw) * 8)];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int w = 0; w < WR; ++w)
+          sacc[w][s2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s2], qf[w][kk], sacc[w][s2], 0, 0, 0);
     }
-  };
-  if (total > 0) load_tile(0);
 
-  for (int it = 0; it < total; ++it) {
-    const bool tree = it >= nprefix;
-    const int tile = tree ? it - nprefix : t_begin + it;
-    const int key0 = tile * kAttnTile;
-
-    __syncthreads();
+    // Softmax in base 2 on unscaled scores: p = 2^(s*c - m).  The running
+    // max m is raised only when some row's tile max exceeds it by more
+    // than kSlack (a wave-uniform branch), so the O rescale is rare; the
+    // weights are then bounded by 2^kSlack, harmless in fp32 and bf16.
+    const bool full = !tree && key0 + kAttnTile <= P;
+    bf16x8_t pf[WR];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + 256 * i;
-      const int kk = c / (HD / 8), d0 = (c % (HD / 8)) * 8;
-      *(uint4*)&sK[kk * KPAD + d0] = kreg[i];
-      const uint32_t w4[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
+    for (int w = 0; w < WR; ++w) {
+      float sv[2][4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        sVt[(d0 + 2 * q) * VPAD + kk] = (uint16_t)(w4[q] & 0xFFFFu);
-        sVt[(d0 + 2 * q + 1) * VPAD + kk] = (uint16_t)(w4[q] >> 16);
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[s2][e] = sacc[w][s2][e];
+      if (!full) {
+        const uint64_t vm =
+            (tree ? sMask[key0 >> 6][rg * 16 * WR + w * 16 + r16]
+                  : (1ull << (P - key0)) - 1ull) >> (kh * 32 + g * 4);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (!((vm >> (s2 * 16 + e)) & 1ull)) sv[s2][e] = -INFINITY;
       }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sv[s2][e]);
+      tmax = fmaxf(tmax, xor_lane<16>(tmax));
+      tmax = fmaxf(tmax, xor_lane<32>(tmax));
+      const float tm = tmax * c;
+      if (__ballot(tm > m_run[w] + kSlack) != 0ull) {
+        const float m_new = fmaxf(m_run[w], tm);
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[w] - m_new);
+        m_run[w] = m_new;
+        lacc[w] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[w][dt] *= alpha;
+      }
+      // a row that has seen no visible key keeps m = -inf and gets p = 0
+      const float mu = m_run[w] == -INFINITY ? 0.f : m_run[w];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          pf[w][s2 * 4 + e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sv[s2][e], c, -mu));
     }
-    __syncthreads();
-    if (it + 1 < total) load_tile(it + 1);
 
-    // S^T = K . Q^T: lane holds row r16, keys sub*16 + 4g + i.
-    f32x4_t sacc[4];
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-      sacc[sub] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        bf16x8_t af = *(const bf16x8_t*)&sK[(sub * 16 + r16) * KPAD + kk * 32 + g * 8];
-        sacc[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[kk], sacc[sub], 0, 0, 0);
-      }
-    }
-
-    float sc[4][4];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = key0 + sub * 16 + g * 4 + i;
-        bool ok;
-        if (tree) ok = (pick_word(mrow, key >> 6) >> (key & 63)) & 1ull;
-        else ok = key < P;
-        float v = ok ? sacc[sub][i] * a.scale_log2 : -INFINITY;
-        sc[sub][i] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    tmax = fmaxf(tmax, xor_lane<16>(tmax));
-    tmax = fmaxf(tmax, xor_lane<32>(tmax));
-    // Branch-free: a row that has seen no visible key yet keeps m = -inf,
-    // alpha = 1 and p = 0 (the matrix instructions below need all lanes).
-    const float m_new = fmaxf(m_run, tmax);
-    const bool none = m_new == -INFINITY;
-    const float alpha = none ? 1.f : exp2f(m_run - m_new);
-    float psum = 0.f;
-    bf16x8_t pf[2];
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float p = none ? 0.f : exp2f(sc[sub][i] - m_new);
-        psum += p;
-        pf[sub >> 1][(sub & 1) * 4 + i] = (__bf16)p;
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-
-    // O^T += V^T . P^T over two 32-key steps.
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    // O^T += V^T . P^T over the wave's 32 keys; V^T by transpose reads.
+    // The reads are issued from inline assembly: the compiler cannot tell
+    // them apart from the direct loads still filling another buffer, and
+    // would otherwise wait for those loads (vmcnt(0)) before each read.
+    // The block waits for its own reads (lgkmcnt(0)) through in/out operands,
+    // so no use of the values can be scheduled before that wait.
+    {
+      u32x2_t vlo[DT], vhi[DT];
+      const int vrow = kh * 32 + g * 4 + (r16 >> 2);
+      const uint32_t vbase = lds_addr(Vs + vrow * HD) + (r16 & 1) * 8;
+      const int vsw = vrow & (CPR - 1);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint16_t* vr = &sVt[(dt * 16 + r16) * VPAD + ks * 32 + g * 4];
-        const uint2 lo = *(const uint2*)vr;
-        const uint2 hi = *(const uint2*)(vr + 16);
-        bf16x8_t af;
-        uint32_t* afw = (uint32_t*)&af;
-        afw[0] = lo.x;
-        afw[1] = lo.y;
-        afw[2] = hi.x;
-        afw[3] = hi.y;
-        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf[ks], oacc[dt], 0, 0, 0);
+        // this lane's source word: key row vrow (+16), d = dt*16 + 4*(r16%4)
+        const uint32_t va = vbase + (((dt * 2 + ((r16 >> 1) & 1)) ^ vsw) * 16);
+        vlo[dt] = ds_read_tr16(va);
+        vhi[dt] = HD == 128 ? ds_read_tr16_off4k(va) : ds_read_tr16_off2k(va);
       }
+      lds_wait_all(vlo, vhi);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        bf16x8_t af;
+        u32x2_t* afh = (u32x2_t*)&af;
+        afh[0] = vlo[dt];
+        afh[1] = vhi[dt];
+#pragma unroll
+        for (int w = 0; w < WR; ++w)
+          oacc[w][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf[w], oacc[w][dt], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < WR; ++w)
+      lacc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[w], lacc[w], 0, 0, 0);
+    // tile it+1 must have landed before the barrier; tile it+2 may fly on
+    if (it + 2 < cnt) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * CH));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    barrier_no_fence();
   }
 
-  l_run += xor_lane<16>(l_run);
-  l_run += xor_lane<32>(l_run);
-  if (r >= RT) return;
-  if (a.S == 1) {
-    uint16_t* orow = out + (((int64_t)b * a.T + slot) * a.Hq + kvh * a.G + gg) * HD;
-    const float inv = (rvalid && l_run > 0.f) ? 1.0f / l_run : 0.f;
+  // Combine the two key halves of every row group: the kh = 1 waves
+  // publish (m, l, O) in LDS (the tile buffers are idle now: every direct
+  // load has landed and every read has returned), the kh = 0 waves merge.
+  float* xo = (float*)&sKV[0][0][0];
+  float* xm = xo + 4 * WR * DT * 64 * 4;
+  float* xl = xm + 4 * WR * 16;
+  static_assert((4 * WR * DT * 64 * 4 + 2 * 4 * WR * 16) * 4 <= NB * 2 * TE * 2,
+                "the exchange fits in the tile buffers");
+  if (kh == 1) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      uint2 w;
-      w.x = (uint32_t)f32_to_bf16_rne(oacc[dt][0] * inv) |
-            ((uint32_t)f32_to_bf16_rne(oacc[dt][1] * inv) << 16);
-      w.y = (uint32_t)f32_to_bf16_rne(oacc[dt][2] * inv) |
-            ((uint32_t)f32_to_bf16_rne(oacc[dt][3] * inv) << 16);
-      *(uint2*)(orow + dt * 16 + g * 4) = w;
+    for (int w = 0; w < WR; ++w) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *(f32x4_t*)&xo[(((rg * WR + w) * DT + dt) * 64 + lane) * 4] = oacc[w][dt];
+      if (g == 0) {
+        xm[(rg * WR + w) * 16 + r16] = m_run[w];
+        xl[(rg * WR + w) * 16 + r16] = lacc[w][0];
+      }
     }
-  } else {
-    const int64_t pr = ((int64_t)(bh * a.nqb + qb) * a.S + split) * kAttnRows +
-                       wave * 16 + r16;
+  }
+  __syncthreads();
+  if (kh == 1) return;
+
+#pragma unroll
+  for (int w = 0; w < WR; ++w) {
+    const float m1 = xm[(rg * WR + w) * 16 + r16];
+    const float l1 = xl[(rg * WR + w) * 16 + r16];
+    const float m0 = m_run[w];
+    const float m = fmaxf(m0, m1);
+    const float f0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - m);
+    const float f1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+    const float l = lacc[w][0] * f0 + l1 * f1;
+    f32x4_t o[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-      *(f32x4_t*)(a.po + pr * HD + dt * 16 + g * 4) = oacc[dt];
-    if (g == 0) {
-      a.pm[pr] = m_run;
-      a.pl[pr] = l_run;
+      o[dt] = oacc[w][dt] * f0 +
+              *(const f32x4_t*)&xo[(((rg * WR + w) * DT + dt) * 64 + lane) * 4] * f1;
+    const int rr = rg * 16 * WR + w * 16 + r16;
+    const int r = row0 + rr;
+    if (r >= RT) continue;
+    if (a.S == 1) {
+      const int slot = r / a.G, gg = r - slot * a.G;
+      uint16_t* orow = out + (((int64_t)b * a.T + slot) * a.Hq + kvh * a.G + gg) * HD;
+      const float inv = (r < R && l > 0.f) ? 1.0f / l : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        uint2 wv;
+        wv.x = (uint32_t)f32_to_bf16_rne(o[dt][0] * inv) |
+               ((uint32_t)f32_to_bf16_rne(o[dt][1] * inv) << 16);
+        wv.y = (uint32_t)f32_to_bf16_rne(o[dt][2] * inv) |
+               ((uint32_t)f32_to_bf16_rne(o[dt][3] * inv) << 16);
+        *(uint2*)(orow + dt * 16 + g * 4) = wv;
+      }
+    } else {
+      const int64_t pr = ((int64_t)(unit * a.nqb + qb) * a.S + split) * BR + rr;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) *(f32x4_t*)(a.po + pr * HD + dt * 16 + g * 4) = o[dt];
+      if (g == 0) {
+        a.pm[pr] = m;
+        a.pl[pr] = l;
+      }
     }
   }
 }
 
-// Combine the S split partials: o = sum_i O_i 2^(m_i - m) / l.  Grid
-// (nqb * 16, B * Hkv); a block covers 4 rows; thread = (row, 4 columns).
-// All of a thread's loads are independent, so they are issued together.
-template <int HD>
+#undef ET_ISSUE_TILE
+
+// Combine the S split partials: o = sum_i O_i 2^(m_i - m) / l.  A block
+// covers RPB rows of one (unit, row block); thread = (row, 4 columns).
+// Blocks map to XCDs like the main kernel, so the partials are read from
+// the L2 they were written to.  Every load of a thread is independent and
+// issued up front.
+template <int HD, int WR>
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a) {
-  constexpr int TPR = HD / 4;            // threads per row
-  constexpr int RPB = 256 / TPR;         // rows per block
-  const int qb = blockIdx.x / (kAttnRows / RPB);
-  const int rr = (blockIdx.x % (kAttnRows / RPB)) * RPB + threadIdx.x / TPR;
+  constexpr int TPR = HD / 4;     // threads per row
+  constexpr int RPB = 256 / TPR;  // rows per block
+  constexpr int BR = 64 * WR;
+  constexpr int MB = BR / RPB;    // merge blocks per (unit, row block)
+  int unit, rem;
+  if (!attn_block_coords(blockIdx.x, a.B * a.Hkv, a.nqb * MB, &unit, &rem)) return;
+  const int qb = rem / MB, mb = rem - qb * MB;
+  const int rr = mb * RPB + threadIdx.x / TPR;
   const int col = (threadIdx.x % TPR) * 4;
-  const int bh = blockIdx.y;
-  const int b = bh / a.Hkv, kvh = bh - b * a.Hkv;
-  const int r = qb * kAttnRows + rr;
+  const int b = unit / a.Hkv, kvh = unit - b * a.Hkv;
+  const int r = qb * BR + rr;
   const int RT = a.T * a.G;
   if (r >= RT) return;
   const int R = (a.n_kept[b] + 1) * a.G;
@@ -293,24 +486,34 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a) {
     *(uint2*)orow = make_uint2(0u, 0u);
     return;
   }
-  const int64_t base = (int64_t)(bh * a.nqb + qb) * a.S;
-  constexpr int kMaxS = 64;
+  const int64_t base = (int64_t)(unit * a.nqb + qb) * a.S;
+  float mi[kAttnMaxSplits], li[kAttnMaxSplits];
+  float4 oi[kAttnMaxSplits];
+#pragma unroll
+  for (int i = 0; i < kAttnMaxSplits; ++i) {
+    mi[i] = -INFINITY;
+    li[i] = 0.f;
+    oi[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < a.S) {
+      const int64_t pr = (base + i) * BR + rr;
+      mi[i] = a.pm[pr];
+      li[i] = a.pl[pr];
+      oi[i] = *(const float4*)(a.po + pr * HD + col);
+    }
+  }
   float m = -INFINITY;
-  for (int i = 0; i < a.S; ++i) m = fmaxf(m, a.pm[(base + i) * kAttnRows + rr]);
+#pragma unroll
+  for (int i = 0; i < kAttnMaxSplits; ++i) m = fmaxf(m, mi[i]);
   float l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-  for (int i = 0; i < kMaxS; ++i) {
-    if (i >= a.S) break;
-    const int64_t pr = (base + i) * kAttnRows + rr;
-    const float mi = a.pm[pr];
-    const float f = mi == -INFINITY ? 0.f : exp2f(mi - m);
-    const float4 v = *(const float4*)(a.po + pr * HD + col);
-    l += a.pl[pr] * f;
-    acc.x += v.x * f;
-    acc.y += v.y * f;
-    acc.z += v.z * f;
-    acc.w += v.w * f;
+#pragma unroll
+  for (int i = 0; i < kAttnMaxSplits; ++i) {
+    const float f = mi[i] == -INFINITY ? 0.f : exp2f(mi[i] - m);
+    l += li[i] * f;
+    acc.x += oi[i].x * f;
+    acc.y += oi[i].y * f;
+    acc.z += oi[i].z * f;
+    acc.w += oi[i].w * f;
   }
   const float inv = l > 0.f ? 1.0f / l : 0.f;
   uint2 w;
@@ -427,14 +630,24 @@ hipError_t launch_tree_attention(const Plan& p, const AttnWs& w,
     tree_attn_f32_kernel<<<dim3(p.T, p.Hq, p.B), 256, 0, s>>>(a, p.HD);
     return hipGetLastError();
   }
-  dim3 grid(p.attn_splits, p.attn_nqb, p.B * p.Hkv);
-  if (p.HD == 128) tree_attn_bf16_kernel<128><<<grid, 256, 0, s>>>(a);
-  else tree_attn_bf16_kernel<64><<<grid, 256, 0, s>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.attn_splits == 1) return e;
-  dim3 mgrid(p.attn_nqb * (kAttnRows / (256 / (p.HD / 4))), p.B * p.Hkv);
-  if (p.HD == 128) tree_attn_merge_kernel<128><<<mgrid, 256, 0, s>>>(a);
-  else tree_attn_merge_kernel<64><<<mgrid, 256, 0, s>>>(a);
+  const int units8 = (p.B * p.Hkv + 7) / 8 * 8;  // whole units per XCD
+  const int blocks = units8 * p.attn_nqb * p.attn_splits;
+#define ET_ATTN(HD, WR)                                                          \
+  do {                                                                           \
+    tree_attn_bf16_kernel<HD, WR><<<blocks, 512, 0, s>>>(a);                     \
+    hipError_t e = hipGetLastError();                                            \
+    if (e != hipSuccess || p.attn_splits == 1) return e;                         \
+    tree_attn_merge_kernel<HD, WR>                                               \
+        <<<units8 * p.attn_nqb * (64 * WR / (256 / (HD / 4))), 256, 0, s>>>(a);  \
+  } while (0)
+  if (p.HD == 128) {
+    if (p.attn_wr == 2) ET_ATTN(128, 2);
+    else ET_ATTN(128, 1);
+  } else {
+    if (p.attn_wr == 2) ET_ATTN(64, 2);
+    else ET_ATTN(64, 1);
+  }
+#undef ET_ATTN
   return hipGetLastError();
 }
 

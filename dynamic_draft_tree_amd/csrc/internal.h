@@ -35,8 +35,9 @@ constexpr int kElemsF32 = 16;            // fp32 elements per thread (4 x 16 B)
 constexpr int chunk_elems(int dtype) {
   return kScanThreads * (dtype == ET_BF16 ? kElemsBf16 : kElemsF32);
 }
-constexpr int kAttnRows = 64;            // query rows per attention block
 constexpr int kAttnTile = 64;            // keys per staged K/V tile
+constexpr int kAttnMaxSplits = 32;       // key splits per (kv head, row block)
+constexpr int kAttnTargetBlocks = 256;   // blocks the split count aims for
 
 struct DraftWs {
   uint32_t* row_ticket;   // [B][k]
@@ -66,8 +67,8 @@ struct AcceptWs {
 };
 
 struct AttnWs {
-  float* o;               // [B*Hkv][nqb][S][kAttnRows][d]
-  float* m;               // [B*Hkv][nqb][S][kAttnRows]
+  float* o;               // [B*Hkv][nqb][S][rows per block][d]
+  float* m;               // [B*Hkv][nqb][S][rows per block]
   float* l;
 };
 
@@ -77,6 +78,7 @@ struct Plan {
   int Hq, Hkv, G, HD, Pcap;
   int ldt, qdt;           // et_dtype of logits and q/k/v
   int s_draft;            // vocab chunks per row
+  int attn_wr;            // 16-row groups per wave (rows per block 64*wr)
   int attn_nqb, attn_splits;
   // workspace layout
   size_t off_counters, n_counters;

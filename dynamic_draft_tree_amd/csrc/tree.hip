@@ -28,48 +28,134 @@ struct RerankArgs {
   int B, N, T, cap;
 };
 
-// One block per sequence.  Pool keys (value, -depth, -token, -index) are
-// sorted descending in LDS with a bitonic network; the first n = min(N,
-// pool) ranks become slots 1..n.  A parent's key exceeds its child's key
-// (value(child) = value(parent) * conf <= value(parent), and equal values
-// fall back to the shallower depth), so rank order is topological.
+// One block per sequence.  Pool keys (value, -depth, -token, -index) order
+// the nodes totally.  A parent's key exceeds its child's key (value(child)
+// = value(parent) * conf <= value(parent), and equal values fall back to
+// the shallower depth), so rank order is topological.
+//
+// Selection of the n = min(N, pool) largest keys is a radix select from
+// the top: a 256-bucket histogram of the next 8 key bits, restricted to
+// the keys that share the prefix chosen so far, picks the bucket where the
+// count from the top first reaches n.  Usually two levels (value exponent
+// and leading mantissa bits) leave at most kRerankCand keys at or above
+// the prefix; further levels run only while more remain.  Keys are
+// distinct (the index field), so the eighth level leaves exactly n.  The
+// survivors are ranked by counting in LDS.
+constexpr int kRerankCand = 1024;
+
+// Wave 0: find the largest bucket c of hist[0..255] whose suffix count
+// (sum of hist[c..255]) reaches `need`; returns c and the count above c.
+__device__ __forceinline__ void suffix_pick(const uint32_t* hist, int need,
+                                            int* bucket, int* above) {
+  const int lane = threadIdx.x & 63;
+  uint32_t h[4];
+  // lane l holds buckets 255 - 4l - q (q = 0..3): descending order
+#pragma unroll
+  for (int q = 0; q < 4; ++q) h[q] = hist[255 - 4 * lane - q];
+  const uint32_t mine = h[0] + h[1] + h[2] + h[3];
+  // inclusive prefix over lanes (lane 0 = highest buckets)
+  uint32_t inc = mine;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_up(inc, d);
+    if (lane >= d) inc += o;
+  }
+  uint32_t run = inc - mine;  // count strictly above this lane's buckets
+  int found = -1, ab = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (found < 0 && run + h[q] >= (uint32_t)need) {
+      found = 255 - 4 * lane - q;
+      ab = (int)run;
+    }
+    run += h[q];
+  }
+  // the first lane (highest buckets) that reaches `need` holds the answer
+  const uint64_t bal = __ballot(found >= 0);
+  const int src = bal ? (int)__ffsll((unsigned long long)bal) - 1 : 0;
+  *bucket = __shfl(found, src);
+  *above = __shfl(ab, src);
+}
+
 __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(RerankArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x;
-  __shared__ uint64_t s_key[kRerankMaxPool];
+  __shared__ uint64_t s_key[kMaxBudget + 1];  // rank -> key
+  __shared__ uint64_t s_cand[kRerankCand];
   __shared__ int16_t s_slot[kRerankMaxPool];
+  __shared__ uint32_t s_hist[256];
+  __shared__ int s_pick, s_above, s_count;
   const int64_t pb = (int64_t)b * a.cap;
   const int P = a.ws.pool_count[b];
-  int Pp = 2;
-  while (Pp < P) Pp <<= 1;
-  for (int i = tid; i < Pp; i += kRerankThreads) {
-    uint64_t key = 0;
-    if (i < P)
-      key = pool_key(a.ws.pool_value[pb + i], a.ws.pool_depth[pb + i],
-                     a.ws.pool_token[pb + i], i);
-    s_key[i] = key;
-    s_slot[i] = -1;
+  const int n = P < a.N ? P : a.N;
+  constexpr int PER = kRerankMaxPool / kRerankThreads;
+  uint64_t key[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = tid + kRerankThreads * i;
+    key[i] = 0;
+    if (idx < P)
+      key[i] = pool_key(a.ws.pool_value[pb + idx], a.ws.pool_depth[pb + idx],
+                        a.ws.pool_token[pb + idx], idx);
+    s_slot[idx] = -1;
+  }
+  if (tid == 0) s_count = 0;
+  uint64_t prefix = 0;  // chosen high key bits, right-aligned
+  int above = 0;        // keys strictly above the chosen prefix
+  int cnt = 0;          // keys at or above it
+  int shift = 64;
+  for (int level = 0; level < 8 && n > 0; ++level) {
+    if (tid < 256) s_hist[tid] = 0;
+    __syncthreads();
+    const int sh = shift - 8;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const bool in = key[i] != 0 && (level == 0 || (key[i] >> shift) == prefix);
+      if (in) atomicAdd(&s_hist[(key[i] >> sh) & 0xFFu], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      int c, ab;
+      suffix_pick(s_hist, n - above, &c, &ab);
+      if (tid == 0) {
+        s_pick = c;
+        s_above = ab;
+      }
+    }
+    __syncthreads();
+    const int c = s_pick;
+    prefix = (prefix << 8) | (uint64_t)c;
+    above += s_above;
+    cnt = above + (int)s_hist[c];
+    shift = sh;
+    __syncthreads();  // s_hist and s_pick are rewritten by the next level
+    if (cnt <= kRerankCand) break;
+  }
+  const uint64_t T = prefix << shift;
+  const int64_t ob = (int64_t)b * a.T;
+  if (n > 0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (key[i] != 0 && key[i] >= T) s_cand[atomicAdd(&s_count, 1)] = key[i];
+    __syncthreads();
+    for (int t = tid; t < cnt; t += kRerankThreads) {
+      const uint64_t me = s_cand[t];
+      int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+      int j = 0;
+      for (; j + 4 <= cnt; j += 4) {
+        r0 += s_cand[j] > me;
+        r1 += s_cand[j + 1] > me;
+        r2 += s_cand[j + 2] > me;
+        r3 += s_cand[j + 3] > me;
+      }
+      for (; j < cnt; ++j) r0 += s_cand[j] > me;
+      const int rank = (r0 + r1) + (r2 + r3);
+      if (rank < n) {
+        s_key[rank] = me;
+        s_slot[pool_index_of(me)] = (int16_t)(rank + 1);
+      }
+    }
   }
   __syncthreads();
-  for (int k = 2; k <= Pp; k <<= 1)
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < Pp; i += kRerankThreads) {
-        int ixj = i ^ j;
-        if (ixj > i) {
-          uint64_t x = s_key[i], y = s_key[ixj];
-          bool desc = (i & k) == 0;
-          if (desc ? (x < y) : (x > y)) {
-            s_key[i] = y;
-            s_key[ixj] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  const int n = P < a.N ? P : a.N;
-  for (int r = tid; r < n; r += kRerankThreads)
-    s_slot[pool_index_of(s_key[r])] = (int16_t)(r + 1);
-  __syncthreads();
-  const int64_t ob = (int64_t)b * a.T;
   for (int s = tid; s < a.T; s += kRerankThreads) {
     int tok = -1, ps = -1;
     float cf = 0.f, vl = 0.f;
@@ -78,8 +164,8 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(RerankArgs a) {
       cf = 1.f;
       vl = 1.f;
     } else if (s <= n) {
-      int idx = pool_index_of(s_key[s - 1]);
-      int par = a.ws.pool_parent[pb + idx];
+      const int idx = pool_index_of(s_key[s - 1]);
+      const int par = a.ws.pool_parent[pb + idx];
       tok = a.ws.pool_token[pb + idx];
       ps = par < 0 ? 0 : s_slot[par];
       cf = a.ws.pool_conf[pb + idx];
