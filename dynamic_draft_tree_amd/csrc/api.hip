@@ -278,7 +278,7 @@ int et_draft_step(et_plan_t plan, void* ws, int32_t step,
                 "workspace", fn, step, p.last_step);
   const int per = p.ldt == ET_BF16 ? 8 : 4;
   const bool vec = aligned16(logits) && batch_stride % per == 0 &&
-                   row_stride % per == 0;
+                   row_stride % per == 0 && p.V >= per;
   int rc = hip_status(
       et::launch_draft_step(p, et::draft_ws(p, ws), step, root_tokens, logits,
                             batch_stride, row_stride, vec, next_tokens,
@@ -390,7 +390,7 @@ int et_accept(et_plan_t plan, void* ws, const void* target_logits,
     return fail(ET_EINVAL, "%s: workspace not 256-byte aligned", fn);
   const int per = p.ldt == ET_BF16 ? 8 : 4;
   const bool vec = aligned16(target_logits) && batch_stride % per == 0 &&
-                   row_stride % per == 0;
+                   row_stride % per == 0 && p.V >= per;
   return hip_status(
       et::launch_accept(p, et::accept_ws(p, ws), target_logits, batch_stride,
                         row_stride, vec, tokens, parent_slot, n_kept,

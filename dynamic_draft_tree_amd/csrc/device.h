@@ -445,22 +445,31 @@ __device__ __forceinline__ void load_chunk(const void* row, int base, int V,
                                            int tid, float (&x)[E]) {
   constexpr int per = BF16 ? 8 : 4;
   if constexpr (VEC) {
+    // All vector loads are issued before any is used: a vector that runs
+    // past the row end loads the row's first vector instead (in bounds,
+    // as the vector path needs V >= per) and is redone element-wise.
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    constexpr int NV = E / per;
+    u32x4_t raw[NV];
 #pragma unroll
-    for (int i = 0; i < E / per; ++i) {
+    for (int i = 0; i < NV; ++i) {
       const int off = base + (i * kLoadThreads + tid) * per;
-      if (off + per <= V) {
-        const uint4 u = *(const uint4*)((const char*)row + (size_t)off * (BF16 ? 2 : 4));
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+      const int src = off + per <= V ? off : 0;
+      raw[i] = *(const u32x4_t*)((const char*)row + (size_t)src * (BF16 ? 2 : 4));
+    }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if constexpr (BF16) {
-            x[i * 8 + 2 * q] = __uint_as_float(w[q] << 16);
-            x[i * 8 + 2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
-          } else {
-            x[i * 4 + q] = __uint_as_float(w[q]);
-          }
+    for (int i = 0; i < NV; ++i) {
+      const int off = base + (i * kLoadThreads + tid) * per;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (BF16) {
+          x[i * 8 + 2 * q] = __uint_as_float(raw[i][q] << 16);
+          x[i * 8 + 2 * q + 1] = __uint_as_float(raw[i][q] & 0xFFFF0000u);
+        } else {
+          x[i * 4 + q] = __uint_as_float(raw[i][q]);
         }
-      } else {
+      }
+      if (off + per > V) {
 #pragma unroll
         for (int u = 0; u < per; ++u)
           x[i * per + u] = off + u < V

@@ -8,12 +8,12 @@
 // stage: nodes whose value is below the threshold are not expanded.
 //
 // One launch per step.  Grid (S chunks, k frontier rows, B sequences),
-// 256 threads.  Each block streams one 4096-element chunk of one logits
-// row with 16-byte loads and produces (max, sum of exp, top-k keys).  The
-// last block to finish a row merges that row's S partials; the last row to
-// finish a sequence turns the rows into children (conf, value), appends
-// them to the pool and selects the next frontier.  No host sync, no
-// second launch.
+// 256 threads.  Each block streams one chunk of one logits row with
+// 16-byte loads and publishes the chunk's (max, sum of exp) and its top-k
+// logit keys.  The last block of a sequence to finish (one arrival
+// ticket over all F x S blocks) merges every row of that sequence, turns
+// the rows into children (conf, value), appends them to the pool and
+// selects the next frontier.  No host sync, no second launch.
 #include "device.h"
 #include "internal.h"
 
@@ -30,11 +30,38 @@ struct DraftArgs {
   float thr;
 };
 
-constexpr int kCandCap = 512;            // LDS candidate slots per block
 constexpr int kWaves = kScanThreads / 64;  // waves per scan block
-// wave-list keys of one row: (max chunks per row) * waves * k
-constexpr int row_keys_cap(int E) {
-  return ((kMaxVocab + kScanThreads * E - 1) / (kScanThreads * E)) * kWaves * kMaxTopk;
+constexpr int kWaveCap = 64;             // candidate slots per wave
+constexpr int kMaxChunks = 64;           // chunks per row (fp32, V = 2^18)
+constexpr int kStage = 4;                // keys per chunk list read up front
+constexpr int kRowCap = 64;              // merge candidates per row
+
+// The k-th largest of the wave's 64 keys (k <= 64): the largest T whose
+// count of keys >= T is at least k, built bit by bit from the top (bits
+// below `lo` are known to be zero in every key).  One compare and one
+// ballot per bit, no data exchange.
+__device__ __forceinline__ uint32_t wave_kth_largest_u32(uint32_t key, int k, int lo) {
+  uint32_t t = 0;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    if (bit < lo) break;
+    const uint32_t cand = t | (1u << bit);
+    if (__popcll(__ballot(key >= cand)) >= k) t = cand;
+  }
+  return t;
+}
+// The same over float values through their order-preserving image; values
+// from bf16 have 16 significant bits.  (For negative bf16 values the image
+// has ones in its low bits, so the result can sit slightly below the exact
+// k-th largest: still a lower bound.)
+template <bool BF16>
+__device__ __forceinline__ float wave_kth_largest(float v, int k) {
+  return unordered_f32(wave_kth_largest_u32(ordered_f32(v), k, BF16 ? 16 : 0));
+}
+
+// Smallest logit key whose logit is >= x.
+__device__ __forceinline__ uint64_t key_floor(float x) {
+  return (uint64_t)ordered_f32(x) << 32;
 }
 
 template <bool BF16, bool VEC, int E>
@@ -44,14 +71,19 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
   constexpr float kLog2e = 1.4426950408889634f;
   const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int k = a.k;
-  __shared__ uint64_t s_keys[kCandCap];  // also 4 x 128 wave scratch
-  constexpr int kRowKeys = row_keys_cap(E);
-  __shared__ uint64_t s_aux[kRowKeys];
-  __shared__ uint64_t s_top[kMaxTopk];
-  __shared__ uint64_t s_red[kWaves];
+  const int k = a.k, S = a.S;
+  __shared__ __attribute__((aligned(16))) float s_x[kScanThreads * E];  // lane values
+  __shared__ uint64_t s_wl[kWaves * kWaveCap];  // wave candidate lists
+  __shared__ uint64_t s_bc[kWaves * kWaveCap];  // block candidates
+  __shared__ float s_wf[3][kWaves];             // wave bound, max, sum
+  __shared__ int s_wcnt[kWaves];
   __shared__ int s_count;
   __shared__ int s_flag;
+  // merge (last block of the sequence)
+  __shared__ float s_rm[kMaxTopk], s_rs[kMaxTopk];
+  __shared__ uint64_t s_rc[kMaxTopk * kRowCap];   // row candidates
+  __shared__ uint64_t s_rk[kMaxTopk * kMaxTopk];  // row top-k keys
+  __shared__ uint64_t s_aux[256];
 
   const int prev = (a.step - 1) & 1, cur = a.step & 1;
   const int F = a.step == 1 ? 1 : a.ws.frontier_count[prev * a.B + b];
@@ -69,12 +101,13 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
   }
   if (j >= F) return;
 
-  // ---- stream one chunk: per wave max, sum of exp and top-k -------------
+  // ---- stream one chunk: per wave max, sum of exp and candidates ---------
   const int64_t esz = BF16 ? 2 : 4;
   const char* row = (const char*)a.logits + (b * a.bstride + j * a.rstride) * esz;
   const int base = c * kChunkE;
   float x[E];
   load_chunk<BF16, VEC, E>(row, base, a.V, tid, x);
+  if (tid == 0) s_count = 0;
   // phase: chunk loaded
 
   // Lane max as a pairwise tree (short dependency chain).
@@ -102,42 +135,33 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
   // phase: max and sum of exp
   // The wave's k-th largest lane maximum Lw bounds its k-th largest
   // element from below (those k maxima are k distinct elements), so every
-  // element of the wave's top-k is >= Lw.  Those elements are compacted
-  // into LDS with ballots (branch-free: non-candidates write a spare slot)
-  // and ranked by counting; each lands at its rank.
-  const float Lw = readlane_f32(wave_sort_desc_f32(lmax), k - 1);
+  // element of the wave's top-k is >= Lw.  Each lane marks its elements
+  // >= Lw in a bit mask; a wave prefix sum of the counts gives each lane
+  // its slots, and the lane writes its (usually zero to two) candidates.
+  const float Lw = wave_kth_largest<BF16>(lmax, k);
   // phase: wave threshold
-  uint64_t* scr = &s_keys[wave * 128];
-  int total = 0;
+  uint32_t bits = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int id = base + elem_off<BF16>(e, tid);
-    const bool pred = id < a.V && x[e] >= Lw;
-    int n_e;
-    const int r = ballot_rank(pred, &n_e);
-    if (n_e != 0 && pred && total + r < 64) scr[total + r] = logit_key(x[e], (uint32_t)id);
-    total += n_e;
+    bits |= (id < a.V && x[e] >= Lw) ? (1u << e) : 0u;
   }
-  wave_lds_sync();
-  // phase: wave candidates
-  const int64_t rowid = (int64_t)b * k + j;
-  const int64_t pidx = (rowid * a.S + c) * kWaves + wave;
-  uint64_t* dst = &a.ws.part_keys[pidx * kMaxTopk];
-  if (total <= 64) {
-    // candidate q sits in lane q; compare against each by readlane
-    const uint64_t me = lane < total ? scr[lane] : 0;
-    int r0 = 0, r1 = 0;
-    int q = 0;
-    for (; q + 2 <= total; q += 2) {
-      r0 += readlane_u64(me, q) > me;
-      r1 += readlane_u64(me, q + 1) > me;
+  int wtot;
+  int o = wave_excl_prefix_small(__popc(bits), &wtot);
+  uint64_t* wl = &s_wl[wave * kWaveCap];
+  if (wtot <= kWaveCap) {
+    // The lane's values are staged in LDS so that each candidate is read
+    // by index (a register array cannot be indexed at run time cheaply).
+    float* xs = &s_x[tid * E];
+#pragma unroll
+    for (int e = 0; e < E; e += 4) *(float4*)&xs[e] = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
+    while (bits) {
+      const int e = __ffs(bits) - 1;
+      bits &= bits - 1;
+      wl[o++] = logit_key(xs[e], (uint32_t)(base + elem_off<BF16>(e, tid)));
     }
-    if (q < total) r0 += readlane_u64(me, q) > me;
-    const int rank = r0 + r1;
-    if (lane < total && rank < k) st_agent(&dst[rank], me);
-    if (lane >= total && lane < k) st_agent(&dst[lane], (uint64_t)0);
   } else {
-    // Many equal logits: k rounds of wave-wide maximum over the registers.
+    // Many equal logits: the wave's exact top-k, by k rounds of maximum.
     uint64_t prevk = ~0ull;
     for (int r = 0; r < k; ++r) {
       uint64_t best = 0;
@@ -148,80 +172,189 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
         if (key < prevk && key > best) best = key;
       }
       const uint64_t w = wave_max_u64(best);
-      if (lane == 0) st_agent(&dst[r], w);
+      if (lane == 0) wl[r] = w;
       prevk = w;
     }
+    wtot = k;
   }
-  // phase: wave top-k
   if (lane == 0) {
-    st_agent(&a.ws.part_m[pidx], mw);
-    st_agent(&a.ws.part_s[pidx], sw);
+    s_wcnt[wave] = wtot;
+    s_wf[0][wave] = Lw;
+    s_wf[1][wave] = mw;
+    s_wf[2][wave] = sw;
   }
-
-  // phase: partial published
-  // ---- last block of this row: merge the S chunk partials --------------
-  if (!block_arrive_last(&a.ws.row_ticket[rowid], (uint32_t)a.S, &s_flag)) return;
+  __syncthreads();
+  // phase: wave candidates
+  // Block: the largest wave bound bounds the block's k-th largest element
+  // from below; the candidates at or above it are ranked by counting.
+  float Lb = s_wf[0][0], mb = s_wf[1][0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    Lb = fmaxf(Lb, s_wf[0][w]);
+    mb = fmaxf(mb, s_wf[1][w]);
+  }
   {
-    const int nl = a.S * kWaves;  // sorted wave lists of this row (<= 256)
-    const int64_t p0 = rowid * a.S * kWaves;
-    const int nk = nl * k;        // <= kRowKeys
-    for (int t = tid; t < nk; t += NT) {
-      const int li = t / k, r = t - li * k;
-      s_aux[t] = ld_agent(&a.ws.part_keys[(p0 + li) * kMaxTopk + r]);
+    const int w = tid / kWaveCap, i = tid - w * kWaveCap;
+    if (i < s_wcnt[w]) {
+      const uint64_t v = s_wl[tid];
+      if (v != 0 && v >= key_floor(Lb)) s_bc[atomicAdd(&s_count, 1)] = v;
     }
-    const float pm = tid < nl ? ld_agent(&a.ws.part_m[p0 + tid]) : -INFINITY;
-    const float ps = tid < nl ? ld_agent(&a.ws.part_s[p0 + tid]) : 0.f;
-    // phase: row partials read
-    // (max, sum of exp) over the nl wave partials, in fp32
-    const float m = block_max_f32<NT>(pm, (float*)s_red);
-    const float sc = pm > -INFINITY ? ps * expf(pm - m) : 0.f;
-    const float srow = block_sum_f32<NT>(sc, (float*)s_red);
-    if (tid == 0) {
-      st_agent(&a.ws.row_m[rowid], m);
-      st_agent(&a.ws.row_s[rowid], srow);
+  }
+  __syncthreads();
+  const int nb = s_count;
+  const int64_t rowid = (int64_t)b * k + j;
+  const int64_t pe = rowid * S + c;  // this block's partial entry
+  uint64_t* dst = &a.ws.part_keys[pe * kMaxTopk];
+  for (int t = tid; t < nb; t += NT) {
+    const uint64_t me = s_bc[t];
+    int rank = 0;
+#pragma unroll 8
+    for (int q = 0; q < nb; ++q) rank += s_bc[q] > me;
+    if (rank < k) st_agent(&dst[rank], me);
+  }
+  if (tid >= nb && tid < k) st_agent(&dst[tid], (uint64_t)0);
+  if (tid == 0) {
+    float sb = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      sb += s_wf[1][w] > -INFINITY ? s_wf[2][w] * expf(s_wf[1][w] - mb) : 0.f;
+    st_agent(&a.ws.part_m[pe], mb);
+    st_agent(&a.ws.part_s[pe], sb);
+  }
+  // phase: partial published
+
+  // ---- last block of this sequence: merge every row ---------------------
+  if (!block_arrive_last(&a.ws.seq_ticket[b], (uint32_t)(F * S), &s_flag)) return;
+  // phase: sequence ticket won
+  // ---- row merges: a segment of SP lanes per row ------------------------
+  // SP is the power of two >= S, so a wave merges 64 / SP rows at once and
+  // lane q of a segment holds chunk q's (max, sum) and the first kStage
+  // keys of its sorted list.  The row's max and sum of exp are segment
+  // reductions.  Bound: with at least k chunks the k-th largest chunk head
+  // bounds the row's k-th largest key from below, so only keys at or above
+  // it (a prefix of every chunk's list) are ranked.
+  const int64_t e0 = (int64_t)b * k * S;  // first partial of the sequence
+  int SP = 1;
+  while (SP < S) SP <<= 1;
+  const int RW = 64 / SP;                 // rows per wave
+  const int seg = lane / SP, q = lane - seg * SP;
+  const uint64_t segmask = SP == 64 ? ~0ull : ((1ull << SP) - 1ull) << (seg * SP);
+  const uint64_t below = segmask & ((1ull << lane) - 1ull);
+  for (int r0 = 0; r0 < F; r0 += kWaves * RW) {
+    const int jr = r0 + wave * RW + seg;
+    const bool on = jr < F && q < S;
+    const int64_t e = e0 + (int64_t)jr * S + q;
+    const float pm = on ? ld_agent(&a.ws.part_m[e]) : -INFINITY;
+    const float ps = on ? ld_agent(&a.ws.part_s[e]) : 0.f;
+    uint64_t pk[kMaxTopk];
+#pragma unroll
+    for (int r = 0; r < kMaxTopk; ++r)
+      pk[r] = (on && r < kStage && r < k) ? ld_agent(&a.ws.part_keys[e * kMaxTopk + r]) : 0;
+    // phase: partials read
+    float m = pm;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1)
+      if (d < SP) m = fmaxf(m, xor_lane_rt(m, d));
+    float sum = pm > -INFINITY ? ps * __builtin_amdgcn_exp2f((pm - m) * kLog2e) : 0.f;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1)
+      if (d < SP) sum += xor_lane_rt(sum, d);
+    // phase: row max and sum
+    // k-th largest head of the segment, bit by bit on the ordered logit
+    uint64_t Lk = 0;
+    if (S >= k) {
+      const uint32_t hk = on && pk[0] != 0 ? (uint32_t)(pk[0] >> 32) : 0u;
+      uint32_t t = 0;
+#pragma unroll
+      for (int bit = 31; bit >= (BF16 ? 16 : 0); --bit) {
+        const uint32_t cand = t | (1u << bit);
+        if (__popcll(__ballot(hk >= cand) & segmask) >= k) t = cand;
+      }
+      Lk = (uint64_t)t << 32;
     }
-    // Each wave list is sorted, so with at least k lists the k-th largest
-    // head bounds the row's k-th largest key from below; rank only the
-    // keys above it (with fewer lists every key is a candidate).
-    __syncthreads();
-    if (tid < nl) s_keys[tid] = s_aux[tid * k];
-    // phase: row sum published
-    uint64_t Lh = 1;
-    if (nl >= k) {
-      block_topk<NT>(s_keys, nl, k, s_top, s_red);
-      Lh = s_top[k - 1];
-    }
-    if (tid == 0) s_count = 0;
-    __syncthreads();
-    // phase: row threshold
-    for (int t = tid; t < nk; t += NT) {
-      const uint64_t v = s_aux[t];
-      if (v >= Lh && v != 0) {
-        const int slot = atomicAdd(&s_count, 1);
-        if (slot < kCandCap) s_keys[slot] = v;
+    // phase: row bound
+    int cq = 0;
+#pragma unroll
+    for (int r = 0; r < kStage; ++r) cq += (pk[r] != 0 && pk[r] >= Lk) ? 1 : 0;
+    if (__ballot(cq == kStage && k > kStage) != 0ull) {
+      // rare: a list qualifies beyond its staged keys
+      if (cq == kStage) {
+#pragma unroll
+        for (int r = kStage; r < kMaxTopk; ++r)
+          if (r < k) pk[r] = ld_agent(&a.ws.part_keys[e * kMaxTopk + r]);
+#pragma unroll
+        for (int r = kStage; r < kMaxTopk; ++r)
+          cq += (r < k && pk[r] != 0 && pk[r] >= Lk) ? 1 : 0;
       }
     }
-    __syncthreads();
-    if (s_count <= kCandCap) block_topk<NT>(s_keys, s_count, k, s_top, s_red);
-    else block_topk<NT>(s_aux, nk, k, s_top, s_red);
-    if (tid < k) st_agent(&a.ws.row_keys[rowid * kMaxTopk + tid], s_top[tid]);
+    // segment prefix sum and total of cq (<= 16), one ballot per bit
+    int off = 0, n = 0;
+#pragma unroll
+    for (int bit = 0; bit < 5; ++bit) {
+      const uint64_t bm = __ballot((cq >> bit) & 1);
+      off += __popcll(bm & below) << bit;
+      n += __popcll(bm & segmask) << bit;
+    }
+    // phase: row prefix
+    const bool fits = n <= kRowCap;
+    if (jr < F) {
+      uint64_t* lst = &s_rc[jr * kRowCap];
+      if (fits) {
+#pragma unroll
+        for (int r = 0; r < kMaxTopk; ++r)
+          if (r < cq) lst[off + r] = pk[r];
+      }
+      if (q == 0) {
+        s_rm[jr] = m;
+        s_rs[jr] = sum;
+      }
+    }
+    wave_lds_sync();
+    // phase: row list written
+    if (jr < F && fits) {
+      const uint64_t* lst = &s_rc[jr * kRowCap];
+      for (int i = q; i < n; i += SP) {
+        const uint64_t me = lst[i];
+        int rank = 0;
+#pragma unroll 8
+        for (int t = 0; t < n; ++t) rank += lst[t] > me;
+        if (rank < k) s_rk[jr * kMaxTopk + rank] = me;
+      }
+    }
+    // phase: row ranked
+    // Many equal logits overflow a row's list: that row takes k rounds of
+    // maximum over all of its chunk lists, with the whole wave.
+    for (int sg = 0; sg < RW; ++sg) {
+      const int jo = r0 + wave * RW + sg;
+      if (jo >= F) break;
+      if ((__ballot(!fits) & (SP == 64 ? ~0ull : ((1ull << SP) - 1ull) << (sg * SP))) == 0ull)
+        continue;
+      uint64_t prevk = ~0ull;
+      for (int r = 0; r < k; ++r) {
+        uint64_t best = 0;
+        for (int t = lane; t < S * k; t += 64) {
+          const uint64_t v = ld_agent(&a.ws.part_keys[(e0 + (int64_t)jo * S + t / k) * kMaxTopk + t % k]);
+          if (v < prevk && v > best) best = v;
+        }
+        const uint64_t w = wave_max_u64(best);
+        if (lane == 0) s_rk[jo * kMaxTopk + r] = w;
+        prevk = w;
+      }
+    }
   }
-
+  __syncthreads();
   // phase: row merged
-  // ---- last row of this sequence: children, pool append, next frontier -
-  if (!block_arrive_last(&a.ws.seq_ticket[b], (uint32_t)F, &s_flag)) return;
-  // phase: sequence ticket won
+
+  // ---- children, pool append ------------------------------------------------
   const int64_t pb = (int64_t)b * a.cap;
   const int P0 = a.step == 1 ? 0 : a.ws.pool_count[b];
   const int n_new = F * k;  // <= 256 = NT
   if (tid < n_new) {
     const int jj = tid / k, r = tid - jj * k;
-    const int64_t rid = (int64_t)b * k + jj;
-    const uint64_t key = ld_agent(&a.ws.row_keys[rid * kMaxTopk + r]);
+    const uint64_t key = s_rk[jj * kMaxTopk + r];
     const float xl = logit_of(key);
     const int tok = (int)id_of(key);
-    const float m = ld_agent(&a.ws.row_m[rid]);
-    const float conf = expf(xl - m) / ld_agent(&a.ws.row_s[rid]);
+    const float conf = __builtin_amdgcn_exp2f((xl - s_rm[jj]) * kLog2e) / s_rs[jj];
     const int par = a.step == 1 ? -1 : a.ws.frontier[(prev * a.B + b) * k + jj];
     const float vpar = par < 0 ? 1.0f : a.ws.pool_value[pb + par];
     const float val = __fmul_rn(vpar, conf);
@@ -237,41 +370,79 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
     a.ws.pool_count[b] = P0 + n_new;
     if (a.step == 1) a.ws.root_token[b] = a.root_tokens[b];
   }
+  __syncthreads();
   // phase: children appended
+  if (wave != 0) return;
+  // ---- next frontier (wave 0): the k most valuable children ---------------
+  // Lane l holds children l, l+64, l+128, l+192.  The k-th largest lane
+  // maximum of the keys' top 32 bits bounds the top 32 bits of the k-th
+  // largest key from below; the keys at or above it are ranked by counting
+  // and the top k, in value order, become the frontier (those below the
+  // expansion threshold, a suffix, stay unexpanded).
   int nf = 0;
   if (a.step < a.D) {
-    // Within a row, children come in order of decreasing confidence, so
-    // the first child carries the row's largest value; with at least k
-    // rows the k-th largest such head value bounds the layer's k-th
-    // largest value from below (with fewer rows every child is a candidate).
-    __syncthreads();
-    if (tid < F) s_keys[tid] = s_aux[tid * k];
-    float vL = 0.f;
-    if (F >= k) {
-      block_topk<NT>(s_keys, F, k, s_top, s_red);
-      vL = pool_value_of(s_top[k - 1]);
+    uint64_t ck[4];
+    uint32_t hmax = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = lane + 64 * u;
+      ck[u] = t < n_new ? s_aux[t] : 0;
+      const uint32_t hi = (uint32_t)(ck[u] >> 32);
+      hmax = hi > hmax ? hi : hmax;
     }
-    if (tid == 0) s_count = 0;
-    __syncthreads();
-    // phase: frontier threshold
-    if (tid < n_new && !(pool_value_of(s_aux[tid]) < vL))
-      s_keys[atomicAdd(&s_count, 1)] = s_aux[tid];
-    __syncthreads();
-    block_topk<NT>(s_keys, s_count, k, s_top, s_red);
-    const uint64_t ftop = tid < k ? s_top[tid] : 0;
-    const bool keep = tid < k && ftop != 0 && !(pool_value_of(ftop) < a.thr);
-    if (wave == 0) nf = __popcll(__ballot(keep));
-    if (tid < k) {
-      a.ws.frontier[(cur * a.B + b) * k + tid] = keep ? pool_index_of(ftop) : -1;
-      // token field of the pool key: bits 12..29 hold 2^18 - 1 - token
-      a.next_tokens[(int64_t)b * k + tid] =
-          keep ? (int)((1u << 18) - 1u - (uint32_t)((ftop >> 12) & 0x3FFFFu)) : -1;
+    const uint32_t T = wave_kth_largest_u32(hmax, k, 0);
+    int cq = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) cq += (ck[u] != 0 && (uint32_t)(ck[u] >> 32) >= T) ? 1 : 0;
+    int n;
+    const int off = wave_excl_prefix_small(cq, &n);
+    uint64_t* wbuf = &s_bc[0];
+    const int fb = (cur * a.B + b) * k;
+    if (n <= kWaveCap) {
+      int o = off;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (ck[u] != 0 && (uint32_t)(ck[u] >> 32) >= T) wbuf[o++] = ck[u];
+      wave_lds_sync();
+      bool kept = false;
+      if (lane < n) {
+        const uint64_t me = wbuf[lane];
+        int rank = 0;
+#pragma unroll 8
+        for (int q = 0; q < n; ++q) rank += wbuf[q] > me;
+        if (rank < k) {
+          kept = !(pool_value_of(me) < a.thr);
+          a.ws.frontier[fb + rank] = kept ? pool_index_of(me) : -1;
+          // token field of the pool key: bits 12..29 hold 2^18 - 1 - token
+          a.next_tokens[(int64_t)b * k + rank] =
+              kept ? (int)((1u << 18) - 1u - (uint32_t)((me >> 12) & 0x3FFFFu)) : -1;
+        }
+      }
+      nf = __popcll(__ballot(kept));
+    } else {
+      // Many equal values: k rounds of wave maximum.
+      uint64_t prevk = ~0ull;
+      for (int r = 0; r < k; ++r) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (ck[u] < prevk && ck[u] > best) best = ck[u];
+        const uint64_t w = wave_max_u64(best);
+        const bool kept = w != 0 && !(pool_value_of(w) < a.thr);
+        if (lane == 0) {
+          a.ws.frontier[fb + r] = kept ? pool_index_of(w) : -1;
+          a.next_tokens[(int64_t)b * k + r] =
+              kept ? (int)((1u << 18) - 1u - (uint32_t)((w >> 12) & 0x3FFFFu)) : -1;
+        }
+        nf += kept ? 1 : 0;
+        prevk = w;
+      }
     }
-  } else if (tid < k) {
-    a.ws.frontier[(cur * a.B + b) * k + tid] = -1;
-    a.next_tokens[(int64_t)b * k + tid] = -1;
+  } else if (lane < k) {
+    a.ws.frontier[(cur * a.B + b) * k + lane] = -1;
+    a.next_tokens[(int64_t)b * k + lane] = -1;
   }
-  if (tid == 0) {
+  if (lane == 0) {
     a.ws.frontier_count[cur * a.B + b] = nf;
     a.next_count[b] = nf;
   }
