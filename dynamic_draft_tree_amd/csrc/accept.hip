@@ -6,9 +6,9 @@
 // accepted iff it equals the target model's argmax at its parent.
 //
 // One launch.  Grid (S chunks, T slot rows, B), 256 threads.  Each block
-// finds the (max logit, lowest id) of one 4096-element chunk of one target
-// row; the last block of a row merges the chunks into that row's argmax;
-// the last row of a sequence walks the tree from the root.
+// finds the (max logit, lowest id) of one chunk of one target row; the
+// last block of a row merges the chunks into that row's argmax; the last
+// row of a sequence walks the tree from the root.
 #include "device.h"
 #include "internal.h"
 
@@ -43,32 +43,43 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   const int base = c * kChunkE;
   float x[E];
   load_chunk<BF16, VEC, E>(row, base, a.V, tid, x);
-  // (max logit, lowest id) of this thread's elements: elements are scanned
-  // in increasing id order and only a strictly larger logit replaces.
-  uint64_t key = 0;
+  // phase: chunk loaded
+  // (max logit, lowest id) of the chunk: the lane maximum, the wave
+  // maximum, then the lowest id holding it (a lane's ids increase with e).
+  float mx[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
+  for (int e = 0; e < E; ++e) mx[e] = x[e];
+#pragma unroll
+  for (int w = E / 2; w >= 1; w >>= 1)
+#pragma unroll
+    for (int e = 0; e < w; ++e) mx[e] = fmaxf(mx[e], mx[e + w]);
+  const float wm = wave_max_f32(mx[0]);
+  uint32_t lid = 0xFFFFFFFFu;
+#pragma unroll
+  for (int e = E - 1; e >= 0; --e) {
     const int id = base + elem_off<BF16>(e, tid);
-    const uint64_t ke = id < a.V ? logit_key(x[e], (uint32_t)id) : 0;
-    key = ke > key ? ke : key;
+    if (x[e] == wm && id < a.V) lid = (uint32_t)id;
   }
-  key = wave_max_u64(key);
-  if (lane == 0) s_best[wave] = key;
+  const uint32_t wid = wave_min_u32(lid);
+  if (lane == 0) s_best[wave] = wid == 0xFFFFFFFFu ? 0 : logit_key(wm, wid);
   __syncthreads();
-
+  // phase: chunk argmax
   const int64_t rowid = (int64_t)b * a.T + srow;
   if (tid == 0) {
     uint64_t m = s_best[0];
     for (int w = 1; w < 4; ++w) m = s_best[w] > m ? s_best[w] : m;
     st_agent(&a.ws.part[rowid * a.S + c], m);
   }
+  // phase: partial published
   if (!block_arrive_last(&a.ws.row_ticket[rowid], (uint32_t)a.S, &s_flag)) return;
   if (wave == 0) {
     uint64_t m = lane < a.S ? ld_agent(&a.ws.part[rowid * a.S + lane]) : 0;
     m = wave_max_u64(m);
     if (lane == 0) st_agent(&a.ws.amax[rowid], (int32_t)id_of(m));
   }
+  // phase: row merged
   if (!block_arrive_last(&a.ws.seq_ticket[b], (uint32_t)(n + 1), &s_flag)) return;
+  // phase: sequence ticket won
   if (wave != 0) return;
 
   // Greedy walk from the root (one wave).  Lane l holds slots l, l+64, ...
@@ -86,6 +97,7 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
     r_par[i] = ok ? ps[s] : -2;
     r_am[i] = ok ? ld_agent(&am[s]) : -1;
   }
+  // phase: walk inputs read
   int32_t* path = a.path_slots + (int64_t)b * (a.D + 1);
   int32_t* outt = a.out_tokens + (int64_t)b * (a.D + 1);
   int cur = 0, len = 0;
@@ -111,6 +123,7 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
     ++len;
     cur = found;
   }
+  // phase: walk done
   // readlane must run with every lane active (amax_of selects per lane).
   const int bonus = amax_of(cur);
   if (lane == 0) {
@@ -146,13 +159,17 @@ hipError_t launch_accept(const Plan& p, const AcceptWs& w, const void* target,
   a.V = p.V;
   a.T = p.T;
   a.D = p.D;
-  a.S = p.s_draft;
-  dim3 grid(p.s_draft, p.T, p.B);
+  // 16K-element chunks (8 KB of fp32 or bf16 pairs per wave): eight
+  // 16-byte loads in flight per thread and a fan-in of 8 per 128K row
+  constexpr int EB = 64, EF = 32;
   const bool bf = p.ldt == ET_BF16;
-  if (bf && vec) accept_kernel<true, true, kElemsBf16><<<grid, kScanThreads, 0, s>>>(a);
-  else if (bf) accept_kernel<true, false, kElemsBf16><<<grid, kScanThreads, 0, s>>>(a);
-  else if (vec) accept_kernel<false, true, kElemsF32><<<grid, kScanThreads, 0, s>>>(a);
-  else accept_kernel<false, false, kElemsF32><<<grid, kScanThreads, 0, s>>>(a);
+  const int ce = kScanThreads * (bf ? EB : EF);
+  a.S = (p.V + ce - 1) / ce;
+  dim3 grid(a.S, p.T, p.B);
+  if (bf && vec) accept_kernel<true, true, EB><<<grid, kScanThreads, 0, s>>>(a);
+  else if (bf) accept_kernel<true, false, EB><<<grid, kScanThreads, 0, s>>>(a);
+  else if (vec) accept_kernel<false, true, EF><<<grid, kScanThreads, 0, s>>>(a);
+  else accept_kernel<false, false, EF><<<grid, kScanThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
