@@ -159,8 +159,8 @@ hipError_t launch_accept(const Plan& p, const AcceptWs& w, const void* target,
   a.V = p.V;
   a.T = p.T;
   a.D = p.D;
-  // 16K-element chunks (8 KB of fp32 or bf16 pairs per wave): eight
-  // 16-byte loads in flight per thread and a fan-in of 8 per 128K row
+  // Chunks of 16K bf16 (8K fp32) elements: eight 16-byte loads in flight
+  // per thread and a merge fan-in of 8 per 128K-token row
   constexpr int EB = 64, EF = 32;
   const bool bf = p.ldt == ET_BF16;
   const int ce = kScanThreads * (bf ? EB : EF);

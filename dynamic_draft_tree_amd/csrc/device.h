@@ -166,12 +166,12 @@ __device__ __forceinline__ int ballot_rank(bool pred, int* count) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Exclusive prefix sum over the wave of small non-negative values (< 64),
+// Exclusive prefix sum over the wave of small non-negative values (< 128),
 // from one ballot per bit plane; *total receives the wave sum.
 __device__ __forceinline__ int wave_excl_prefix_small(int v, int* total) {
   int pre = 0, tot = 0;
 #pragma unroll
-  for (int bit = 0; bit < 6; ++bit) {
+  for (int bit = 0; bit < 7; ++bit) {
     int cnt;
     const int r = ballot_rank((v >> bit) & 1, &cnt);
     pre += r << bit;
