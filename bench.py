@@ -29,6 +29,102 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 MALL_BYTES = 256 << 20
 
 
+KERNEL_SOURCES = {  # files whose change invalidates a kernel's counters
+    "draft_step_kernel": ["draft.hip", "device.h", "internal.h"],
+    "accept_kernel": ["accept.hip", "device.h", "internal.h"],
+    "tree_attn_bf16_kernel": ["attention.hip", "device.h", "internal.h"],
+}
+
+
+def source_digest(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, []):
+        with open(os.path.join(ROOT, "dynamic_draft_tree_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(kernel, workload):
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel's sources changed since it was taken."""
+    p = traffic_path(kernel, workload)
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        t = json.load(fh)
+    if t.get("source_digest") != source_digest(kernel):
+        return None
+    return t["traffic_bytes_per_launch"]
+
+
+def pmc_rows(d):
+    """(kernel name, counter, value) rows of a rocprofv3 --pmc csv run."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def summarize_pmc(args):
+    """Write profiles/<kernel>_<workload>_traffic.json from four --pmc runs:
+    FETCH_SIZE and WRITE_SIZE of the bench and of the copy calibration."""
+    fetch, write, cfetch, cwrite = args.summarize_pmc
+    copy_bytes = args.copy_mb * (1 << 20)
+
+    def per_dispatch(d, name_part, counter):
+        """Mean over the dispatches (the bench kernel's launches differ in
+        size, as its algorithmic bytes do)."""
+        v = [x for k, c, x in pmc_rows(d) if name_part in k and c == counter]
+        if not v:
+            raise SystemExit(f"no {counter} rows for {name_part} under {d}")
+        return float(np.mean(v)), len(v)
+
+    # the copy kernel reads and writes copy_bytes per dispatch
+    cf, _ = per_dispatch(cfetch, "neg_kernel", "FETCH_SIZE")
+    cw, _ = per_dispatch(cwrite, "neg_kernel", "WRITE_SIZE")
+    f_fetch = copy_bytes / cf
+    f_write = copy_bytes / cw
+    kf, nf = per_dispatch(fetch, args.summarize_kernel, "FETCH_SIZE")
+    kw, nw = per_dispatch(write, args.summarize_kernel, "WRITE_SIZE")
+    out = {
+        "kernel": args.summarize_kernel, "workload": args.workload,
+        "fetch_size_kib_mean": kf, "write_size_kib_mean": kw,
+        "dispatches": [nf, nw],
+        "copy_calibration": {"bytes": copy_bytes, "fetch_kib": cf, "write_kib": cw,
+                             "fetch_bytes_per_unit": f_fetch,
+                             "write_bytes_per_unit": f_write},
+        "fetch_bytes_per_launch": kf * f_fetch,
+        "write_bytes_per_launch": kw * f_write,
+        "traffic_bytes_per_launch": round(kf * f_fetch + kw * f_write),
+        "source_digest": source_digest(args.summarize_kernel),
+    }
+    with open(traffic_path(args.summarize_kernel, args.workload), "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
+def copy_calibration(args):
+    """A plain device copy of --copy-mb MiB, the reference for scaling the
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = args.copy_mb * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)  # one elementwise kernel: reads n, writes n
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_mb": args.copy_mb, "dispatches": 5}), flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -42,6 +138,12 @@ def parse():
                     help="budget for the CPU oracle baseline (0 = skip)")
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets to rotate (0 = enough to pass the MALL)")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="only run the copy used to calibrate HBM counters")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar="DIR",
+                    help="write the traffic summary from the FETCH_SIZE and "
+                         "WRITE_SIZE runs of the bench and of the copy")
+    ap.add_argument("--summarize-kernel", default="draft_step_kernel")
     return ap.parse_args()
 
 
@@ -62,10 +164,16 @@ def algorithmic(w, n_kept, frontier_rows):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
+    if args.copy_mb:
+        copy_calibration(args)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is "
-              "not supported (the batch would shard by sequence with no "
-              "exchange; see the design notes)", file=sys.stderr)
+              "not supported (a batch would shard by sequence across GPUs "
+              "with no exchange between them)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -156,13 +264,15 @@ def main():
     per_batch = 10
 
     def enqueue_cycle(ds, row):
+        # the D draft steps run back to back between one pair of events;
+        # their average carries no per-launch event overhead
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
         for step in range(1, w.depth + 1):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
             plan.draft_step(step, ds["roots"], ds["draft"][:, step - 1], stream)
-            e1.record(stream)
-            row.append(("draft", e0, e1))
+        e1.record(stream)
+        row.append(("draft", e0, e1))
         for n, fn in (("rerank", lambda: plan.rerank(stream)),
                       ("mask", lambda: plan.tree_mask(ds["prefix"], stream)),
                       ("attention", lambda: plan.tree_attention(
@@ -211,7 +321,7 @@ def main():
         for row in rows:
             for n, e0, e1 in row:
                 acc[n] += e0.elapsed_time(e1) * 1e3  # us
-                cnt[n] += 1
+                cnt[n] += w.depth if n == "draft" else 1
         done += nb
     avg_us = {n: acc[n] / cnt[n] for n in names}
     per_cycle_us = {n: acc[n] / K for n in names}
@@ -238,7 +348,8 @@ def main():
     achieved = bytes_per_launch / (avg_us[dominant] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(kernel, w.name),
                 "kernel": kernel, "avg_us": round(avg_us[dominant], 3),
                 "bytes_per_launch": bytes_per_launch}
 
