@@ -40,7 +40,7 @@ et::Plan* as_plan(et_plan_t p) { return reinterpret_cast<et::Plan*>(p); }
 enum {
   R_DRAFT_ROW_TICKET, R_DRAFT_SEQ_TICKET, R_ACC_ROW_TICKET, R_ACC_SEQ_TICKET,
   R_POOL_TOKEN, R_POOL_PARENT, R_POOL_DEPTH, R_POOL_CONF, R_POOL_VALUE,
-  R_POOL_COUNT, R_ROOT, R_FRONTIER, R_FRONTIER_COUNT, R_PART_M, R_PART_S,
+  R_POOL_COUNT, R_ROOT, R_FRONTIER, R_FRONTIER_VAL, R_FRONTIER_COUNT, R_PART_M, R_PART_S,
   R_PART_KEYS, R_ROW_M, R_ROW_S, R_ROW_KEYS, R_ACC_PART, R_ACC_AMAX,
   R_ATT_O, R_ATT_M, R_ATT_L, R_COUNT
 };
@@ -58,6 +58,7 @@ void layout(et::Plan& p) {
   sz[R_POOL_CONF] = sz[R_POOL_VALUE] = B * cap * 4;
   sz[R_POOL_COUNT] = sz[R_ROOT] = B * 4;
   sz[R_FRONTIER] = 2 * B * k * 4;
+  sz[R_FRONTIER_VAL] = 2 * B * k * 4;
   sz[R_FRONTIER_COUNT] = 2 * B * 4;
   // draft partials: one per (row, chunk, wave of the scan block)
   const size_t W4 = et::kScanThreads / 64;
@@ -103,6 +104,7 @@ DraftWs draft_ws(const Plan& p, void* ws) {
   w.pool_count = at<int32_t>(ws, p, R_POOL_COUNT);
   w.root_token = at<int32_t>(ws, p, R_ROOT);
   w.frontier = at<int32_t>(ws, p, R_FRONTIER);
+  w.frontier_val = at<float>(ws, p, R_FRONTIER_VAL);
   w.frontier_count = at<int32_t>(ws, p, R_FRONTIER_COUNT);
   w.part_m = at<float>(ws, p, R_PART_M);
   w.part_s = at<float>(ws, p, R_PART_S);

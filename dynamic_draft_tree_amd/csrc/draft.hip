@@ -80,12 +80,20 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
   __shared__ int s_count;
   __shared__ int s_flag;
   // merge (last block of the sequence)
-  __shared__ float s_rm[kMaxTopk], s_rs[kMaxTopk];
   __shared__ uint64_t s_rc[kMaxTopk * kRowCap];   // row candidates
   __shared__ uint64_t s_rk[kMaxTopk * kMaxTopk];  // row top-k keys
   __shared__ uint64_t s_aux[256];
 
   const int prev = (a.step - 1) & 1, cur = a.step & 1;
+  if (a.step == 1 && j > 0) return;  // the root is the only row of step 1
+  // The chunk's loads are issued before the frontier count arrives (every
+  // row j < topk is readable memory by contract; rows j >= F are dropped
+  // below), so the count's latency hides behind the logits'.
+  const int64_t esz = BF16 ? 2 : 4;
+  const char* row = (const char*)a.logits + (b * a.bstride + j * a.rstride) * esz;
+  const int base = c * kChunkE;
+  float x[E];
+  load_chunk<BF16, VEC, E>(row, base, a.V, tid, x);
   const int F = a.step == 1 ? 1 : a.ws.frontier_count[prev * a.B + b];
   // phase: frontier count read
   if (F == 0) {
@@ -101,12 +109,7 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
   }
   if (j >= F) return;
 
-  // ---- stream one chunk: per wave max, sum of exp and candidates ---------
-  const int64_t esz = BF16 ? 2 : 4;
-  const char* row = (const char*)a.logits + (b * a.bstride + j * a.rstride) * esz;
-  const int base = c * kChunkE;
-  float x[E];
-  load_chunk<BF16, VEC, E>(row, base, a.V, tid, x);
+  // ---- one chunk: per wave max, sum of exp and candidates ----------------
   if (tid == 0) s_count = 0;
   // phase: chunk loaded
 
@@ -240,9 +243,17 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
   const int seg = lane / SP, q = lane - seg * SP;
   const uint64_t segmask = SP == 64 ? ~0ull : ((1ull << SP) - 1ull) << (seg * SP);
   const uint64_t below = segmask & ((1ull << lane) - 1ull);
+  const int64_t pb = (int64_t)b * a.cap;
+  const int P0 = a.step == 1 ? 0 : a.ws.pool_count[b];
   for (int r0 = 0; r0 < F; r0 += kWaves * RW) {
     const int jr = r0 + wave * RW + seg;
     const bool on = jr < F && q < S;
+    // the row's parent: its frontier slot's pool index and value, both
+    // stored by the previous step (no dependent load)
+    const int64_t fs = ((int64_t)prev * a.B + b) * k + jr;
+    const bool hp = a.step > 1 && jr < F;
+    const int par = hp ? a.ws.frontier[fs] : -1;
+    const float vpar = hp ? a.ws.frontier_val[fs] : 1.0f;
     const int64_t e = e0 + (int64_t)jr * S + q;
     const float pm = on ? ld_agent(&a.ws.part_m[e]) : -INFINITY;
     const float ps = on ? ld_agent(&a.ws.part_s[e]) : 0.f;
@@ -304,10 +315,6 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
         for (int r = 0; r < kMaxTopk; ++r)
           if (r < cq) lst[off + r] = pk[r];
       }
-      if (q == 0) {
-        s_rm[jr] = m;
-        s_rs[jr] = sum;
-      }
     }
     wave_lds_sync();
     // phase: row list written
@@ -341,31 +348,27 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
         prevk = w;
       }
     }
+    wave_lds_sync();
+    // phase: row merged
+    // Children of the row, in rank order (conf decreasing): child r of row
+    // jr is pool node P0 + jr * k + r.
+    if (jr < F) {
+      for (int r = q; r < k; r += SP) {
+        const uint64_t key = s_rk[jr * kMaxTopk + r];
+        const int tok = (int)id_of(key);
+        const float conf = __builtin_amdgcn_exp2f((logit_of(key) - m) * kLog2e) / sum;
+        const float val = __fmul_rn(vpar, conf);
+        const int ci = jr * k + r, pi = P0 + ci;
+        a.ws.pool_token[pb + pi] = tok;
+        a.ws.pool_parent[pb + pi] = par;
+        a.ws.pool_depth[pb + pi] = a.step;
+        a.ws.pool_conf[pb + pi] = conf;
+        a.ws.pool_value[pb + pi] = val;
+        s_aux[ci] = pool_key(val, a.step, tok, pi);
+      }
+    }
   }
-  __syncthreads();
-  // phase: row merged
-
-  // ---- children, pool append ------------------------------------------------
-  const int64_t pb = (int64_t)b * a.cap;
-  const int P0 = a.step == 1 ? 0 : a.ws.pool_count[b];
   const int n_new = F * k;  // <= 256 = NT
-  if (tid < n_new) {
-    const int jj = tid / k, r = tid - jj * k;
-    const uint64_t key = s_rk[jj * kMaxTopk + r];
-    const float xl = logit_of(key);
-    const int tok = (int)id_of(key);
-    const float conf = __builtin_amdgcn_exp2f((xl - s_rm[jj]) * kLog2e) / s_rs[jj];
-    const int par = a.step == 1 ? -1 : a.ws.frontier[(prev * a.B + b) * k + jj];
-    const float vpar = par < 0 ? 1.0f : a.ws.pool_value[pb + par];
-    const float val = __fmul_rn(vpar, conf);
-    const int pi = P0 + tid;
-    a.ws.pool_token[pb + pi] = tok;
-    a.ws.pool_parent[pb + pi] = par;
-    a.ws.pool_depth[pb + pi] = a.step;
-    a.ws.pool_conf[pb + pi] = conf;
-    a.ws.pool_value[pb + pi] = val;
-    s_aux[tid] = pool_key(val, a.step, tok, pi);
-  }
   if (tid == 0) {
     a.ws.pool_count[b] = P0 + n_new;
     if (a.step == 1) a.ws.root_token[b] = a.root_tokens[b];
@@ -413,6 +416,7 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
         if (rank < k) {
           kept = !(pool_value_of(me) < a.thr);
           a.ws.frontier[fb + rank] = kept ? pool_index_of(me) : -1;
+          a.ws.frontier_val[fb + rank] = pool_value_of(me);
           // token field of the pool key: bits 12..29 hold 2^18 - 1 - token
           a.next_tokens[(int64_t)b * k + rank] =
               kept ? (int)((1u << 18) - 1u - (uint32_t)((me >> 12) & 0x3FFFFu)) : -1;
@@ -431,6 +435,7 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
         const bool kept = w != 0 && !(pool_value_of(w) < a.thr);
         if (lane == 0) {
           a.ws.frontier[fb + r] = kept ? pool_index_of(w) : -1;
+          a.ws.frontier_val[fb + r] = pool_value_of(w);
           a.next_tokens[(int64_t)b * k + r] =
               kept ? (int)((1u << 18) - 1u - (uint32_t)((w >> 12) & 0x3FFFFu)) : -1;
         }

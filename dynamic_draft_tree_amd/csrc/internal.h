@@ -5,8 +5,9 @@
 //                      et_workspace_init and reset by every consumer
 //   pool         SoA   token/parent/depth i32, conf/value f32  [B][cap]
 //   pool_count, root_token                                     [B]
-//   frontier     i32   [2][B][k] pool indices, double-buffered by step
-//                      parity so a launch never reads what it writes
+//   frontier     i32   [2][B][k] pool indices (and f32 values), double-
+//                      buffered by step parity so a launch never reads
+//                      what it writes
 //   frontier_count i32 [2][B]
 //   draft partials     per (row, chunk, wave): max, sum, top-k logit keys
 //   draft rows         per row: max, fp64 sum, top-k logit keys
@@ -50,6 +51,7 @@ struct DraftWs {
   int32_t* pool_count;    // [B]
   int32_t* root_token;    // [B]
   int32_t* frontier;      // [2][B][k]
+  float* frontier_val;    // [2][B][k] value of each frontier node
   int32_t* frontier_count;// [2][B]
   float* part_m;          // [B][k][S][waves]
   float* part_s;          // [B][k][S][waves]

@@ -121,7 +121,10 @@ int et_workspace_init(et_plan_t plan, void* ws, et_stream_t stream);
  * F_b, in the order of the previous call's next_tokens) reads the vocab
  * logits row at
  *     logits + b * batch_stride + j * row_stride      (elements)
- * (dtype = logits_dtype; rows j >= F_b are not read).  For each row the
+ * (dtype = logits_dtype).  At steps s >= 2 all topk rows j < topk of every
+ * sequence must be readable memory, whatever F_b: they are loaded before
+ * F_b is known, and rows j >= F_b are then ignored (they may hold any
+ * bits).  Step 1 reads row 0 only.  For each row the
  * call computes the full-vocab softmax at temperature 1, takes the topk
  * largest logits (ties: lower token id first) as children, with
  *     conf  = softmax probability of the child token,

@@ -276,6 +276,36 @@ def test_unaligned_rows_take_scalar_path():
     assert torch.equal(plan_a.value, plan_b.value)
 
 
+@pytest.mark.parametrize("name", ["tiny", "small_bf16"])
+def test_rows_past_frontier_are_ignored(name):
+    """Rows j >= F are loaded before F is known but never used: NaN there
+    changes no output bit."""
+    d = _lib()
+    w = _w(name)
+    inp = make_inputs(w)
+    dev = dev_inputs(inp)
+    plan_a = d.Plan(w)
+    plan_b = d.Plan(w)
+    F = np.ones(w.batch, dtype=np.int64)
+    poisoned_rows = 0
+    for step in range(1, w.depth + 1):
+        rows = dev["draft"][:, step - 1].clone()
+        for b in range(w.batch):
+            rows[b, int(F[b]):] = float("nan")
+            poisoned_rows += w.topk - int(F[b])
+        plan_a.draft_step(step, dev["root_tokens"], dev["draft"][:, step - 1])
+        plan_b.draft_step(step, dev["root_tokens"], rows)
+        torch.cuda.synchronize()
+        assert torch.equal(plan_a.next_tokens, plan_b.next_tokens)
+        F = plan_b.next_count.cpu().numpy()
+    plan_a.rerank()
+    plan_b.rerank()
+    torch.cuda.synchronize()
+    assert poisoned_rows > 0
+    for t in ("tokens", "parent_slot", "conf", "value", "n_kept"):
+        assert torch.equal(getattr(plan_a, t), getattr(plan_b, t)), t
+
+
 def test_tree_stops_when_all_below_threshold():
     """Threshold 0.9 with flat rows: step 1 expands nothing further; later
     steps leave the pool unchanged and report an empty frontier."""
