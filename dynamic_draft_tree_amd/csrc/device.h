@@ -142,12 +142,12 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
   return v;
 }
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint32_t o = xor_lane_rt(v, m);
-    v = o < v ? o : v;
-  }
-  return v;
+  v = min(v, xor_lane<32>(v));
+  v = min(v, xor_lane<16>(v));
+  v = min(v, xor_lane<8>(v));
+  v = min(v, xor_lane<4>(v));
+  v = min(v, xor_lane<2>(v));
+  return min(v, xor_lane<1>(v));
 }
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll

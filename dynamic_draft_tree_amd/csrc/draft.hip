@@ -155,13 +155,17 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
   if (wtot <= kWaveCap) {
     // The lane's values are staged in LDS so that each candidate is read
     // by index (a register array cannot be indexed at run time cheaply).
-    float* xs = &s_x[tid * E];
+    // Layout: 16-byte group q of every lane in one contiguous row of the
+    // block, so each group's store is free of bank conflicts.
 #pragma unroll
-    for (int e = 0; e < E; e += 4) *(float4*)&xs[e] = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
+    for (int q = 0; q < E / 4; ++q)
+      *(float4*)&s_x[(q * kScanThreads + tid) * 4] =
+          make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
     while (bits) {
       const int e = __ffs(bits) - 1;
       bits &= bits - 1;
-      wl[o++] = logit_key(xs[e], (uint32_t)(base + elem_off<BF16>(e, tid)));
+      wl[o++] = logit_key(s_x[((e >> 2) * kScanThreads + tid) * 4 + (e & 3)],
+                          (uint32_t)(base + elem_off<BF16>(e, tid)));
     }
   } else {
     // Many equal logits: the wave's exact top-k, by k rounds of maximum.
