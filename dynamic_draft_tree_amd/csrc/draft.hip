@@ -32,7 +32,6 @@ struct DraftArgs {
 
 constexpr int kWaves = kScanThreads / 64;  // waves per scan block
 constexpr int kWaveCap = 64;             // candidate slots per wave
-constexpr int kMaxChunks = 64;           // chunks per row (fp32, V = 2^18)
 constexpr int kStage = 4;                // keys per chunk list read up front
 constexpr int kRowCap = 64;              // merge candidates per row
 
