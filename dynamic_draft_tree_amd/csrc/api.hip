@@ -201,6 +201,21 @@ int et_plan_create(const et_config* cfg, et_plan_t* out) {
   p->ldt = c.logits_dtype;
   p->qdt = c.qkv_dtype;
   p->s_draft = (p->V + et::chunk_elems(p->ldt) - 1) / et::chunk_elems(p->ldt);
+  {
+    // one fused launch per step unless its grid is large; then a scan
+    // launch whose blocks take cpb chunks each (spread evenly over the
+    // row's blocks) and a merge launch
+    const long long blocks = (long long)p->B * p->k * p->s_draft;
+    p->draft_split = blocks > et::kDraftFusedMaxBlocks ? 1 : 0;
+    long long cpb = 1;
+    if (p->draft_split) {
+      cpb = (blocks + et::kDraftTargetBlocks - 1) / et::kDraftTargetBlocks;
+      if (cpb > p->s_draft) cpb = p->s_draft;
+      const long long per_row = (p->s_draft + cpb - 1) / cpb;
+      cpb = (p->s_draft + per_row - 1) / per_row;
+    }
+    p->draft_cpb = (int)cpb;
+  }
   // Attention: the G*T query rows of one kv head are cut into blocks of
   // 64 or 128 rows (128 when that adds no padding rows: each K/V tile then
   // serves twice the rows); the keys are split until the grid has about

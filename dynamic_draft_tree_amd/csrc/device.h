@@ -239,6 +239,13 @@ __device__ __forceinline__ uint64_t wave_sort_desc_u64(uint64_t v) {
 }
 
 // Make this wave's LDS writes visible to its own later LDS reads.
+// LDS writes of this wave visible to its later LDS reads, without waiting
+// for outstanding global loads.
+__device__ __forceinline__ void wave_lds_fence() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
   __threadfence_block();
   __builtin_amdgcn_wave_barrier();
@@ -417,18 +424,19 @@ __device__ __forceinline__ void wait_stores() {
 
 // Block-level "last arrival" ticket.  Every wave waits for its own stores
 // (published with st_agent) to complete, the block synchronises, thread 0
-// takes a ticket, and the block whose ticket completes `total` resets the
-// counter.  Returns the same value in every thread of the block; the
+// adds the n units the block finished, and the block whose addition
+// completes `total` resets the counter.  Returns the same value in every thread of the block; the
 // winner then reads the published data with ld_agent.
 __device__ __forceinline__ bool block_arrive_last(uint32_t* ctr,
                                                   uint32_t total,
-                                                  int* s_flag) {
+                                                  int* s_flag,
+                                                  uint32_t n = 1u) {
   wait_stores();
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED,
+    uint32_t prev = __hip_atomic_fetch_add(ctr, n, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
-    int last = prev == total - 1;
+    int last = prev + n == total;
     if (last) st_agent(ctr, 0u);
     *s_flag = last;
   }
@@ -448,44 +456,91 @@ __device__ __forceinline__ int elem_off(int e, int tid) {
   return ((e / per) * kLoadThreads + tid) * per + (e % per);
 }
 
-template <bool BF16, bool VEC, int E>
-__device__ __forceinline__ void load_chunk(const void* row, int base, int V,
-                                           int tid, float (&x)[E]) {
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+// 16-byte vectors a thread holds for E elements of a chunk
+template <bool BF16, int E>
+constexpr int chunk_vectors() { return E / (BF16 ? 8 : 4); }
+
+// Vector path, first half: issue the thread's 16-byte loads of the chunk
+// at `base`.  A vector that runs past the row end loads the row's first
+// vector instead (in bounds, as the vector path needs V >= per); the
+// decode redoes it element-wise.
+template <bool BF16, int E>
+__device__ __forceinline__ void issue_chunk(const void* row, int base, int V, int tid,
+                                            u32x4_t (&raw)[chunk_vectors<BF16, E>()]) {
   constexpr int per = BF16 ? 8 : 4;
-  if constexpr (VEC) {
-    // All vector loads are issued before any is used: a vector that runs
-    // past the row end loads the row's first vector instead (in bounds,
-    // as the vector path needs V >= per) and is redone element-wise.
-    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-    constexpr int NV = E / per;
-    u32x4_t raw[NV];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int off = base + (i * kLoadThreads + tid) * per;
-      const int src = off + per <= V ? off : 0;
-      raw[i] = *(const u32x4_t*)((const char*)row + (size_t)src * (BF16 ? 2 : 4));
+  for (int i = 0; i < chunk_vectors<BF16, E>(); ++i) {
+    const int off = base + (i * kLoadThreads + tid) * per;
+    const int src = off + per <= V ? off : 0;
+    raw[i] = *(const u32x4_t*)((const char*)row + (size_t)src * (BF16 ? 2 : 4));
+  }
+}
+
+// Vector path, second half: widen the loaded vectors to fp32 (elements
+// past the row end become -inf).
+template <bool BF16, int E>
+__device__ __forceinline__ void decode_chunk(const void* row, int base, int V, int tid,
+                                             const u32x4_t (&raw)[chunk_vectors<BF16, E>()],
+                                             float (&x)[E]) {
+  constexpr int per = BF16 ? 8 : 4;
+  constexpr int NV = chunk_vectors<BF16, E>();
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int off = base + (i * kLoadThreads + tid) * per;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (BF16) {
+        x[i * 8 + 2 * q] = __uint_as_float(raw[i][q] << 16);
+        x[i * 8 + 2 * q + 1] = __uint_as_float(raw[i][q] & 0xFFFF0000u);
+      } else {
+        x[i * 4 + q] = __uint_as_float(raw[i][q]);
+      }
     }
+    if (off + per > V) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int off = base + (i * kLoadThreads + tid) * per;
+      for (int u = 0; u < per; ++u)
+        x[i * per + u] = off + u < V
+            ? (BF16 ? bf16_bits_to_f32(((const uint16_t*)row)[off + u])
+                    : ((const float*)row)[off + u])
+            : -INFINITY;
+    }
+  }
+}
+
+// Vector path, tail: a vector that runs past the row end is rebuilt in
+// place from element loads, elements past the end becoming -inf.
+template <bool BF16, int E>
+__device__ __forceinline__ void fix_chunk_tail(const void* row, int base, int V, int tid,
+                                               u32x4_t (&raw)[chunk_vectors<BF16, E>()]) {
+  constexpr int per = BF16 ? 8 : 4;
+#pragma unroll
+  for (int i = 0; i < chunk_vectors<BF16, E>(); ++i) {
+    const int off = base + (i * kLoadThreads + tid) * per;
+    if (off + per > V) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if constexpr (BF16) {
-          x[i * 8 + 2 * q] = __uint_as_float(raw[i][q] << 16);
-          x[i * 8 + 2 * q + 1] = __uint_as_float(raw[i][q] & 0xFFFF0000u);
+          const uint16_t* r16 = (const uint16_t*)row;
+          const uint32_t lo = off + 2 * q < V ? r16[off + 2 * q] : 0xFF80u;
+          const uint32_t hi = off + 2 * q + 1 < V ? r16[off + 2 * q + 1] : 0xFF80u;
+          raw[i][q] = lo | (hi << 16);
         } else {
-          x[i * 4 + q] = __uint_as_float(raw[i][q]);
+          raw[i][q] = off + q < V ? ((const uint32_t*)row)[off + q] : 0xFF800000u;
         }
       }
-      if (off + per > V) {
-#pragma unroll
-        for (int u = 0; u < per; ++u)
-          x[i * per + u] = off + u < V
-              ? (BF16 ? bf16_bits_to_f32(((const uint16_t*)row)[off + u])
-                      : ((const float*)row)[off + u])
-              : -INFINITY;
-      }
     }
+  }
+}
+
+template <bool BF16, bool VEC, int E>
+__device__ __forceinline__ void load_chunk(const void* row, int base, int V,
+                                           int tid, float (&x)[E]) {
+  if constexpr (VEC) {
+    // all vector loads are issued before any is used
+    u32x4_t raw[chunk_vectors<BF16, E>()];
+    issue_chunk<BF16, E>(row, base, V, tid, raw);
+    decode_chunk<BF16, E>(row, base, V, tid, raw, x);
   } else {
 #pragma unroll
     for (int e = 0; e < E; ++e) {

@@ -7,13 +7,17 @@
 // Draft Trees", value equation.  EAGLE notes, "EAGLE 2 / 方法", Expand
 // stage: nodes whose value is below the threshold are not expanded.
 //
-// One launch per step.  Grid (S chunks, k frontier rows, B sequences),
-// 256 threads.  Each block streams one chunk of one logits row with
-// 16-byte loads and publishes the chunk's (max, sum of exp) and its top-k
-// logit keys.  The last block of a sequence to finish (one arrival
-// ticket over all F x S blocks) merges every row of that sequence, turns
-// the rows into children (conf, value), appends them to the pool and
-// selects the next frontier.  No host sync, no second launch.
+// One launch per step for small grids.  Grid (S chunks, k frontier rows,
+// B sequences), 256 threads.  Each block streams one chunk of one logits
+// row with 16-byte loads and publishes the chunk's (max, sum of exp) and
+// its top-k logit keys.  The last block of a sequence to finish (one
+// arrival ticket over all F x S chunks) merges every row of that
+// sequence, turns the rows into children (conf, value), appends them to
+// the pool and selects the next frontier.  No host sync.
+// Large grids (many times the blocks the chip holds at once) split the
+// step in two launches instead: scan blocks that stream several chunks
+// each (the next chunk's loads in flight while the current one is
+// reduced) and exit without a ticket, then one merge block per sequence.
 #include "device.h"
 #include "internal.h"
 
@@ -26,7 +30,7 @@ struct DraftArgs {
   const int32_t* root_tokens;
   int32_t* next_tokens;
   int32_t* next_count;
-  int B, V, k, D, S, step, cap;
+  int B, V, k, D, S, cpb, parts, step, cap;
   float thr;
 };
 
@@ -63,59 +67,61 @@ __device__ __forceinline__ uint64_t key_floor(float x) {
   return (uint64_t)ordered_f32(x) << 32;
 }
 
-template <bool BF16, bool VEC, int E>
-__global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
+// Chunks [c0, c0 + nch) of row j of sequence b: per chunk, the block's
+// (max, sum of exp) and its top-k logit keys, published with agent-scope
+// stores; with WAVE, each wave publishes its own 1/4 of the chunk instead
+// (no block-level step, the waves never wait for one another).  The caller has issued the first chunk's loads (raw, or x on
+// the element-wise path); the next chunk's loads are issued once the
+// current chunk's values are staged in LDS.  On the vector path the
+// values stay in their loaded form (bf16 pairs) and are widened where
+// used, which keeps the register count down.
+template <bool BF16, bool VEC, int E, bool WAVE>
+__device__ __forceinline__ void scan_chunks(const DraftArgs& a, const char* row, int j, int b,
+                                            int c0, int nch, float (&x)[E],
+                                            u32x4_t (&raw)[VEC ? chunk_vectors<BF16, E>() : 1]) {
   constexpr int NT = kScanThreads;
   constexpr int kChunkE = NT * E;
   constexpr float kLog2e = 1.4426950408889634f;
-  const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k = a.k, S = a.S;
-  __shared__ __attribute__((aligned(16))) float s_x[kScanThreads * E];  // lane values
+  constexpr int NV = chunk_vectors<BF16, E>();
+  // lane values as loaded (vector path) or as fp32 (element-wise path)
+  __shared__ u32x4_t s_x[kScanThreads * (VEC ? NV : E / 4)];
   __shared__ uint64_t s_wl[kWaves * kWaveCap];  // wave candidate lists
   __shared__ uint64_t s_bc[kWaves * kWaveCap];  // block candidates
   __shared__ float s_wf[3][kWaves];             // wave bound, max, sum
   __shared__ int s_wcnt[kWaves];
   __shared__ int s_count;
-  __shared__ int s_flag;
-  // merge (last block of the sequence)
-  __shared__ uint64_t s_rc[kMaxTopk * kRowCap];   // row candidates
-  __shared__ uint64_t s_rk[kMaxTopk * kMaxTopk];  // row top-k keys
-  __shared__ uint64_t s_aux[256];
-
-  const int prev = (a.step - 1) & 1, cur = a.step & 1;
-  if (a.step == 1 && j > 0) return;  // the root is the only row of step 1
-  // The chunk's loads are issued before the frontier count arrives (every
-  // row j < topk is readable memory by contract; rows j >= F are dropped
-  // below), so the count's latency hides behind the logits'.
-  const int64_t esz = BF16 ? 2 : 4;
-  const char* row = (const char*)a.logits + (b * a.bstride + j * a.rstride) * esz;
+  // ---- chunks: per wave max, sum of exp and candidates --------------------
+  for (int ci = 0; ci < nch; ++ci) {
+  const int c = c0 + ci;
   const int base = c * kChunkE;
-  float x[E];
-  load_chunk<BF16, VEC, E>(row, base, a.V, tid, x);
-  const int F = a.step == 1 ? 1 : a.ws.frontier_count[prev * a.B + b];
-  // phase: frontier count read
-  if (F == 0) {
-    // The tree stopped growing earlier: no rows, empty next frontier.
-    if (c == 0 && j == 0) {
-      if (tid < k) a.next_tokens[(int64_t)b * k + tid] = -1;
-      if (tid == 0) {
-        a.next_count[b] = 0;
-        a.ws.frontier_count[cur * a.B + b] = 0;
-      }
-    }
-    return;
-  }
-  if (j >= F) return;
-
-  // ---- one chunk: per wave max, sum of exp and candidates ----------------
+  if constexpr (VEC) fix_chunk_tail<BF16, E>(row, base, a.V, tid, raw);
   if (tid == 0) s_count = 0;
   // phase: chunk loaded
+  // element e of the lane (e a compile-time index)
+  auto xv = [&](int e) -> float {
+    if constexpr (VEC && BF16) {
+      const uint32_t w = raw[e >> 3][(e >> 1) & 3];
+      return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    } else if constexpr (VEC) {
+      return __uint_as_float(raw[e >> 2][e & 3]);
+    } else {
+      return x[e];
+    }
+  };
+  // element e of the lane from its LDS copy (e may be a run-time index)
+  auto xs = [&](int e) -> float {
+    if constexpr (VEC && BF16)
+      return __uint_as_float((uint32_t)((const uint16_t*)s_x)[((e >> 3) * NT + tid) * 8 + (e & 7)] << 16);
+    else
+      return ((const float*)s_x)[((e >> 2) * NT + tid) * 4 + (e & 3)];
+  };
 
   // Lane max as a pairwise tree (short dependency chain).
   float mx[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) mx[e] = x[e];
+  for (int e = 0; e < E; ++e) mx[e] = xv(e);
 #pragma unroll
   for (int w = E / 2; w >= 1; w >>= 1)
 #pragma unroll
@@ -130,7 +136,7 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      acc[e & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], kLog2e, -off));
+      acc[e & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(xv(e), kLog2e, -off));
     sl = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   }
   const float sw = wave_sum_f32(sl);
@@ -142,29 +148,43 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
   // its slots, and the lane writes its (usually zero to two) candidates.
   const float Lw = wave_kth_largest<BF16>(lmax, k);
   // phase: wave threshold
-  uint32_t bits = 0;
+  // element e's vocab id is lid + (its offset from the lane's first
+  // element, a constant); ids at or past V are padding
+  constexpr int per = BF16 ? 8 : 4;
+  const int lid = base + tid * per;
+  const int lim = a.V - lid;
+  // (one is opaque to the compiler: written as cond ? 1 << e : 0 the 32
+  // masks would be hoisted out of the chunk loop into registers)
+  uint32_t one = 1u, bits = 0u;
+  asm volatile("" : "+v"(one));
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int id = base + elem_off<BF16>(e, tid);
-    bits |= (id < a.V && x[e] >= Lw) ? (1u << e) : 0u;
+  for (int e = 0; e < E; ++e)
+    bits |= (elem_off<BF16>(e, 0) < lim && xv(e) >= Lw ? one : 0u) << e;
+  // The lane's values are staged in LDS so that each candidate is read by
+  // index (a register array cannot be indexed at run time cheaply).
+  // Layout: 16-byte group q of every lane in one contiguous row of the
+  // block, so each group's store is free of bank conflicts.
+  if constexpr (VEC) {
+#pragma unroll
+    for (int q = 0; q < NV; ++q) s_x[q * kScanThreads + tid] = raw[q];
+  } else {
+#pragma unroll
+    for (int q = 0; q < E / 4; ++q)
+      s_x[q * kScanThreads + tid] = u32x4_t{__float_as_uint(x[4 * q]), __float_as_uint(x[4 * q + 1]),
+                                            __float_as_uint(x[4 * q + 2]), __float_as_uint(x[4 * q + 3])};
   }
+  // The registers are free from here on: the next chunk's loads go out
+  // and land while this chunk's candidates are ranked and published.
+  if constexpr (VEC)
+    if (ci + 1 < nch) issue_chunk<BF16, E>(row, base + kChunkE, a.V, tid, raw);
   int wtot;
   int o = wave_excl_prefix_small(__popc(bits), &wtot);
   uint64_t* wl = &s_wl[wave * kWaveCap];
   if (wtot <= kWaveCap) {
-    // The lane's values are staged in LDS so that each candidate is read
-    // by index (a register array cannot be indexed at run time cheaply).
-    // Layout: 16-byte group q of every lane in one contiguous row of the
-    // block, so each group's store is free of bank conflicts.
-#pragma unroll
-    for (int q = 0; q < E / 4; ++q)
-      *(float4*)&s_x[(q * kScanThreads + tid) * 4] =
-          make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
     while (bits) {
       const int e = __ffs(bits) - 1;
       bits &= bits - 1;
-      wl[o++] = logit_key(s_x[((e >> 2) * kScanThreads + tid) * 4 + (e & 3)],
-                          (uint32_t)(base + elem_off<BF16>(e, tid)));
+      wl[o++] = logit_key(xs(e), (uint32_t)(lid + elem_off<BF16>(e, 0)));
     }
   } else {
     // Many equal logits: the wave's exact top-k, by k rounds of maximum.
@@ -173,8 +193,8 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
       uint64_t best = 0;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const int id = base + elem_off<BF16>(e, tid);
-        const uint64_t key = id < a.V ? logit_key(x[e], (uint32_t)id) : 0;
+        const int id = lid + elem_off<BF16>(e, 0);
+        const uint64_t key = id < a.V ? logit_key(xs(e), (uint32_t)id) : 0;
         if (key < prevk && key > best) best = key;
       }
       const uint64_t w = wave_max_u64(best);
@@ -182,6 +202,29 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
       prevk = w;
     }
     wtot = k;
+  }
+  if constexpr (WAVE) {
+    // The wave's list, ranked by counting; its entry is partial
+    // (row, chunk, wave).
+    wave_lds_fence();
+    const int64_t pe = (((int64_t)b * k + j) * S + c) * kWaves + wave;
+    uint64_t* dst = &a.ws.part_keys[pe * kMaxTopk];
+    if (lane < wtot) {
+      const uint64_t me = wl[lane];
+      int rank = 0;
+#pragma unroll 8
+      for (int q = 0; q < wtot; ++q) rank += wl[q] > me;
+      if (rank < k) st_agent(&dst[rank], me);
+    }
+    if (lane >= wtot && lane < k) st_agent(&dst[lane], (uint64_t)0);
+    if (lane == 0) {
+      st_agent(&a.ws.part_m[pe], mw);
+      st_agent(&a.ws.part_s[pe], sw);
+    }
+    // phase: wave published
+    if constexpr (!VEC)
+      if (ci + 1 < nch) load_chunk<BF16, false, E>(row, base + kChunkE, a.V, tid, x);
+    continue;
   }
   if (lane == 0) {
     s_wcnt[wave] = wtot;
@@ -227,11 +270,26 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
     st_agent(&a.ws.part_m[pe], mb);
     st_agent(&a.ws.part_s[pe], sb);
   }
-  // phase: partial published
+  if (ci + 1 < nch) {
+    if constexpr (!VEC) load_chunk<BF16, false, E>(row, base + kChunkE, a.V, tid, x);
+    __syncthreads();  // the LDS lists are reused by the next chunk
+  }
+  }
+}
 
-  // ---- last block of this sequence: merge every row ---------------------
-  if (!block_arrive_last(&a.ws.seq_ticket[b], (uint32_t)(F * S), &s_flag)) return;
-  // phase: sequence ticket won
+// The F rows of sequence b, every chunk published: row softmax statistics
+// and top-k, children appended to the pool, next frontier.  Needs the
+// whole block of NW waves.
+template <bool BF16, int NW>
+__device__ __forceinline__ void merge_sequence(const DraftArgs& a, int b, int F) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k = a.k, S = a.parts;  // partial lists per row
+  const int prev = (a.step - 1) & 1, cur = a.step & 1;
+  __shared__ uint64_t s_rc[kMaxTopk * kRowCap];   // row candidates
+  __shared__ uint64_t s_rk[kMaxTopk * kMaxTopk];  // row top-k keys
+  __shared__ uint64_t s_aux[256];                 // children's pool keys
+  __shared__ uint64_t s_fb[kWaveCap];             // frontier candidates
   // ---- row merges: a segment of SP lanes per row ------------------------
   // SP is the power of two >= S, so a wave merges 64 / SP rows at once and
   // lane q of a segment holds chunk q's (max, sum) and the first kStage
@@ -248,7 +306,7 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
   const uint64_t below = segmask & ((1ull << lane) - 1ull);
   const int64_t pb = (int64_t)b * a.cap;
   const int P0 = a.step == 1 ? 0 : a.ws.pool_count[b];
-  for (int r0 = 0; r0 < F; r0 += kWaves * RW) {
+  for (int r0 = 0; r0 < F; r0 += NW * RW) {
     const int jr = r0 + wave * RW + seg;
     const bool on = jr < F && q < S;
     // the row's parent: its frontier slot's pool index and value, both
@@ -402,7 +460,7 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
     for (int u = 0; u < 4; ++u) cq += (ck[u] != 0 && (uint32_t)(ck[u] >> 32) >= T) ? 1 : 0;
     int n;
     const int off = wave_excl_prefix_small(cq, &n);
-    uint64_t* wbuf = &s_bc[0];
+    uint64_t* wbuf = &s_fb[0];
     const int fb = (cur * a.B + b) * k;
     if (n <= kWaveCap) {
       int o = off;
@@ -457,6 +515,78 @@ __global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
   // phase: frontier written
 }
 
+// A sequence whose tree stopped growing: no rows, empty next frontier.
+__device__ __forceinline__ void empty_frontier(const DraftArgs& a, int b) {
+  const int tid = threadIdx.x, cur = a.step & 1;
+  if (tid < a.k) a.next_tokens[(int64_t)b * a.k + tid] = -1;
+  if (tid == 0) {
+    a.next_count[b] = 0;
+    a.ws.frontier_count[cur * a.B + b] = 0;
+  }
+}
+
+// Prologue shared by the scan kernels: the row pointer and the first
+// chunk's loads, issued before the frontier count arrives (every row
+// j < topk is readable memory by contract; rows j >= F are dropped), so
+// the count's latency hides behind the logits'.
+#define ET_DRAFT_PROLOGUE(C0)                                                          \
+  constexpr int kChunkE = kScanThreads * E;                                            \
+  const int j = blockIdx.y, b = blockIdx.z;                                            \
+  const int prev = (a.step - 1) & 1;                                                   \
+  if (a.step == 1 && j > 0) return; /* the root is the only row of step 1 */           \
+  const char* row = (const char*)a.logits + (b * a.bstride + j * a.rstride) * (BF16 ? 2 : 4); \
+  const int c0 = (C0);                                                                 \
+  float x[E];                                                                          \
+  u32x4_t raw[VEC ? chunk_vectors<BF16, E>() : 1];                                     \
+  if constexpr (VEC) issue_chunk<BF16, E>(row, c0 * kChunkE, a.V, threadIdx.x, raw);   \
+  else load_chunk<BF16, false, E>(row, c0 * kChunkE, a.V, threadIdx.x, x);             \
+  const int F = a.step == 1 ? 1 : a.ws.frontier_count[prev * a.B + b]
+
+// Fused step: one chunk per block; the last block of a sequence to
+// publish (one arrival ticket over its F x S chunks) merges the sequence.
+template <bool BF16, bool VEC, int E>
+__global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
+  __shared__ int s_flag;
+  ET_DRAFT_PROLOGUE(blockIdx.x);
+  // phase: frontier count read
+  if (F == 0) {
+    if (c0 == 0 && j == 0) empty_frontier(a, b);
+    return;
+  }
+  if (j >= F) return;
+  scan_chunks<BF16, VEC, E, false>(a, row, j, b, c0, 1, x, raw);
+  // phase: partial published
+  if (!block_arrive_last(&a.ws.seq_ticket[b], (uint32_t)(F * a.S), &s_flag)) return;
+  // phase: sequence ticket won
+  merge_sequence<BF16, kWaves>(a, b, F);
+}
+
+// Split step, first launch (large grids): every block scans cpb chunks
+// and exits; no ticket, so no block waits for its stores to complete.
+// WAVE: per-wave partials (when the row's S * 4 lists fit one merge wave).
+template <bool BF16, bool VEC, int E, bool WAVE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? 3 : 1))) void draft_scan_kernel(DraftArgs a) {
+  ET_DRAFT_PROLOGUE(blockIdx.x * a.cpb);
+  if (j >= F) return;
+  scan_chunks<BF16, VEC, E, WAVE>(a, row, j, b, c0, min(a.cpb, a.S - c0), x, raw);
+}
+#undef ET_DRAFT_PROLOGUE
+
+// Split step, second launch: one block per sequence merges its rows, with
+// 16 waves so that every row (up to 16, one wave each when a row has 64
+// lists) is merged in one pass.
+constexpr int kMergeWaves = 16;
+template <bool BF16>
+__global__ __launch_bounds__(kMergeWaves * 64) void draft_merge_kernel(DraftArgs a) {
+  const int b = blockIdx.x;
+  const int F = a.step == 1 ? 1 : a.ws.frontier_count[((a.step - 1) & 1) * a.B + b];
+  if (F == 0) {
+    empty_frontier(a, b);
+    return;
+  }
+  merge_sequence<BF16, kMergeWaves>(a, b, F);
+}
+
 hipError_t launch_draft_step(const Plan& p, const DraftWs& w, int step,
                              const int32_t* root_tokens, const void* logits,
                              int64_t bstride, int64_t rstride, bool vec,
@@ -475,15 +605,35 @@ hipError_t launch_draft_step(const Plan& p, const DraftWs& w, int step,
   a.k = p.k;
   a.D = p.D;
   a.S = p.s_draft;
+  a.cpb = p.draft_cpb;
+  a.parts = p.s_draft;
   a.step = step;
   a.cap = p.cap;
   a.thr = p.cfg.expand_threshold;
-  dim3 grid(p.s_draft, p.k, p.B);
   const bool bf = p.ldt == ET_BF16;
-  if (bf && vec) draft_step_kernel<true, true, kElemsBf16><<<grid, kScanThreads, 0, s>>>(a);
-  else if (bf) draft_step_kernel<true, false, kElemsBf16><<<grid, kScanThreads, 0, s>>>(a);
-  else if (vec) draft_step_kernel<false, true, kElemsF32><<<grid, kScanThreads, 0, s>>>(a);
-  else draft_step_kernel<false, false, kElemsF32><<<grid, kScanThreads, 0, s>>>(a);
+  if (p.draft_split) {
+    const dim3 grid((p.s_draft + p.draft_cpb - 1) / p.draft_cpb, p.k, p.B);
+    const bool wv = p.s_draft * kWaves <= 64;
+    a.parts = wv ? p.s_draft * kWaves : p.s_draft;
+#define ET_SCAN(W)                                                                           \
+    do {                                                                                     \
+      if (bf && vec) draft_scan_kernel<true, true, kElemsBf16, W><<<grid, kScanThreads, 0, s>>>(a);  \
+      else if (bf) draft_scan_kernel<true, false, kElemsBf16, W><<<grid, kScanThreads, 0, s>>>(a);   \
+      else if (vec) draft_scan_kernel<false, true, kElemsF32, W><<<grid, kScanThreads, 0, s>>>(a);   \
+      else draft_scan_kernel<false, false, kElemsF32, W><<<grid, kScanThreads, 0, s>>>(a);          \
+    } while (0)
+    if (wv) ET_SCAN(true);
+    else ET_SCAN(false);
+#undef ET_SCAN
+    if (bf) draft_merge_kernel<true><<<p.B, kMergeWaves * 64, 0, s>>>(a);
+    else draft_merge_kernel<false><<<p.B, kMergeWaves * 64, 0, s>>>(a);
+  } else {
+    const dim3 grid(p.s_draft, p.k, p.B);
+    if (bf && vec) draft_step_kernel<true, true, kElemsBf16><<<grid, kScanThreads, 0, s>>>(a);
+    else if (bf) draft_step_kernel<true, false, kElemsBf16><<<grid, kScanThreads, 0, s>>>(a);
+    else if (vec) draft_step_kernel<false, true, kElemsF32><<<grid, kScanThreads, 0, s>>>(a);
+    else draft_step_kernel<false, false, kElemsF32><<<grid, kScanThreads, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
