@@ -38,10 +38,10 @@ et::Plan* as_plan(et_plan_t p) { return reinterpret_cast<et::Plan*>(p); }
 
 // Region indices of Plan::off.
 enum {
-  R_DRAFT_ROW_TICKET, R_DRAFT_SEQ_TICKET, R_ACC_ROW_TICKET, R_ACC_SEQ_TICKET,
+  R_ACC_ROW_TICKET, R_ACC_SEQ_TICKET,
   R_POOL_TOKEN, R_POOL_PARENT, R_POOL_DEPTH, R_POOL_CONF, R_POOL_VALUE,
   R_POOL_COUNT, R_ROOT, R_FRONTIER, R_FRONTIER_VAL, R_FRONTIER_COUNT, R_PART_M, R_PART_S,
-  R_PART_KEYS, R_ROW_M, R_ROW_S, R_ROW_KEYS, R_ACC_PART, R_ACC_AMAX,
+  R_PART_KEYS, R_ACC_PART, R_ACC_AMAX,
   R_ATT_O, R_ATT_M, R_ATT_L, R_COUNT
 };
 
@@ -50,8 +50,6 @@ void layout(et::Plan& p) {
   const size_t units = (size_t)p.B * p.Hkv * p.attn_nqb * p.attn_splits;
   const size_t att_rows = p.attn_splits > 1 ? units * 64 * p.attn_wr : 0;
   size_t sz[R_COUNT] = {};
-  sz[R_DRAFT_ROW_TICKET] = B * k * 4;
-  sz[R_DRAFT_SEQ_TICKET] = B * 4;
   sz[R_ACC_ROW_TICKET] = B * T * 4;
   sz[R_ACC_SEQ_TICKET] = B * 4;
   sz[R_POOL_TOKEN] = sz[R_POOL_PARENT] = sz[R_POOL_DEPTH] = B * cap * 4;
@@ -64,9 +62,6 @@ void layout(et::Plan& p) {
   const size_t W4 = et::kScanThreads / 64;
   sz[R_PART_M] = sz[R_PART_S] = B * k * S * W4 * 4;
   sz[R_PART_KEYS] = B * k * S * W4 * et::kMaxTopk * 8;
-  sz[R_ROW_M] = B * k * 4;
-  sz[R_ROW_S] = B * k * 8;
-  sz[R_ROW_KEYS] = B * k * et::kMaxTopk * 8;
   sz[R_ACC_PART] = B * T * S * 8;
   sz[R_ACC_AMAX] = B * T * 4;
   sz[R_ATT_O] = att_rows * p.HD * 4;
@@ -94,8 +89,6 @@ namespace et {
 
 DraftWs draft_ws(const Plan& p, void* ws) {
   DraftWs w;
-  w.row_ticket = at<uint32_t>(ws, p, R_DRAFT_ROW_TICKET);
-  w.seq_ticket = at<uint32_t>(ws, p, R_DRAFT_SEQ_TICKET);
   w.pool_token = at<int32_t>(ws, p, R_POOL_TOKEN);
   w.pool_parent = at<int32_t>(ws, p, R_POOL_PARENT);
   w.pool_depth = at<int32_t>(ws, p, R_POOL_DEPTH);
@@ -109,9 +102,6 @@ DraftWs draft_ws(const Plan& p, void* ws) {
   w.part_m = at<float>(ws, p, R_PART_M);
   w.part_s = at<float>(ws, p, R_PART_S);
   w.part_keys = at<uint64_t>(ws, p, R_PART_KEYS);
-  w.row_m = at<float>(ws, p, R_ROW_M);
-  w.row_s = at<double>(ws, p, R_ROW_S);
-  w.row_keys = at<uint64_t>(ws, p, R_ROW_KEYS);
   return w;
 }
 
@@ -202,19 +192,13 @@ int et_plan_create(const et_config* cfg, et_plan_t* out) {
   p->qdt = c.qkv_dtype;
   p->s_draft = (p->V + et::chunk_elems(p->ldt) - 1) / et::chunk_elems(p->ldt);
   {
-    // one fused launch per step unless its grid is large; then a scan
-    // launch whose blocks take cpb chunks each (spread evenly over the
-    // row's blocks) and a merge launch
+    // chunks per draft scan block: 1 unless B * k * S blocks would be
+    // many times what the chip holds; then spread evenly over the row
     const long long blocks = (long long)p->B * p->k * p->s_draft;
-    p->draft_split = blocks > et::kDraftFusedMaxBlocks ? 1 : 0;
-    long long cpb = 1;
-    if (p->draft_split) {
-      cpb = (blocks + et::kDraftTargetBlocks - 1) / et::kDraftTargetBlocks;
-      if (cpb > p->s_draft) cpb = p->s_draft;
-      const long long per_row = (p->s_draft + cpb - 1) / cpb;
-      cpb = (p->s_draft + per_row - 1) / per_row;
-    }
-    p->draft_cpb = (int)cpb;
+    long long cpb = (blocks + et::kDraftTargetBlocks - 1) / et::kDraftTargetBlocks;
+    if (cpb > p->s_draft) cpb = p->s_draft;
+    const long long per_row = (p->s_draft + cpb - 1) / cpb;
+    p->draft_cpb = (int)((p->s_draft + per_row - 1) / per_row);
   }
   // Attention: the G*T query rows of one kv head are cut into blocks of
   // 64 or 128 rows (128 when that adds no padding rows: each K/V tile then

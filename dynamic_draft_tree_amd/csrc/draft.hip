@@ -7,17 +7,17 @@
 // Draft Trees", value equation.  EAGLE notes, "EAGLE 2 / 方法", Expand
 // stage: nodes whose value is below the threshold are not expanded.
 //
-// One launch per step for small grids.  Grid (S chunks, k frontier rows,
-// B sequences), 256 threads.  Each block streams one chunk of one logits
-// row with 16-byte loads and publishes the chunk's (max, sum of exp) and
-// its top-k logit keys.  The last block of a sequence to finish (one
-// arrival ticket over all F x S chunks) merges every row of that
-// sequence, turns the rows into children (conf, value), appends them to
-// the pool and selects the next frontier.  No host sync.
-// Large grids (many times the blocks the chip holds at once) split the
-// step in two launches instead: scan blocks that stream several chunks
-// each (the next chunk's loads in flight while the current one is
-// reduced) and exit without a ticket, then one merge block per sequence.
+// Two launches per step.  Scan: grid (chunk groups, k frontier rows, B
+// sequences), 256 threads; each block streams cpb consecutive 8K-element
+// chunks of one logits row with 16-byte loads (the next chunk's loads in
+// flight while the current one is reduced) and publishes, per chunk and
+// wave, the wave's (max, sum of exp) and its top-k logit keys.  cpb is 1
+// unless the grid would be many times what the chip holds at once.
+// Merge: one block per sequence combines every row's partials into the
+// row's softmax statistics and top-k, turns the rows into children (conf,
+// value), appends them to the pool and selects the next frontier.  (A
+// single launch in which the last scan block to arrive does the merge was
+// slower: every block then waits for its stores and an arrival ticket.)
 #include "device.h"
 #include "internal.h"
 
@@ -525,56 +525,31 @@ __device__ __forceinline__ void empty_frontier(const DraftArgs& a, int b) {
   }
 }
 
-// Prologue shared by the scan kernels: the row pointer and the first
-// chunk's loads, issued before the frontier count arrives (every row
-// j < topk is readable memory by contract; rows j >= F are dropped), so
-// the count's latency hides behind the logits'.
-#define ET_DRAFT_PROLOGUE(C0)                                                          \
-  constexpr int kChunkE = kScanThreads * E;                                            \
-  const int j = blockIdx.y, b = blockIdx.z;                                            \
-  const int prev = (a.step - 1) & 1;                                                   \
-  if (a.step == 1 && j > 0) return; /* the root is the only row of step 1 */           \
-  const char* row = (const char*)a.logits + (b * a.bstride + j * a.rstride) * (BF16 ? 2 : 4); \
-  const int c0 = (C0);                                                                 \
-  float x[E];                                                                          \
-  u32x4_t raw[VEC ? chunk_vectors<BF16, E>() : 1];                                     \
-  if constexpr (VEC) issue_chunk<BF16, E>(row, c0 * kChunkE, a.V, threadIdx.x, raw);   \
-  else load_chunk<BF16, false, E>(row, c0 * kChunkE, a.V, threadIdx.x, x);             \
-  const int F = a.step == 1 ? 1 : a.ws.frontier_count[prev * a.B + b]
-
-// Fused step: one chunk per block; the last block of a sequence to
-// publish (one arrival ticket over its F x S chunks) merges the sequence.
-template <bool BF16, bool VEC, int E>
-__global__ __launch_bounds__(256) void draft_step_kernel(DraftArgs a) {
-  __shared__ int s_flag;
-  ET_DRAFT_PROLOGUE(blockIdx.x);
-  // phase: frontier count read
-  if (F == 0) {
-    if (c0 == 0 && j == 0) empty_frontier(a, b);
-    return;
-  }
-  if (j >= F) return;
-  scan_chunks<BF16, VEC, E, false>(a, row, j, b, c0, 1, x, raw);
-  // phase: partial published
-  if (!block_arrive_last(&a.ws.seq_ticket[b], (uint32_t)(F * a.S), &s_flag)) return;
-  // phase: sequence ticket won
-  merge_sequence<BF16, kWaves>(a, b, F);
-}
-
-// Split step, first launch (large grids): every block scans cpb chunks
-// and exits; no ticket, so no block waits for its stores to complete.
-// WAVE: per-wave partials (when the row's S * 4 lists fit one merge wave).
+// Scan launch: block (x, j, b) streams chunks [x * cpb, x * cpb + cpb) of
+// row j of sequence b and exits.  The first chunk's loads are issued
+// before the frontier count arrives (every row j < topk is readable memory
+// by contract; rows j >= F are dropped), so the count's latency hides
+// behind the logits'.  WAVE: per-wave partials (when a row's S * 4 lists
+// fit one merge wave), else per-block partials.
 template <bool BF16, bool VEC, int E, bool WAVE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? 3 : 1))) void draft_scan_kernel(DraftArgs a) {
-  ET_DRAFT_PROLOGUE(blockIdx.x * a.cpb);
+  constexpr int kChunkE = kScanThreads * E;
+  const int j = blockIdx.y, b = blockIdx.z;
+  if (a.step == 1 && j > 0) return;  // the root is the only row of step 1
+  const char* row = (const char*)a.logits + (b * a.bstride + j * a.rstride) * (BF16 ? 2 : 4);
+  const int c0 = blockIdx.x * a.cpb;
+  float x[E];
+  u32x4_t raw[VEC ? chunk_vectors<BF16, E>() : 1];
+  if constexpr (VEC) issue_chunk<BF16, E>(row, c0 * kChunkE, a.V, threadIdx.x, raw);
+  else load_chunk<BF16, false, E>(row, c0 * kChunkE, a.V, threadIdx.x, x);
+  const int F = a.step == 1 ? 1 : a.ws.frontier_count[((a.step - 1) & 1) * a.B + b];
   if (j >= F) return;
   scan_chunks<BF16, VEC, E, WAVE>(a, row, j, b, c0, min(a.cpb, a.S - c0), x, raw);
 }
-#undef ET_DRAFT_PROLOGUE
 
-// Split step, second launch: one block per sequence merges its rows, with
-// 16 waves so that every row (up to 16, one wave each when a row has 64
-// lists) is merged in one pass.
+// Merge launch: one block per sequence merges its rows, with 16 waves so
+// that every row (up to 16, one wave each when a row has 64 lists) is
+// merged in one pass.
 constexpr int kMergeWaves = 16;
 template <bool BF16>
 __global__ __launch_bounds__(kMergeWaves * 64) void draft_merge_kernel(DraftArgs a) {
@@ -606,34 +581,25 @@ hipError_t launch_draft_step(const Plan& p, const DraftWs& w, int step,
   a.D = p.D;
   a.S = p.s_draft;
   a.cpb = p.draft_cpb;
-  a.parts = p.s_draft;
   a.step = step;
   a.cap = p.cap;
   a.thr = p.cfg.expand_threshold;
   const bool bf = p.ldt == ET_BF16;
-  if (p.draft_split) {
-    const dim3 grid((p.s_draft + p.draft_cpb - 1) / p.draft_cpb, p.k, p.B);
-    const bool wv = p.s_draft * kWaves <= 64;
-    a.parts = wv ? p.s_draft * kWaves : p.s_draft;
-#define ET_SCAN(W)                                                                           \
-    do {                                                                                     \
-      if (bf && vec) draft_scan_kernel<true, true, kElemsBf16, W><<<grid, kScanThreads, 0, s>>>(a);  \
-      else if (bf) draft_scan_kernel<true, false, kElemsBf16, W><<<grid, kScanThreads, 0, s>>>(a);   \
-      else if (vec) draft_scan_kernel<false, true, kElemsF32, W><<<grid, kScanThreads, 0, s>>>(a);   \
-      else draft_scan_kernel<false, false, kElemsF32, W><<<grid, kScanThreads, 0, s>>>(a);          \
-    } while (0)
-    if (wv) ET_SCAN(true);
-    else ET_SCAN(false);
+  const dim3 grid((p.s_draft + p.draft_cpb - 1) / p.draft_cpb, p.k, p.B);
+  const bool wv = p.s_draft * kWaves <= 64;
+  a.parts = wv ? p.s_draft * kWaves : p.s_draft;
+#define ET_SCAN(W)                                                                               \
+  do {                                                                                           \
+    if (bf && vec) draft_scan_kernel<true, true, kElemsBf16, W><<<grid, kScanThreads, 0, s>>>(a);  \
+    else if (bf) draft_scan_kernel<true, false, kElemsBf16, W><<<grid, kScanThreads, 0, s>>>(a);   \
+    else if (vec) draft_scan_kernel<false, true, kElemsF32, W><<<grid, kScanThreads, 0, s>>>(a);   \
+    else draft_scan_kernel<false, false, kElemsF32, W><<<grid, kScanThreads, 0, s>>>(a);          \
+  } while (0)
+  if (wv) ET_SCAN(true);
+  else ET_SCAN(false);
 #undef ET_SCAN
-    if (bf) draft_merge_kernel<true><<<p.B, kMergeWaves * 64, 0, s>>>(a);
-    else draft_merge_kernel<false><<<p.B, kMergeWaves * 64, 0, s>>>(a);
-  } else {
-    const dim3 grid(p.s_draft, p.k, p.B);
-    if (bf && vec) draft_step_kernel<true, true, kElemsBf16><<<grid, kScanThreads, 0, s>>>(a);
-    else if (bf) draft_step_kernel<true, false, kElemsBf16><<<grid, kScanThreads, 0, s>>>(a);
-    else if (vec) draft_step_kernel<false, true, kElemsF32><<<grid, kScanThreads, 0, s>>>(a);
-    else draft_step_kernel<false, false, kElemsF32><<<grid, kScanThreads, 0, s>>>(a);
-  }
+  if (bf) draft_merge_kernel<true><<<p.B, kMergeWaves * 64, 0, s>>>(a);
+  else draft_merge_kernel<false><<<p.B, kMergeWaves * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -36,24 +36,17 @@ constexpr int kElemsF32 = 16;            // fp32 elements per thread (4 x 16 B)
 constexpr int chunk_elems(int dtype) {
   return kScanThreads * (dtype == ET_BF16 ? kElemsBf16 : kElemsF32);
 }
-// Draft steps whose one-chunk grid exceeds kDraftFusedMaxBlocks run as a
-// scan launch plus a merge launch, the scan blocks taking several chunks
-// each so that the scan grid is about kDraftTargetBlocks.
-#ifndef ET_DRAFT_FUSED_MAX
-#define ET_DRAFT_FUSED_MAX 1024
-#endif
+// Draft scan grids above this many one-chunk blocks give each block
+// several chunks of its row (the chip holds a few thousand at once).
 #ifndef ET_DRAFT_TARGET_BLOCKS
 #define ET_DRAFT_TARGET_BLOCKS 6000
 #endif
-constexpr int kDraftFusedMaxBlocks = ET_DRAFT_FUSED_MAX;
 constexpr int kDraftTargetBlocks = ET_DRAFT_TARGET_BLOCKS;
 constexpr int kAttnTile = 64;            // keys per staged K/V tile
 constexpr int kAttnMaxSplits = 32;       // key splits per (kv head, row block)
 constexpr int kAttnTargetBlocks = 256;   // blocks the split count aims for
 
 struct DraftWs {
-  uint32_t* row_ticket;   // [B][k]
-  uint32_t* seq_ticket;   // [B]
   int32_t* pool_token;    // [B][cap]
   int32_t* pool_parent;
   int32_t* pool_depth;
@@ -67,9 +60,6 @@ struct DraftWs {
   float* part_m;          // [B][k][S][waves]
   float* part_s;          // [B][k][S][waves]
   uint64_t* part_keys;    // [B][k][S][waves][kMaxTopk]
-  float* row_m;           // [B][k]
-  double* row_s;          // [B][k]
-  uint64_t* row_keys;     // [B][k][kMaxTopk]
 };
 
 struct AcceptWs {
@@ -92,7 +82,6 @@ struct Plan {
   int ldt, qdt;           // et_dtype of logits and q/k/v
   int s_draft;            // vocab chunks per row
   int draft_cpb;          // chunks streamed by one draft scan block
-  int draft_split;        // 1: scan and merge launches; 0: one fused launch
   int attn_wr;            // 16-row groups per wave (rows per block 64*wr)
   int attn_nqb, attn_splits;
   // workspace layout

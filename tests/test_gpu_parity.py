@@ -61,6 +61,16 @@ VARIANTS = {
                            sharpness=(1.0,), n_q_heads=2, n_kv_heads=1,
                            head_dim=128, prefix_cap=64, prefix_range=(64, 64),
                            qkv_dtype="bf16", seed=10),
+    # a row's 4 * S wave lists exceed one merge wave: per-block partials
+    "wide_f32": TINY.with_(batch=2, vocab=70000, topk=4, depth=3,
+                           budget_n=10, threshold=0.0, sharpness=(2.5, 0.8),
+                           n_q_heads=2, n_kv_heads=1, head_dim=64,
+                           prefix_cap=64, prefix_range=(1, 64), seed=12),
+    "max_vocab": TINY.with_(batch=2, vocab=262144, topk=16, depth=3,
+                            budget_n=40, threshold=0.0, logits_dtype="bf16",
+                            sharpness=(2.5, 0.8), n_q_heads=4, n_kv_heads=1,
+                            head_dim=128, prefix_cap=128,
+                            prefix_range=(64, 128), qkv_dtype="bf16", seed=13),
     "f32_gqa": TINY.with_(batch=2, vocab=1500, topk=3, depth=4, budget_n=10,
                           threshold=0.0, sharpness=(2.0, 1.0), n_q_heads=4,
                           n_kv_heads=2, head_dim=128, prefix_cap=100,
