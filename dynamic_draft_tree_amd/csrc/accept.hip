@@ -5,10 +5,11 @@
 // speedups use greedy decoding.  At temperature 0 a draft token is
 // accepted iff it equals the target model's argmax at its parent.
 //
-// One launch.  Grid (S chunks, T slot rows, B), 256 threads.  Each block
-// finds the (max logit, lowest id) of one chunk of one target row; the
-// last block of a row merges the chunks into that row's argmax; the last
-// row of a sequence walks the tree from the root.
+// Two launches.  Scan: grid (chunk groups, T slot rows, B), 256 threads;
+// each block streams cpb consecutive chunks of one target row and every
+// wave publishes the (max logit, lowest id) key of its quarter of each
+// chunk.  Walk: one block per sequence reduces each kept row's keys to
+// the row's argmax (in LDS) and one wave walks the tree from the root.
 #include "device.h"
 #include "internal.h"
 
@@ -24,62 +25,95 @@ struct AcceptArgs {
   int32_t* accept_len;
   int32_t* path_slots;
   int32_t* out_tokens;
-  int B, V, T, D, S;
+  int B, V, T, D, S, cpb;
 };
 
+constexpr int kAccWaves = kScanThreads / 64;  // keys per chunk
+
+// Scan: the chunk's loads are issued before n_kept arrives (all T rows
+// are readable memory by contract; rows past n_kept are dropped), so the
+// count's latency hides behind the logits'.
 template <bool BF16, bool VEC, int E>
-__global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
+__global__ __launch_bounds__(256) void accept_scan_kernel(AcceptArgs a) {
   constexpr int kChunkE = kScanThreads * E;
-  const int c = blockIdx.x, srow = blockIdx.y, b = blockIdx.z;
+  constexpr int per = BF16 ? 8 : 4;
+  const int srow = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __shared__ uint64_t s_best[4];
-  __shared__ int s_flag;
-
-  const int n = a.n_kept[b];
-  if (srow > n) return;
-
-  const int64_t esz = BF16 ? 2 : 4;
-  const char* row = (const char*)a.target + (b * a.bstride + srow * a.rstride) * esz;
-  const int base = c * kChunkE;
+  const char* row = (const char*)a.target + (b * a.bstride + srow * a.rstride) * (BF16 ? 2 : 4);
+  const int c0 = blockIdx.x * a.cpb;
+  const int nch = min(a.cpb, a.S - c0);
   float x[E];
-  load_chunk<BF16, VEC, E>(row, base, a.V, tid, x);
-  // phase: chunk loaded
-  // (max logit, lowest id) of the chunk: the lane maximum, the wave
-  // maximum, then the lowest id holding it (a lane's ids increase with e).
-  float mx[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) mx[e] = x[e];
-#pragma unroll
-  for (int w = E / 2; w >= 1; w >>= 1)
-#pragma unroll
-    for (int e = 0; e < w; ++e) mx[e] = fmaxf(mx[e], mx[e + w]);
-  const float wm = wave_max_f32(mx[0]);
-  uint32_t lid = 0xFFFFFFFFu;
-#pragma unroll
-  for (int e = E - 1; e >= 0; --e) {
-    const int id = base + elem_off<BF16>(e, tid);
-    if (x[e] == wm && id < a.V) lid = (uint32_t)id;
-  }
-  const uint32_t wid = wave_min_u32(lid);
-  if (lane == 0) s_best[wave] = wid == 0xFFFFFFFFu ? 0 : logit_key(wm, wid);
-  __syncthreads();
-  // phase: chunk argmax
+  u32x4_t raw[VEC ? chunk_vectors<BF16, E>() : 1];
+  if constexpr (VEC) issue_chunk<BF16, E>(row, c0 * kChunkE, a.V, tid, raw);
+  else load_chunk<BF16, false, E>(row, c0 * kChunkE, a.V, tid, x);
+  if (srow > a.n_kept[b]) return;
   const int64_t rowid = (int64_t)b * a.T + srow;
-  if (tid == 0) {
-    uint64_t m = s_best[0];
-    for (int w = 1; w < 4; ++w) m = s_best[w] > m ? s_best[w] : m;
-    st_agent(&a.ws.part[rowid * a.S + c], m);
+  for (int ci = 0; ci < nch; ++ci) {
+    const int c = c0 + ci;
+    const int base = c * kChunkE;
+    if constexpr (VEC) {
+      decode_chunk<BF16, E>(row, base, a.V, tid, raw, x);
+      if (ci + 1 < nch) issue_chunk<BF16, E>(row, base + kChunkE, a.V, tid, raw);
+    }
+    // phase: chunk loaded
+    // (max logit, lowest id) of the wave's elements: the lane maximum as a
+    // pairwise tree, the wave maximum, then the lowest id holding it (a
+    // lane's ids increase with e).
+    float mx[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) mx[e] = x[e];
+#pragma unroll
+    for (int w = E / 2; w >= 1; w >>= 1)
+#pragma unroll
+      for (int e = 0; e < w; ++e) mx[e] = fmaxf(mx[e], mx[e + w]);
+    const float wm = wave_max_f32(mx[0]);
+    const int lid = base + tid * per;  // element e's id is lid + elem_off(e, 0)
+    uint32_t best = 0xFFFFFFFFu;
+#pragma unroll
+    for (int e = E - 1; e >= 0; --e)
+      if (x[e] == wm && elem_off<BF16>(e, 0) < a.V - lid) best = (uint32_t)(lid + elem_off<BF16>(e, 0));
+    const uint32_t wid = wave_min_u32(best);
+    if (lane == 0)
+      a.ws.part[(rowid * a.S + c) * kAccWaves + wave] = wid == 0xFFFFFFFFu ? 0 : logit_key(wm, wid);
+    if constexpr (!VEC)
+      if (ci + 1 < nch) load_chunk<BF16, false, E>(row, base + kChunkE, a.V, tid, x);
   }
-  // phase: partial published
-  if (!block_arrive_last(&a.ws.row_ticket[rowid], (uint32_t)a.S, &s_flag)) return;
-  if (wave == 0) {
-    uint64_t m = lane < a.S ? ld_agent(&a.ws.part[rowid * a.S + lane]) : 0;
-    m = wave_max_u64(m);
-    if (lane == 0) st_agent(&a.ws.amax[rowid], (int32_t)id_of(m));
+}
+
+// Walk: rows are reduced by segments of SP lanes (SP = the power of two
+// >= the row's key count, at most 64; a lane takes every SP-th key), 16
+// waves at a time, into LDS; then wave 0 walks.
+constexpr int kWalkWaves = 16;
+__global__ __launch_bounds__(kWalkWaves * 64) void accept_walk_kernel(AcceptArgs a) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int s_am[kMaxBudget + 1];
+  const int n = a.n_kept[b];
+  const int P = a.S * kAccWaves;  // keys per row
+  int SP = 1;
+  while (SP < P && SP < 64) SP <<= 1;
+  const int RW = 64 / SP;  // rows per wave
+  const int seg = lane / SP, q = lane - seg * SP;
+  for (int r0 = 0; r0 <= n; r0 += kWalkWaves * RW) {
+    const int s = r0 + wave * RW + seg;
+    uint64_t m = 0;
+    if (s <= n) {
+      const uint64_t* pk = a.ws.part + ((int64_t)b * a.T + s) * P;
+      for (int i = q; i < P; i += SP) {
+        const uint64_t v = pk[i];
+        m = v > m ? v : m;
+      }
+    }
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1)
+      if (d < SP) {
+        const uint64_t o = xor_lane_rt(m, d);
+        m = o > m ? o : m;
+      }
+    if (q == 0 && s <= n) s_am[s] = (int)id_of(m);
   }
-  // phase: row merged
-  if (!block_arrive_last(&a.ws.seq_ticket[b], (uint32_t)(n + 1), &s_flag)) return;
-  // phase: sequence ticket won
+  __syncthreads();
+  // phase: rows merged
   if (wave != 0) return;
 
   // Greedy walk from the root (one wave).  Lane l holds slots l, l+64, ...
@@ -87,28 +121,20 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   // current slot matches.
   const int32_t* tk = a.tokens + (int64_t)b * a.T;
   const int32_t* ps = a.parent_slot + (int64_t)b * a.T;
-  const int32_t* am = a.ws.amax + (int64_t)b * a.T;
-  int r_tok[4], r_par[4], r_am[4];
+  int r_tok[4], r_par[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int s = lane + 64 * i;
     const bool ok = s <= n;
     r_tok[i] = ok ? tk[s] : -1;
     r_par[i] = ok ? ps[s] : -2;
-    r_am[i] = ok ? ld_agent(&am[s]) : -1;
   }
-  // phase: walk inputs read
   int32_t* path = a.path_slots + (int64_t)b * (a.D + 1);
   int32_t* outt = a.out_tokens + (int64_t)b * (a.D + 1);
   int cur = 0, len = 0;
   if (lane == 0) path[0] = 0;
-  auto amax_of = [&](int s) {
-    const int w = s >> 6, l = s & 63;
-    const int v = w == 0 ? r_am[0] : w == 1 ? r_am[1] : w == 2 ? r_am[2] : r_am[3];
-    return __builtin_amdgcn_readlane(v, l);
-  };
   for (;;) {
-    const int want = amax_of(cur);
+    const int want = s_am[cur];
     int found = -1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -124,10 +150,8 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
     cur = found;
   }
   // phase: walk done
-  // readlane must run with every lane active (amax_of selects per lane).
-  const int bonus = amax_of(cur);
   if (lane == 0) {
-    outt[len] = bonus;
+    outt[len] = s_am[cur];
     a.accept_len[b] = len;
   }
   for (int i = lane; i <= a.D; i += 64) {
@@ -159,17 +183,15 @@ hipError_t launch_accept(const Plan& p, const AcceptWs& w, const void* target,
   a.V = p.V;
   a.T = p.T;
   a.D = p.D;
-  // Chunks of 16K bf16 (8K fp32) elements: eight 16-byte loads in flight
-  // per thread and a merge fan-in of 8 per 128K-token row
-  constexpr int EB = 64, EF = 32;
+  a.S = p.s_accept;
+  a.cpb = p.accept_cpb;
   const bool bf = p.ldt == ET_BF16;
-  const int ce = kScanThreads * (bf ? EB : EF);
-  a.S = (p.V + ce - 1) / ce;
-  dim3 grid(a.S, p.T, p.B);
-  if (bf && vec) accept_kernel<true, true, EB><<<grid, kScanThreads, 0, s>>>(a);
-  else if (bf) accept_kernel<true, false, EB><<<grid, kScanThreads, 0, s>>>(a);
-  else if (vec) accept_kernel<false, true, EF><<<grid, kScanThreads, 0, s>>>(a);
-  else accept_kernel<false, false, EF><<<grid, kScanThreads, 0, s>>>(a);
+  dim3 grid((p.s_accept + p.accept_cpb - 1) / p.accept_cpb, p.T, p.B);
+  if (bf && vec) accept_scan_kernel<true, true, kAccElemsBf16><<<grid, kScanThreads, 0, s>>>(a);
+  else if (bf) accept_scan_kernel<true, false, kAccElemsBf16><<<grid, kScanThreads, 0, s>>>(a);
+  else if (vec) accept_scan_kernel<false, true, kAccElemsF32><<<grid, kScanThreads, 0, s>>>(a);
+  else accept_scan_kernel<false, false, kAccElemsF32><<<grid, kScanThreads, 0, s>>>(a);
+  accept_walk_kernel<<<p.B, kWalkWaves * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 

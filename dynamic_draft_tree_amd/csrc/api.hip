@@ -38,10 +38,9 @@ et::Plan* as_plan(et_plan_t p) { return reinterpret_cast<et::Plan*>(p); }
 
 // Region indices of Plan::off.
 enum {
-  R_ACC_ROW_TICKET, R_ACC_SEQ_TICKET,
   R_POOL_TOKEN, R_POOL_PARENT, R_POOL_DEPTH, R_POOL_CONF, R_POOL_VALUE,
   R_POOL_COUNT, R_ROOT, R_FRONTIER, R_FRONTIER_VAL, R_FRONTIER_COUNT, R_PART_M, R_PART_S,
-  R_PART_KEYS, R_ACC_PART, R_ACC_AMAX,
+  R_PART_KEYS, R_ACC_PART,
   R_ATT_O, R_ATT_M, R_ATT_L, R_COUNT
 };
 
@@ -50,8 +49,6 @@ void layout(et::Plan& p) {
   const size_t units = (size_t)p.B * p.Hkv * p.attn_nqb * p.attn_splits;
   const size_t att_rows = p.attn_splits > 1 ? units * 64 * p.attn_wr : 0;
   size_t sz[R_COUNT] = {};
-  sz[R_ACC_ROW_TICKET] = B * T * 4;
-  sz[R_ACC_SEQ_TICKET] = B * 4;
   sz[R_POOL_TOKEN] = sz[R_POOL_PARENT] = sz[R_POOL_DEPTH] = B * cap * 4;
   sz[R_POOL_CONF] = sz[R_POOL_VALUE] = B * cap * 4;
   sz[R_POOL_COUNT] = sz[R_ROOT] = B * 4;
@@ -62,20 +59,25 @@ void layout(et::Plan& p) {
   const size_t W4 = et::kScanThreads / 64;
   sz[R_PART_M] = sz[R_PART_S] = B * k * S * W4 * 4;
   sz[R_PART_KEYS] = B * k * S * W4 * et::kMaxTopk * 8;
-  sz[R_ACC_PART] = B * T * S * 8;
-  sz[R_ACC_AMAX] = B * T * 4;
+  sz[R_ACC_PART] = B * T * p.s_accept * W4 * 8;
   sz[R_ATT_O] = att_rows * p.HD * 4;
   sz[R_ATT_M] = sz[R_ATT_L] = att_rows * 4;
   size_t off = 0;
   for (int r = 0; r < R_COUNT; ++r) {
     p.off[r] = off;
     off += align256(sz[r]);
-    if (r == R_ACC_SEQ_TICKET) {
-      p.off_counters = 0;
-      p.n_counters = off / 4;  // counters occupy the first regions
-    }
   }
   p.ws_bytes = off;
+}
+
+// Chunks per scan block for `rows` rows of S chunks: 1 unless rows * S
+// blocks would be many times what the chip holds; then spread evenly
+// over each row's blocks.
+int chunks_per_block(long long rows, int S) {
+  long long cpb = (rows * S + et::kScanTargetBlocks - 1) / et::kScanTargetBlocks;
+  if (cpb > S) cpb = S;
+  const long long per_row = (S + cpb - 1) / cpb;
+  return (int)((S + per_row - 1) / per_row);
 }
 
 template <typename T>
@@ -107,10 +109,7 @@ DraftWs draft_ws(const Plan& p, void* ws) {
 
 AcceptWs accept_ws(const Plan& p, void* ws) {
   AcceptWs w;
-  w.row_ticket = at<uint32_t>(ws, p, R_ACC_ROW_TICKET);
-  w.seq_ticket = at<uint32_t>(ws, p, R_ACC_SEQ_TICKET);
   w.part = at<uint64_t>(ws, p, R_ACC_PART);
-  w.amax = at<int32_t>(ws, p, R_ACC_AMAX);
   return w;
 }
 
@@ -191,15 +190,9 @@ int et_plan_create(const et_config* cfg, et_plan_t* out) {
   p->ldt = c.logits_dtype;
   p->qdt = c.qkv_dtype;
   p->s_draft = (p->V + et::chunk_elems(p->ldt) - 1) / et::chunk_elems(p->ldt);
-  {
-    // chunks per draft scan block: 1 unless B * k * S blocks would be
-    // many times what the chip holds; then spread evenly over the row
-    const long long blocks = (long long)p->B * p->k * p->s_draft;
-    long long cpb = (blocks + et::kDraftTargetBlocks - 1) / et::kDraftTargetBlocks;
-    if (cpb > p->s_draft) cpb = p->s_draft;
-    const long long per_row = (p->s_draft + cpb - 1) / cpb;
-    p->draft_cpb = (int)((p->s_draft + per_row - 1) / per_row);
-  }
+  p->s_accept = (p->V + et::accept_chunk_elems(p->ldt) - 1) / et::accept_chunk_elems(p->ldt);
+  p->draft_cpb = chunks_per_block((long long)p->B * p->k, p->s_draft);
+  p->accept_cpb = chunks_per_block((long long)p->B * p->T, p->s_accept);
   // Attention: the G*T query rows of one kv head are cut into blocks of
   // 64 or 128 rows (128 when that adds no padding rows: each K/V tile then
   // serves twice the rows); the keys are split until the grid has about
@@ -244,12 +237,11 @@ int et_workspace_init(et_plan_t plan, void* ws, et_stream_t stream) {
   CHECK_PTR(ws);
   if (((uintptr_t)ws & 255u) != 0)
     return fail(ET_EINVAL, "%s: workspace not 256-byte aligned", fn);
+  (void)stream;  // no device state needs clearing
   et::Plan& p = *as_plan(plan);
   p.last_ws = nullptr;
   p.last_step = 0;
-  return hip_status(et::launch_clear_u32(static_cast<uint32_t*>(ws),
-                                         p.n_counters, (hipStream_t)stream),
-                    fn);
+  return ET_OK;
 }
 
 int et_draft_step(et_plan_t plan, void* ws, int32_t step,

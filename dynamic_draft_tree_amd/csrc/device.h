@@ -7,8 +7,6 @@
 
 namespace et {
 
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
   return __uint_as_float(h << 16);
 }
@@ -111,15 +109,6 @@ __device__ __forceinline__ T xor_lane_rt(T v, int m) {
   }
 }
 
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int src) {
-  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, src);
-  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
-  return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ float readlane_f32(float v, int src) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
-}
-
 // Butterfly reductions: every lane ends with the same result.
 __device__ __forceinline__ float wave_max_f32(float v) {
 #pragma unroll
@@ -127,16 +116,6 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   return v;
 }
 __device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += xor_lane_rt(v, m);
-  return v;
-}
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += xor_lane_rt(v, m);
-  return v;
-}
-__device__ __forceinline__ int wave_sum_i32(int v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += xor_lane_rt(v, m);
   return v;
@@ -181,267 +160,11 @@ __device__ __forceinline__ int wave_excl_prefix_small(int v, int* total) {
   return pre;
 }
 
-// x[e] for a per-lane index e in [0, E) via a select tree (no dynamic
-// register indexing).
-template <int E>
-__device__ __forceinline__ float select_elem(const float (&x)[E], int e) {
-  float t[E];
-#pragma unroll
-  for (int i = 0; i < E; ++i) t[i] = x[i];
-#pragma unroll
-  for (int w = E / 2; w >= 1; w >>= 1)
-#pragma unroll
-    for (int i = 0; i < w; ++i) t[i] = (e & w) ? t[i + w] : t[i];
-  return t[0];
-}
-
-// Bitonic sort across the 64 lanes, descending (lane 0 = largest).
-template <typename T>
-__device__ __forceinline__ T wave_sort_desc(T v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1)
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const T o = xor_lane_rt(v, j);
-      const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
-      v = take_max ? (o > v ? o : v) : (o < v ? o : v);
-    }
-  return v;
-}
-__device__ __forceinline__ float wave_sort_desc_f32(float v) {
-  return wave_sort_desc<float>(v);
-}
-// Bitonic sort inside each 16-lane row (DPP only), descending.
-__device__ __forceinline__ float row16_sort_desc_f32(float v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int k = 2; k <= 16; k <<= 1)
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const float o = xor_lane_rt(v, j);
-      const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
-      v = take_max ? fmaxf(v, o) : fminf(v, o);
-    }
-  return v;
-}
-// A value with at least k (<= 16) of the wave's 64 values >= it: the
-// minimum over the four 16-lane rows of each row's ceil(k/4)-th largest.
-__device__ __forceinline__ float wave_kth_lower_bound(float v, int k) {
-  const float srt = row16_sort_desc_f32(v);
-  const int q = (k + 3) / 4 - 1;
-  const float r0 = readlane_f32(srt, q), r1 = readlane_f32(srt, 16 + q);
-  const float r2 = readlane_f32(srt, 32 + q), r3 = readlane_f32(srt, 48 + q);
-  return fminf(fminf(r0, r1), fminf(r2, r3));
-}
-__device__ __forceinline__ uint64_t wave_sort_desc_u64(uint64_t v) {
-  return wave_sort_desc<uint64_t>(v);
-}
-
-// Make this wave's LDS writes visible to its own later LDS reads.
 // LDS writes of this wave visible to its later LDS reads, without waiting
 // for outstanding global loads.
 __device__ __forceinline__ void wave_lds_fence() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_wave_barrier();
-}
-
-__device__ __forceinline__ void wave_lds_sync() {
-  __threadfence_block();
-  __builtin_amdgcn_wave_barrier();
-}
-
-// Top-k (k <= 16) of N keys per lane (distinct, 0 = empty) across the
-// wave; lanes 0..k-1 return the result in descending order, other lanes
-// and missing entries return 0.  scratch: 64 u64 of LDS owned by the wave.
-// Fast path: keep only keys >= the k-th largest lane maximum (a lower
-// bound of the k-th largest key) and sort those if they fit one wave;
-// otherwise k rounds of wave-wide maximum.
-template <int N>
-__device__ uint64_t wave_topk_u64(const uint64_t (&keys)[N], int k,
-                                  uint64_t* scratch) {
-  const int lane = lane_id();
-  uint64_t lmax = 0;
-#pragma unroll
-  for (int i = 0; i < N; ++i) lmax = keys[i] > lmax ? keys[i] : lmax;
-  const uint64_t sorted = wave_sort_desc_u64(lmax);
-  uint64_t L = readlane_u64(sorted, k - 1);
-  if (L == 0) L = 1;  // fewer than k lanes hold keys: take every key
-  int c = 0;
-#pragma unroll
-  for (int i = 0; i < N; ++i) c += keys[i] >= L;
-  const int total = wave_sum_i32(c);
-  if (total <= 64) {
-    int base = 0;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      int cnt;
-      const bool pred = keys[i] >= L;
-      const int r = ballot_rank(pred, &cnt);
-      if (pred) scratch[base + r] = keys[i];
-      base += cnt;
-    }
-    wave_lds_sync();
-    uint64_t v = lane < total ? scratch[lane] : 0;
-    wave_lds_sync();
-    v = wave_sort_desc_u64(v);
-    return lane < k ? v : 0;
-  }
-  uint64_t res = 0, prev = ~0ull;
-  for (int r = 0; r < k; ++r) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-      if (keys[i] < prev && keys[i] > best) best = keys[i];
-    const uint64_t w = wave_max_u64(best);
-    if (lane == r) res = w;
-    prev = w;
-    if (w == 0) break;
-  }
-  return res;
-}
-
-// Block-wide max / sum of one float per thread (all threads get it).
-template <int NT>
-__device__ __forceinline__ float block_max_f32(float v, float* red) {
-  v = wave_max_f32(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int w = 1; w < NT / 64; ++w) r = fmaxf(r, red[w]);
-  return r;
-}
-template <int NT>
-__device__ __forceinline__ float block_sum_f32(float v, float* red) {
-  v = wave_sum_f32(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int w = 1; w < NT / 64; ++w) r += red[w];
-  return r;
-}
-
-// ---- block-wide selection -------------------------------------------------
-// Top-k (k <= 16) of n distinct keys held in LDS, written in descending
-// order to out[0..k) (0 where n < k).  n <= kRankMax: every thread ranks
-// its keys by counting the larger keys (LDS broadcast reads, no dependent
-// chains).  Larger n: k rounds of block-wide maximum.  All threads of the
-// block must call it; it starts and ends with a barrier.
-constexpr int kRankMax = 256;
-
-template <int NT>
-__device__ void block_topk(const uint64_t* keys, int n, int k, uint64_t* out,
-                           uint64_t* red /* >= NT / 64 entries */) {
-  __syncthreads();
-  const int tid = threadIdx.x;
-  if (n <= kRankMax) {
-    for (int t = tid; t < n; t += NT) {
-      const uint64_t me = keys[t];
-      int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
-      int j = 0;
-      for (; j + 4 <= n; j += 4) {
-        r0 += keys[j] > me;
-        r1 += keys[j + 1] > me;
-        r2 += keys[j + 2] > me;
-        r3 += keys[j + 3] > me;
-      }
-      for (; j < n; ++j) r0 += keys[j] > me;
-      const int rank = (r0 + r1) + (r2 + r3);
-      if (rank < k) out[rank] = me;
-    }
-    for (int r = n + tid; r < k; r += NT) out[r] = 0;
-    __syncthreads();
-    return;
-  }
-  uint64_t prev = ~0ull;
-  for (int r = 0; r < k; ++r) {
-    uint64_t best = 0;
-    for (int t = tid; t < n; t += NT) {
-      const uint64_t v = keys[t];
-      if (v < prev && v > best) best = v;
-    }
-    best = wave_max_u64(best);
-    if ((tid & 63) == 0) red[tid >> 6] = best;
-    __syncthreads();
-    uint64_t w = red[0];
-#pragma unroll
-    for (int q = 1; q < NT / 64; ++q) w = red[q] > w ? red[q] : w;
-    if (tid == 0) out[r] = w;
-    prev = w;
-    __syncthreads();
-  }
-}
-
-// ---- hand-off between blocks of one launch -------------------------------
-// Data that one block produces and a later-arriving block of the same
-// launch consumes is written and read with relaxed agent-scope atomic
-// accesses, which gfx950 performs coherently across the XCDs' separate L2
-// caches (sc1 loads/stores).  Ordering comes from waiting for the
-// producer's stores to complete before it takes its arrival ticket.  This
-// avoids agent-scope fences, which write back and invalidate the L2.
-__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_agent(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_agent(int32_t* p, int32_t v) {
-  st_agent(reinterpret_cast<uint32_t*>(p), (uint32_t)v);
-}
-__device__ __forceinline__ void st_agent(float* p, float v) {
-  st_agent(reinterpret_cast<uint32_t*>(p), __float_as_uint(v));
-}
-__device__ __forceinline__ void st_agent(double* p, double v) {
-  st_agent(reinterpret_cast<uint64_t*>(p), (uint64_t)__double_as_longlong(v));
-}
-__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ld_agent(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int32_t ld_agent(const int32_t* p) {
-  return (int32_t)ld_agent(reinterpret_cast<const uint32_t*>(p));
-}
-__device__ __forceinline__ float ld_agent(const float* p) {
-  return __uint_as_float(ld_agent(reinterpret_cast<const uint32_t*>(p)));
-}
-__device__ __forceinline__ double ld_agent(const double* p) {
-  return __longlong_as_double((long long)ld_agent(reinterpret_cast<const uint64_t*>(p)));
-}
-
-// Wait until this wave's stores have completed (s_waitcnt vmcnt(0)); the
-// signal fences keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void wait_stores() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// Block-level "last arrival" ticket.  Every wave waits for its own stores
-// (published with st_agent) to complete, the block synchronises, thread 0
-// adds the n units the block finished, and the block whose addition
-// completes `total` resets the counter.  Returns the same value in every thread of the block; the
-// winner then reads the published data with ld_agent.
-__device__ __forceinline__ bool block_arrive_last(uint32_t* ctr,
-                                                  uint32_t total,
-                                                  int* s_flag,
-                                                  uint32_t n = 1u) {
-  wait_stores();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t prev = __hip_atomic_fetch_add(ctr, n, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    int last = prev + n == total;
-    if (last) st_agent(ctr, 0u);
-    *s_flag = last;
-  }
-  __syncthreads();
-  return *s_flag != 0;
 }
 
 // ---- row chunk loader shared by the vocab scans ---------------------------

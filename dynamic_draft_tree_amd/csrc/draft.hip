@@ -68,8 +68,8 @@ __device__ __forceinline__ uint64_t key_floor(float x) {
 }
 
 // Chunks [c0, c0 + nch) of row j of sequence b: per chunk, the block's
-// (max, sum of exp) and its top-k logit keys, published with agent-scope
-// stores; with WAVE, each wave publishes its own 1/4 of the chunk instead
+// (max, sum of exp) and its top-k logit keys, stored for the merge launch;
+// with WAVE, each wave publishes its own 1/4 of the chunk instead
 // (no block-level step, the waves never wait for one another).  The caller has issued the first chunk's loads (raw, or x on
 // the element-wise path); the next chunk's loads are issued once the
 // current chunk's values are staged in LDS.  On the vector path the
@@ -214,12 +214,12 @@ __device__ __forceinline__ void scan_chunks(const DraftArgs& a, const char* row,
       int rank = 0;
 #pragma unroll 8
       for (int q = 0; q < wtot; ++q) rank += wl[q] > me;
-      if (rank < k) st_agent(&dst[rank], me);
+      if (rank < k) dst[rank] = me;
     }
-    if (lane >= wtot && lane < k) st_agent(&dst[lane], (uint64_t)0);
+    if (lane >= wtot && lane < k) dst[lane] = 0;
     if (lane == 0) {
-      st_agent(&a.ws.part_m[pe], mw);
-      st_agent(&a.ws.part_s[pe], sw);
+      a.ws.part_m[pe] = mw;
+      a.ws.part_s[pe] = sw;
     }
     // phase: wave published
     if constexpr (!VEC)
@@ -259,16 +259,16 @@ __device__ __forceinline__ void scan_chunks(const DraftArgs& a, const char* row,
     int rank = 0;
 #pragma unroll 8
     for (int q = 0; q < nb; ++q) rank += s_bc[q] > me;
-    if (rank < k) st_agent(&dst[rank], me);
+    if (rank < k) dst[rank] = me;
   }
-  if (tid >= nb && tid < k) st_agent(&dst[tid], (uint64_t)0);
+  if (tid >= nb && tid < k) dst[tid] = 0;
   if (tid == 0) {
     float sb = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w)
       sb += s_wf[1][w] > -INFINITY ? s_wf[2][w] * expf(s_wf[1][w] - mb) : 0.f;
-    st_agent(&a.ws.part_m[pe], mb);
-    st_agent(&a.ws.part_s[pe], sb);
+    a.ws.part_m[pe] = mb;
+    a.ws.part_s[pe] = sb;
   }
   if (ci + 1 < nch) {
     if constexpr (!VEC) load_chunk<BF16, false, E>(row, base + kChunkE, a.V, tid, x);
@@ -316,12 +316,12 @@ __device__ __forceinline__ void merge_sequence(const DraftArgs& a, int b, int F)
     const int par = hp ? a.ws.frontier[fs] : -1;
     const float vpar = hp ? a.ws.frontier_val[fs] : 1.0f;
     const int64_t e = e0 + (int64_t)jr * S + q;
-    const float pm = on ? ld_agent(&a.ws.part_m[e]) : -INFINITY;
-    const float ps = on ? ld_agent(&a.ws.part_s[e]) : 0.f;
+    const float pm = on ? a.ws.part_m[e] : -INFINITY;
+    const float ps = on ? a.ws.part_s[e] : 0.f;
     uint64_t pk[kMaxTopk];
 #pragma unroll
     for (int r = 0; r < kMaxTopk; ++r)
-      pk[r] = (on && r < kStage && r < k) ? ld_agent(&a.ws.part_keys[e * kMaxTopk + r]) : 0;
+      pk[r] = (on && r < kStage && r < k) ? a.ws.part_keys[e * kMaxTopk + r] : 0;
     // phase: partials read
     float m = pm;
 #pragma unroll
@@ -353,7 +353,7 @@ __device__ __forceinline__ void merge_sequence(const DraftArgs& a, int b, int F)
       if (cq == kStage) {
 #pragma unroll
         for (int r = kStage; r < kMaxTopk; ++r)
-          if (r < k) pk[r] = ld_agent(&a.ws.part_keys[e * kMaxTopk + r]);
+          if (r < k) pk[r] = a.ws.part_keys[e * kMaxTopk + r];
 #pragma unroll
         for (int r = kStage; r < kMaxTopk; ++r)
           cq += (r < k && pk[r] != 0 && pk[r] >= Lk) ? 1 : 0;
@@ -377,7 +377,7 @@ __device__ __forceinline__ void merge_sequence(const DraftArgs& a, int b, int F)
           if (r < cq) lst[off + r] = pk[r];
       }
     }
-    wave_lds_sync();
+    wave_lds_fence();
     // phase: row list written
     if (jr < F && fits) {
       const uint64_t* lst = &s_rc[jr * kRowCap];
@@ -401,7 +401,7 @@ __device__ __forceinline__ void merge_sequence(const DraftArgs& a, int b, int F)
       for (int r = 0; r < k; ++r) {
         uint64_t best = 0;
         for (int t = lane; t < S * k; t += 64) {
-          const uint64_t v = ld_agent(&a.ws.part_keys[(e0 + (int64_t)jo * S + t / k) * kMaxTopk + t % k]);
+          const uint64_t v = a.ws.part_keys[(e0 + (int64_t)jo * S + t / k) * kMaxTopk + t % k];
           if (v < prevk && v > best) best = v;
         }
         const uint64_t w = wave_max_u64(best);
@@ -409,7 +409,7 @@ __device__ __forceinline__ void merge_sequence(const DraftArgs& a, int b, int F)
         prevk = w;
       }
     }
-    wave_lds_sync();
+    wave_lds_fence();
     // phase: row merged
     // Children of the row, in rank order (conf decreasing): child r of row
     // jr is pool node P0 + jr * k + r.
@@ -467,7 +467,7 @@ __device__ __forceinline__ void merge_sequence(const DraftArgs& a, int b, int F)
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         if (ck[u] != 0 && (uint32_t)(ck[u] >> 32) >= T) wbuf[o++] = ck[u];
-      wave_lds_sync();
+      wave_lds_fence();
       bool kept = false;
       if (lane < n) {
         const uint64_t me = wbuf[lane];

@@ -32,16 +32,24 @@ constexpr int kMaxPool = 4095;           // pool index fits the 12-bit field
 constexpr int kScanThreads = 256;        // threads per row-scan block
 constexpr int kElemsBf16 = 32;           // bf16 elements per thread (4 x 16 B)
 constexpr int kElemsF32 = 16;            // fp32 elements per thread (4 x 16 B)
+// accept scan: 16K bf16 (8K fp32) elements per chunk, eight 16-byte loads
+// in flight per thread
+constexpr int kAccElemsBf16 = 64;
+constexpr int kAccElemsF32 = 32;
+constexpr int accept_chunk_elems(int dtype) {
+  return kScanThreads * (dtype == ET_BF16 ? kAccElemsBf16 : kAccElemsF32);
+}
 // vocab elements per row-scan block for a logits dtype
 constexpr int chunk_elems(int dtype) {
   return kScanThreads * (dtype == ET_BF16 ? kElemsBf16 : kElemsF32);
 }
-// Draft scan grids above this many one-chunk blocks give each block
-// several chunks of its row (the chip holds a few thousand at once).
-#ifndef ET_DRAFT_TARGET_BLOCKS
-#define ET_DRAFT_TARGET_BLOCKS 6000
+// Scan grids (draft and accept) above this many one-chunk blocks give
+// each block several chunks of its row (the chip holds a few thousand
+// blocks at once).
+#ifndef ET_SCAN_TARGET_BLOCKS
+#define ET_SCAN_TARGET_BLOCKS 6000
 #endif
-constexpr int kDraftTargetBlocks = ET_DRAFT_TARGET_BLOCKS;
+constexpr int kScanTargetBlocks = ET_SCAN_TARGET_BLOCKS;
 constexpr int kAttnTile = 64;            // keys per staged K/V tile
 constexpr int kAttnMaxSplits = 32;       // key splits per (kv head, row block)
 constexpr int kAttnTargetBlocks = 256;   // blocks the split count aims for
@@ -63,10 +71,7 @@ struct DraftWs {
 };
 
 struct AcceptWs {
-  uint32_t* row_ticket;   // [B][T]
-  uint32_t* seq_ticket;   // [B]
-  uint64_t* part;         // [B][T][S]
-  int32_t* amax;          // [B][T]
+  uint64_t* part;         // [B][T][S][waves] (max logit, lowest id) keys
 };
 
 struct AttnWs {
@@ -82,10 +87,11 @@ struct Plan {
   int ldt, qdt;           // et_dtype of logits and q/k/v
   int s_draft;            // vocab chunks per row
   int draft_cpb;          // chunks streamed by one draft scan block
+  int s_accept;           // target-row chunks per row
+  int accept_cpb;         // chunks streamed by one accept scan block
   int attn_wr;            // 16-row groups per wave (rows per block 64*wr)
   int attn_nqb, attn_splits;
   // workspace layout
-  size_t off_counters, n_counters;
   size_t off[32];
   size_t ws_bytes;
   // call-order check
@@ -98,7 +104,6 @@ AcceptWs accept_ws(const Plan& p, void* ws);
 AttnWs attn_ws(const Plan& p, void* ws);
 
 // Launchers (return hipError_t of the launch).
-hipError_t launch_clear_u32(uint32_t* p, size_t n, hipStream_t s);
 hipError_t launch_draft_step(const Plan& p, const DraftWs& w, int step,
                              const int32_t* root_tokens, const void* logits,
                              int64_t bstride, int64_t rstride, bool vec,

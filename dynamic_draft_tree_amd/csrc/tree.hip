@@ -279,18 +279,4 @@ hipError_t launch_pool_export(const Plan& p, const DraftWs& w, int32_t* token,
   return hipGetLastError();
 }
 
-__global__ void clear_u32_kernel(uint32_t* p, size_t n) {
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x)
-    p[i] = 0u;
-}
-
-hipError_t launch_clear_u32(uint32_t* p, size_t n, hipStream_t s) {
-  int blocks = (int)((n + 255) / 256);
-  if (blocks > 1024) blocks = 1024;
-  if (blocks < 1) blocks = 1;
-  clear_u32_kernel<<<blocks, 256, 0, s>>>(p, n);
-  return hipGetLastError();
-}
-
 }  // namespace et

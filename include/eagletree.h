@@ -102,15 +102,18 @@ int et_plan_destroy(et_plan_t plan);
 
 /* Bytes of device workspace the plan needs (256-byte aligned base
  * required).  The workspace holds the candidate pool, the frontier,
- * per-chunk partial results and arrival counters. */
+ * per-chunk partial results of the vocab scans and the attention split
+ * partials. */
 size_t et_workspace_bytes(et_plan_t plan);
 
 /* Pool capacity per sequence: topk + (depth - 1) * topk^2 nodes. */
 int32_t et_pool_capacity(et_plan_t plan);
 
-/* Clear the workspace's arrival counters with a fill kernel on `stream`.
- * Must run once after the workspace is allocated and before its first
- * use; afterwards every call leaves the counters cleared again. */
+/* Bind a freshly allocated workspace to the plan: checks its alignment
+ * (256 bytes) and resets the plan's record of the call order.  Must run
+ * once after the workspace is allocated and before its first use.  No
+ * device memory needs clearing (every call writes what it later reads),
+ * so nothing is launched on `stream`. */
 int et_workspace_init(et_plan_t plan, void* ws, et_stream_t stream);
 
 /* One expansion layer ([P1] s4.1; [P2] value equation; [P3] Expand).
@@ -194,7 +197,9 @@ int et_tree_attention(et_plan_t plan, void* ws, const void* q,
 /* Greedy acceptance at temperature 0 ([P1] s2.1: tokens are accepted in
  * order along the draft; [P4] s五: greedy decoding).  Target row s of
  * sequence b is at target_logits + b * batch_stride + s * row_stride
- * (dtype = logits_dtype), for s = 0 .. n_kept[b].  With a_s = argmax of
+ * (dtype = logits_dtype), for s = 0 .. n_kept[b].  All T rows s = 0 .. N
+ * must be readable memory: they are loaded before n_kept[b] is known, and
+ * rows past n_kept[b] are then ignored (any bits).  With a_s = argmax of
  * row s (ties: lowest id), the walk starts at slot 0 and moves to the
  * child c of the current slot whose token equals a_current, while one
  * exists.  Outputs (device int32):

@@ -243,6 +243,28 @@ def test_accept_exact(name):
     print(f"{name}: accept_len {plan.accept_len.cpu().numpy()[:8]}")
 
 
+@pytest.mark.parametrize("name", ["tiny", "odd_vocab", "small_bf16"])
+def test_target_rows_past_n_kept_are_ignored(name):
+    """Target rows s > n_kept are loaded before n_kept is known but never
+    used: NaN there changes no output bit."""
+    r = _run(name)
+    w, plan, inp = r["w"], r["plan"], r["inp"]
+    n_kept = r["gpu_rr"]["n_kept"]
+    if not (n_kept < w.budget_n).any():
+        pytest.skip("every sequence kept N nodes")
+    td = to_dev(inp["target"])
+    plan.accept(td)
+    torch.cuda.synchronize()
+    ref = [t.cpu().clone() for t in (plan.accept_len, plan.path_slots, plan.out_tokens)]
+    poisoned = td.clone()
+    for b in range(w.batch):
+        poisoned[b, int(n_kept[b]) + 1:] = float("nan")
+    plan.accept(poisoned)
+    torch.cuda.synchronize()
+    for a, t in zip(ref, (plan.accept_len, plan.path_slots, plan.out_tokens)):
+        assert torch.equal(a, t.cpu())
+
+
 def test_cycle_is_deterministic():
     """Two cycles (second on a fresh workspace) give identical bits."""
     d = _lib()
