@@ -194,13 +194,17 @@ int et_plan_create(const et_config* cfg, et_plan_t* out) {
   p->draft_cpb = chunks_per_block((long long)p->B * p->k, p->s_draft);
   p->accept_cpb = chunks_per_block((long long)p->B * p->T, p->s_accept);
   // Attention: the G*T query rows of one kv head are cut into blocks of
-  // 64 or 128 rows (128 when that adds no padding rows: each K/V tile then
-  // serves twice the rows); the keys are split until the grid has about
-  // one block per compute unit.
+  // 64 or 128 rows.  When the kv heads alone leave most compute units idle
+  // (keys must be split, and every split writes partials of its block's
+  // rows), 64-row blocks keep the partials small; otherwise 128 rows when
+  // that adds no padding rows (each K/V tile then serves twice the rows).
+  // The keys are split until the grid has about one block per compute
+  // unit.
   {
     const int R = p->T * p->G;
     const int q1 = (R + 63) / 64, q2 = (R + 127) / 128;
-    p->attn_wr = q2 * 128 <= q1 * 64 ? 2 : 1;
+    const bool split_keys = (long long)p->B * p->Hkv * q1 < et::kAttnTargetBlocks;
+    p->attn_wr = !split_keys && q2 * 128 <= q1 * 64 ? 2 : 1;
     p->attn_nqb = p->attn_wr == 2 ? q2 : q1;
   }
   const long long units = (long long)p->B * p->Hkv * p->attn_nqb;
