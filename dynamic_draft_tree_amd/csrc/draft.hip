@@ -36,7 +36,6 @@ struct DraftArgs {
 
 constexpr int kWaves = kScanThreads / 64;  // waves per scan block
 constexpr int kWaveCap = 64;             // candidate slots per wave
-constexpr int kStage = 4;                // keys per chunk list read up front
 constexpr int kRowCap = 64;              // merge candidates per row
 
 // The k-th largest of the wave's 64 keys (k <= 64): the largest T whose
@@ -207,16 +206,18 @@ __device__ __forceinline__ void scan_chunks(const DraftArgs& a, const char* row,
     // The wave's list, ranked by counting; its entry is partial
     // (row, chunk, wave).
     wave_lds_fence();
-    const int64_t pe = (((int64_t)b * k + j) * S + c) * kWaves + wave;
-    uint64_t* dst = &a.ws.part_keys[pe * kMaxTopk];
+    const int64_t rowid = (int64_t)b * k + j;
+    const int li = c * kWaves + wave;  // list index within the row
+    const int64_t pe = rowid * a.parts + li;
+    uint64_t* dst = &a.ws.part_keys[rowid * kMaxTopk * a.parts + li];  // rank r at r * parts
     if (lane < wtot) {
       const uint64_t me = wl[lane];
       int rank = 0;
 #pragma unroll 8
       for (int q = 0; q < wtot; ++q) rank += wl[q] > me;
-      if (rank < k) dst[rank] = me;
+      if (rank < k) dst[(int64_t)rank * a.parts] = me;
     }
-    if (lane >= wtot && lane < k) dst[lane] = 0;
+    if (lane >= wtot && lane < k) dst[(int64_t)lane * a.parts] = 0;
     if (lane == 0) {
       a.ws.part_m[pe] = mw;
       a.ws.part_s[pe] = sw;
@@ -253,15 +254,15 @@ __device__ __forceinline__ void scan_chunks(const DraftArgs& a, const char* row,
   const int nb = s_count;
   const int64_t rowid = (int64_t)b * k + j;
   const int64_t pe = rowid * S + c;  // this block's partial entry
-  uint64_t* dst = &a.ws.part_keys[pe * kMaxTopk];
+  uint64_t* dst = &a.ws.part_keys[rowid * kMaxTopk * S + c];  // rank r at r * S
   for (int t = tid; t < nb; t += NT) {
     const uint64_t me = s_bc[t];
     int rank = 0;
 #pragma unroll 8
     for (int q = 0; q < nb; ++q) rank += s_bc[q] > me;
-    if (rank < k) dst[rank] = me;
+    if (rank < k) dst[(int64_t)rank * S] = me;
   }
-  if (tid >= nb && tid < k) dst[tid] = 0;
+  if (tid >= nb && tid < k) dst[(int64_t)tid * S] = 0;
   if (tid == 0) {
     float sb = 0.f;
 #pragma unroll
@@ -277,12 +278,31 @@ __device__ __forceinline__ void scan_chunks(const DraftArgs& a, const char* row,
   }
 }
 
-// The F rows of sequence b, every chunk published: row softmax statistics
-// and top-k, children appended to the pool, next frontier.  Needs the
-// whole block of NW waves.
-template <bool BF16, int NW>
-__device__ __forceinline__ void merge_sequence(const DraftArgs& a, int b, int F) {
+// A sequence whose tree stopped growing: no rows, empty next frontier.
+__device__ __forceinline__ void empty_frontier(const DraftArgs& a, int b) {
+  const int tid = threadIdx.x, cur = a.step & 1;
+  if (tid < a.k) a.next_tokens[(int64_t)b * a.k + tid] = -1;
+  if (tid == 0) {
+    a.next_count[b] = 0;
+    a.ws.frontier_count[cur * a.B + b] = 0;
+  }
+}
+
+// The rows of sequence b, every chunk's partials stored by the scan launch:
+// row softmax statistics and top-k, children appended to the pool, next
+// frontier.  One block of kMergeWaves waves (one per SIMD: they start
+// together; a block of more waves per SIMD starts them in groups).
+// LPLM: partial lists per lane, at most; KST: keys staged per list (lists
+// are sorted, so the keys at or above the bound are a prefix of each).
+// With many short lists (64 per row) four keys per list almost always
+// hold every candidate; with 16 lists per row eight are needed.
+constexpr int kMergeWaves = 4;
+template <bool BF16, int LPLM, int KST>
+__device__ __forceinline__ void merge_sequence(const DraftArgs& a, int b) {
+  constexpr int kLPL = LPLM;
+  constexpr int kStage = KST;
   constexpr float kLog2e = 1.4426950408889634f;
+  constexpr int NW = kMergeWaves;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k = a.k, S = a.parts;  // partial lists per row
   const int prev = (a.step - 1) & 1, cur = a.step & 1;
@@ -291,142 +311,184 @@ __device__ __forceinline__ void merge_sequence(const DraftArgs& a, int b, int F)
   __shared__ uint64_t s_aux[256];                 // children's pool keys
   __shared__ uint64_t s_fb[kWaveCap];             // frontier candidates
   // ---- row merges: a segment of SP lanes per row ------------------------
-  // SP is the power of two >= S, so a wave merges 64 / SP rows at once and
-  // lane q of a segment holds chunk q's (max, sum) and the first kStage
-  // keys of its sorted list.  The row's max and sum of exp are segment
-  // reductions.  Bound: with at least k chunks the k-th largest chunk head
-  // bounds the row's k-th largest key from below, so only keys at or above
-  // it (a prefix of every chunk's list) are ranked.
+  // RW rows per wave (a power of two, NW * RW >= k, so one pass covers
+  // every row), SP = 64 / RW lanes per row; lane q of a segment holds
+  // lists q, q + SP, ... (LPL of them): each list's (max, sum) and its
+  // first kStage keys (lists are sorted).  The row's max and sum of exp
+  // are segment reductions.  Bound: with at least k lists the k-th largest
+  // list head bounds the row's k-th largest key from below, so only keys
+  // at or above it (a prefix of every list) are ranked.
+  // Every load below is issued before the frontier count F arrives: rows
+  // j < k of the workspace are always readable, rows j >= F are dropped.
   const int64_t e0 = (int64_t)b * k * S;  // first partial of the sequence
-  int SP = 1;
-  while (SP < S) SP <<= 1;
-  const int RW = 64 / SP;                 // rows per wave
+  int RW = 1;
+  while (NW * RW < k) RW <<= 1;
+  const int SP = 64 / RW;
+  const int LPL = (S + SP - 1) / SP;
   const int seg = lane / SP, q = lane - seg * SP;
   const uint64_t segmask = SP == 64 ? ~0ull : ((1ull << SP) - 1ull) << (seg * SP);
   const uint64_t below = segmask & ((1ull << lane) - 1ull);
   const int64_t pb = (int64_t)b * a.cap;
+  const int jr = wave * RW + seg;  // this lane's row
+  const int jl = min(jr, k - 1);   // row whose memory is loaded
+  const int64_t fs = ((int64_t)prev * a.B + b) * k + jl;
+  const int par0 = a.ws.frontier[fs];
+  const float vpar0 = a.ws.frontier_val[fs];
+  float pm[kLPL], ps[kLPL];
+  uint64_t pk[kLPL][kStage];
+#pragma unroll
+  for (int l = 0; l < kLPL; ++l) {
+    const int li = min(q + l * SP, S - 1);
+    const int64_t e = e0 + (int64_t)jl * S + li;
+    pm[l] = a.ws.part_m[e];
+    ps[l] = a.ws.part_s[e];
+#pragma unroll
+    for (int r = 0; r < kStage; ++r)
+      pk[l][r] = a.ws.part_keys[((int64_t)(b * k + jl) * kMaxTopk + min(r, k - 1)) * S + li];
+  }
   const int P0 = a.step == 1 ? 0 : a.ws.pool_count[b];
-  for (int r0 = 0; r0 < F; r0 += NW * RW) {
-    const int jr = r0 + wave * RW + seg;
-    const bool on = jr < F && q < S;
-    // the row's parent: its frontier slot's pool index and value, both
-    // stored by the previous step (no dependent load)
-    const int64_t fs = ((int64_t)prev * a.B + b) * k + jr;
-    const bool hp = a.step > 1 && jr < F;
-    const int par = hp ? a.ws.frontier[fs] : -1;
-    const float vpar = hp ? a.ws.frontier_val[fs] : 1.0f;
-    const int64_t e = e0 + (int64_t)jr * S + q;
-    const float pm = on ? a.ws.part_m[e] : -INFINITY;
-    const float ps = on ? a.ws.part_s[e] : 0.f;
-    uint64_t pk[kMaxTopk];
+  const int F = a.step == 1 ? 1 : a.ws.frontier_count[prev * a.B + b];
+  if (F == 0) {
+    empty_frontier(a, b);
+    return;
+  }
+  // phase: partials read
+  const bool on_row = jr < F;
 #pragma unroll
-    for (int r = 0; r < kMaxTopk; ++r)
-      pk[r] = (on && r < kStage && r < k) ? a.ws.part_keys[e * kMaxTopk + r] : 0;
-    // phase: partials read
-    float m = pm;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1)
-      if (d < SP) m = fmaxf(m, xor_lane_rt(m, d));
-    float sum = pm > -INFINITY ? ps * __builtin_amdgcn_exp2f((pm - m) * kLog2e) : 0.f;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1)
-      if (d < SP) sum += xor_lane_rt(sum, d);
-    // phase: row max and sum
-    // k-th largest head of the segment, bit by bit on the ordered logit
-    uint64_t Lk = 0;
-    if (S >= k) {
-      const uint32_t hk = on && pk[0] != 0 ? (uint32_t)(pk[0] >> 32) : 0u;
-      uint32_t t = 0;
-#pragma unroll
-      for (int bit = 31; bit >= (BF16 ? 16 : 0); --bit) {
-        const uint32_t cand = t | (1u << bit);
-        if (__popcll(__ballot(hk >= cand) & segmask) >= k) t = cand;
-      }
-      Lk = (uint64_t)t << 32;
+  for (int l = 0; l < kLPL; ++l) {
+    const bool on = on_row && l < LPL && q + l * SP < S;
+    if (!on) {
+      pm[l] = -INFINITY;
+      ps[l] = 0.f;
     }
-    // phase: row bound
-    int cq = 0;
 #pragma unroll
-    for (int r = 0; r < kStage; ++r) cq += (pk[r] != 0 && pk[r] >= Lk) ? 1 : 0;
-    if (__ballot(cq == kStage && k > kStage) != 0ull) {
-      // rare: a list qualifies beyond its staged keys
-      if (cq == kStage) {
+    for (int r = 0; r < kStage; ++r)
+      if (!on || r >= k) pk[l][r] = 0;
+  }
+  const int par = a.step > 1 ? par0 : -1;
+  const float vpar = a.step > 1 ? vpar0 : 1.0f;
+  float m = pm[0];
 #pragma unroll
-        for (int r = kStage; r < kMaxTopk; ++r)
-          if (r < k) pk[r] = a.ws.part_keys[e * kMaxTopk + r];
+  for (int l = 1; l < kLPL; ++l) m = fmaxf(m, pm[l]);
 #pragma unroll
-        for (int r = kStage; r < kMaxTopk; ++r)
-          cq += (r < k && pk[r] != 0 && pk[r] >= Lk) ? 1 : 0;
-      }
+  for (int d = 1; d < 64; d <<= 1)
+    if (d < SP) m = fmaxf(m, xor_lane_rt(m, d));
+  float sum = 0.f;
+#pragma unroll
+  for (int l = 0; l < kLPL; ++l)
+    sum += pm[l] > -INFINITY ? ps[l] * __builtin_amdgcn_exp2f((pm[l] - m) * kLog2e) : 0.f;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1)
+    if (d < SP) sum += xor_lane_rt(sum, d);
+  // phase: row max and sum
+  // k-th largest list head of the segment, bit by bit on the ordered logit
+  uint64_t Lk = 0;
+  if (S >= k) {
+    uint32_t hk[kLPL];
+#pragma unroll
+    for (int l = 0; l < kLPL; ++l) hk[l] = (uint32_t)(pk[l][0] >> 32);  // 0 for no key
+    uint32_t t = 0;
+#pragma unroll
+    for (int bit = 31; bit >= (BF16 ? 16 : 0); --bit) {
+      const uint32_t cand = t | (1u << bit);
+      int c = 0;
+#pragma unroll
+      for (int l = 0; l < kLPL; ++l) c += __popcll(__ballot(hk[l] >= cand) & segmask);
+      if (c >= k) t = cand;
     }
-    // segment prefix sum and total of cq (<= 16), one ballot per bit
-    int off = 0, n = 0;
+    Lk = (uint64_t)t << 32;
+  }
+  // phase: row bound
+  // keys at or above the bound: a prefix of each list; a list whose staged
+  // keys all qualify may hold more (then the row takes the exact path)
+  int cq = 0, cl[kLPL];
+  bool more = false;
 #pragma unroll
-    for (int bit = 0; bit < 5; ++bit) {
-      const uint64_t bm = __ballot((cq >> bit) & 1);
-      off += __popcll(bm & below) << bit;
-      n += __popcll(bm & segmask) << bit;
-    }
-    // phase: row prefix
-    const bool fits = n <= kRowCap;
-    if (jr < F) {
-      uint64_t* lst = &s_rc[jr * kRowCap];
-      if (fits) {
+  for (int l = 0; l < kLPL; ++l) {
+    cl[l] = 0;
 #pragma unroll
-        for (int r = 0; r < kMaxTopk; ++r)
-          if (r < cq) lst[off + r] = pk[r];
-      }
+    for (int r = 0; r < kStage; ++r) cl[l] += (pk[l][r] != 0 && pk[l][r] >= Lk) ? 1 : 0;
+    cq += cl[l];
+    more |= cl[l] == kStage && k > kStage;
+  }
+  // segment prefix sum and total of cq (<= kLPL * kStage), one ballot per bit
+  int off = 0, n = 0;
+#pragma unroll
+  for (int bit = 0; bit < 6; ++bit) {
+    const uint64_t bm = __ballot((cq >> bit) & 1);
+    off += __popcll(bm & below) << bit;
+    n += __popcll(bm & segmask) << bit;
+  }
+  const bool fits = n <= kRowCap && (__ballot(more) & segmask) == 0ull;
+  // phase: row prefix
+  if (on_row && fits) {
+    uint64_t* lst = &s_rc[jr * kRowCap + off];
+    int o = 0;
+#pragma unroll
+    for (int l = 0; l < kLPL; ++l) {
+#pragma unroll
+      for (int r = 0; r < kStage; ++r)
+        if (r < cl[l]) lst[o + r] = pk[l][r];
+      o += cl[l];
     }
-    wave_lds_fence();
-    // phase: row list written
-    if (jr < F && fits) {
-      const uint64_t* lst = &s_rc[jr * kRowCap];
-      for (int i = q; i < n; i += SP) {
-        const uint64_t me = lst[i];
-        int rank = 0;
+  }
+  wave_lds_fence();
+  // phase: row list written
+  if (on_row && fits) {
+    const uint64_t* lst = &s_rc[jr * kRowCap];
+    for (int i = q; i < n; i += SP) {
+      const uint64_t me = lst[i];
+      int rank = 0;
 #pragma unroll 8
-        for (int t = 0; t < n; ++t) rank += lst[t] > me;
-        if (rank < k) s_rk[jr * kMaxTopk + rank] = me;
-      }
+      for (int t = 0; t < n; ++t) rank += lst[t] > me;
+      if (rank < k) s_rk[jr * kMaxTopk + rank] = me;
     }
-    // phase: row ranked
-    // Many equal logits overflow a row's list: that row takes k rounds of
-    // maximum over all of its chunk lists, with the whole wave.
-    for (int sg = 0; sg < RW; ++sg) {
-      const int jo = r0 + wave * RW + sg;
-      if (jo >= F) break;
-      if ((__ballot(!fits) & (SP == 64 ? ~0ull : ((1ull << SP) - 1ull) << (sg * SP))) == 0ull)
-        continue;
-      uint64_t prevk = ~0ull;
-      for (int r = 0; r < k; ++r) {
-        uint64_t best = 0;
-        for (int t = lane; t < S * k; t += 64) {
-          const uint64_t v = a.ws.part_keys[(e0 + (int64_t)jo * S + t / k) * kMaxTopk + t % k];
-          if (v < prevk && v > best) best = v;
-        }
-        const uint64_t w = wave_max_u64(best);
-        if (lane == 0) s_rk[jo * kMaxTopk + r] = w;
-        prevk = w;
-      }
+  }
+  // phase: row ranked
+  // A row whose candidates do not fit the staged keys (many equal or
+  // clustered logits) takes k rounds of maximum over all of its lists'
+  // keys (at most 64 lists x 16 ranks: 16 per lane, loaded once), with
+  // the whole wave.
+  for (int sg = 0; sg < RW; ++sg) {
+    const int jo = wave * RW + sg;
+    if (jo >= F) break;
+    if ((__ballot(!fits) & (SP == 64 ? ~0ull : ((1ull << SP) - 1ull) << (sg * SP))) == 0ull)
+      continue;
+    const uint64_t* rk = &a.ws.part_keys[(int64_t)(b * k + jo) * kMaxTopk * S];  // [rank][list]
+    uint64_t v[kMaxTopk];
+#pragma unroll
+    for (int i = 0; i < kMaxTopk; ++i) {
+      const int t = lane + 64 * i;  // rank t / S of list t % S
+      v[i] = t < S * k ? rk[t] : 0;
     }
-    wave_lds_fence();
-    // phase: row merged
-    // Children of the row, in rank order (conf decreasing): child r of row
-    // jr is pool node P0 + jr * k + r.
-    if (jr < F) {
-      for (int r = q; r < k; r += SP) {
-        const uint64_t key = s_rk[jr * kMaxTopk + r];
-        const int tok = (int)id_of(key);
-        const float conf = __builtin_amdgcn_exp2f((logit_of(key) - m) * kLog2e) / sum;
-        const float val = __fmul_rn(vpar, conf);
-        const int ci = jr * k + r, pi = P0 + ci;
-        a.ws.pool_token[pb + pi] = tok;
-        a.ws.pool_parent[pb + pi] = par;
-        a.ws.pool_depth[pb + pi] = a.step;
-        a.ws.pool_conf[pb + pi] = conf;
-        a.ws.pool_value[pb + pi] = val;
-        s_aux[ci] = pool_key(val, a.step, tok, pi);
-      }
+    uint64_t prevk = ~0ull;
+    for (int r = 0; r < k; ++r) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int i = 0; i < kMaxTopk; ++i)
+        if (v[i] < prevk && v[i] > best) best = v[i];
+      const uint64_t w = wave_max_u64(best);
+      if (lane == 0) s_rk[jo * kMaxTopk + r] = w;
+      prevk = w;
+    }
+  }
+  wave_lds_fence();
+  // phase: row merged
+  // Children of the row, in rank order (conf decreasing): child r of row
+  // jr is pool node P0 + jr * k + r.
+  if (on_row) {
+    for (int r = q; r < k; r += SP) {
+      const uint64_t key = s_rk[jr * kMaxTopk + r];
+      const int tok = (int)id_of(key);
+      const float conf = __builtin_amdgcn_exp2f((logit_of(key) - m) * kLog2e) / sum;
+      const float val = __fmul_rn(vpar, conf);
+      const int ci = jr * k + r, pi = P0 + ci;
+      a.ws.pool_token[pb + pi] = tok;
+      a.ws.pool_parent[pb + pi] = par;
+      a.ws.pool_depth[pb + pi] = a.step;
+      a.ws.pool_conf[pb + pi] = conf;
+      a.ws.pool_value[pb + pi] = val;
+      s_aux[ci] = pool_key(val, a.step, tok, pi);
     }
   }
   const int n_new = F * k;  // <= 256 = NT
@@ -515,16 +577,6 @@ __device__ __forceinline__ void merge_sequence(const DraftArgs& a, int b, int F)
   // phase: frontier written
 }
 
-// A sequence whose tree stopped growing: no rows, empty next frontier.
-__device__ __forceinline__ void empty_frontier(const DraftArgs& a, int b) {
-  const int tid = threadIdx.x, cur = a.step & 1;
-  if (tid < a.k) a.next_tokens[(int64_t)b * a.k + tid] = -1;
-  if (tid == 0) {
-    a.next_count[b] = 0;
-    a.ws.frontier_count[cur * a.B + b] = 0;
-  }
-}
-
 // Scan launch: block (x, j, b) streams chunks [x * cpb, x * cpb + cpb) of
 // row j of sequence b and exits.  The first chunk's loads are issued
 // before the frontier count arrives (every row j < topk is readable memory
@@ -547,19 +599,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? 3 : 1
   scan_chunks<BF16, VEC, E, WAVE>(a, row, j, b, c0, min(a.cpb, a.S - c0), x, raw);
 }
 
-// Merge launch: one block per sequence merges its rows, with 16 waves so
-// that every row (up to 16, one wave each when a row has 64 lists) is
-// merged in one pass.
-constexpr int kMergeWaves = 16;
-template <bool BF16>
+// Merge launch: one block per sequence.
+template <bool BF16, int LPLM, int KST>
 __global__ __launch_bounds__(kMergeWaves * 64) void draft_merge_kernel(DraftArgs a) {
-  const int b = blockIdx.x;
-  const int F = a.step == 1 ? 1 : a.ws.frontier_count[((a.step - 1) & 1) * a.B + b];
-  if (F == 0) {
-    empty_frontier(a, b);
-    return;
-  }
-  merge_sequence<BF16, kMergeWaves>(a, b, F);
+  merge_sequence<BF16, LPLM, KST>(a, blockIdx.x);
 }
 
 hipError_t launch_draft_step(const Plan& p, const DraftWs& w, int step,
@@ -598,8 +641,15 @@ hipError_t launch_draft_step(const Plan& p, const DraftWs& w, int step,
   if (wv) ET_SCAN(true);
   else ET_SCAN(false);
 #undef ET_SCAN
-  if (bf) draft_merge_kernel<true><<<p.B, kMergeWaves * 64, 0, s>>>(a);
-  else draft_merge_kernel<false><<<p.B, kMergeWaves * 64, 0, s>>>(a);
+  // lists per lane of the merge: rows per wave RW (NW * RW >= k), 64 / RW
+  // lanes per row
+  int RW = 1;
+  while (kMergeWaves * RW < p.k) RW <<= 1;
+  const bool many = a.parts > 64 / RW;
+  if (bf && many) draft_merge_kernel<true, 4, 4><<<p.B, kMergeWaves * 64, 0, s>>>(a);
+  else if (bf) draft_merge_kernel<true, 1, 8><<<p.B, kMergeWaves * 64, 0, s>>>(a);
+  else if (many) draft_merge_kernel<false, 4, 4><<<p.B, kMergeWaves * 64, 0, s>>>(a);
+  else draft_merge_kernel<false, 1, 8><<<p.B, kMergeWaves * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 

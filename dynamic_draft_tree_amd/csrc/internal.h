@@ -65,9 +65,9 @@ struct DraftWs {
   int32_t* frontier;      // [2][B][k]
   float* frontier_val;    // [2][B][k] value of each frontier node
   int32_t* frontier_count;// [2][B]
-  float* part_m;          // [B][k][S][waves]
-  float* part_s;          // [B][k][S][waves]
-  uint64_t* part_keys;    // [B][k][S][waves][kMaxTopk]
+  float* part_m;          // [B][k][lists] (lists = S, or S * waves)
+  float* part_s;          // [B][k][lists]
+  uint64_t* part_keys;    // [B][k][kMaxTopk][lists]: rank r of every list, contiguous
 };
 
 struct AcceptWs {
