@@ -7,9 +7,10 @@ Llama-3.1-8B shape at batch 1 (vocab 128256, top-k 10, depth 8, N 60,
 GQA 32/8 x 128, prefix 4096, bf16).  Input sets rotate so the working set
 exceeds the 256 MB MALL and every cycle reads HBM.
 
-Prints one JSON line: cycles/s, the roofline of the dominant kernel
+Prints one JSON line: cycles/s, the roofline of the dominant call
 (algorithmic bytes / its average duration, HIP events on the launch
-stream) and the CPU oracle timed on this host as a reported baseline.
+stream; a call is one or two back-to-back launches) and the CPU oracle
+timed on this host as a reported baseline.
 """
 from __future__ import annotations
 
@@ -29,37 +30,42 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 MALL_BYTES = 256 << 20
 
 
-KERNEL_SOURCES = {  # files whose change invalidates a kernel's counters
-    "draft_step_kernel": ["draft.hip", "device.h", "internal.h"],
-    "accept_kernel": ["accept.hip", "device.h", "internal.h"],
-    "tree_attn_bf16_kernel": ["attention.hip", "device.h", "internal.h"],
+# Each measured call, the kernels one call launches (one dispatch each) and
+# the files whose change invalidates its counters.
+CALLS = {
+    "draft_step": (["draft_scan_kernel", "draft_merge_kernel"],
+                   ["draft.hip", "device.h", "internal.h"]),
+    "accept": (["accept_scan_kernel", "accept_walk_kernel"],
+               ["accept.hip", "device.h", "internal.h"]),
+    "tree_attention": (["tree_attn_bf16_kernel", "tree_attn_merge_kernel"],
+                       ["attention.hip", "device.h", "internal.h"]),
 }
 
 
-def source_digest(kernel):
+def source_digest(call):
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES.get(kernel, []):
+    for f in CALLS[call][1]:
         with open(os.path.join(ROOT, "dynamic_draft_tree_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_path(kernel, workload):
-    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+def traffic_path(call, workload):
+    return os.path.join(ROOT, "profiles", f"{call}_{workload}_traffic.json")
 
 
-def measured_traffic(kernel, workload):
-    """HBM bytes per launch from the committed counter summary, or None when
-    there is none or the kernel's sources changed since it was taken."""
-    p = traffic_path(kernel, workload)
+def measured_traffic(call, workload):
+    """HBM bytes per call from the committed counter summary, or None when
+    there is none or the call's sources changed since it was taken."""
+    p = traffic_path(call, workload)
     if not os.path.exists(p):
         return None
     with open(p) as fh:
         t = json.load(fh)
-    if t.get("source_digest") != source_digest(kernel):
+    if t.get("source_digest") != source_digest(call):
         return None
-    return t["traffic_bytes_per_launch"]
+    return t["traffic_bytes_per_call"]
 
 
 def pmc_rows(d):
@@ -75,14 +81,16 @@ def pmc_rows(d):
 
 
 def summarize_pmc(args):
-    """Write profiles/<kernel>_<workload>_traffic.json from four --pmc runs:
-    FETCH_SIZE and WRITE_SIZE of the bench and of the copy calibration."""
+    """Write profiles/<call>_<workload>_traffic.json from four --pmc runs:
+    FETCH_SIZE and WRITE_SIZE of the bench and of the copy calibration.
+    A call's traffic is the sum over its kernels of the mean per dispatch."""
     fetch, write, cfetch, cwrite = args.summarize_pmc
     copy_bytes = args.copy_mb * (1 << 20)
+    call = args.summarize_call
 
     def per_dispatch(d, name_part, counter):
-        """Mean over the dispatches (the bench kernel's launches differ in
-        size, as its algorithmic bytes do)."""
+        """Mean over the dispatches (a call's launches differ in size, as
+        its algorithmic bytes do)."""
         v = [x for k, c, x in pmc_rows(d) if name_part in k and c == counter]
         if not v:
             raise SystemExit(f"no {counter} rows for {name_part} under {d}")
@@ -93,21 +101,23 @@ def summarize_pmc(args):
     cw, _ = per_dispatch(cwrite, "neg_kernel", "WRITE_SIZE")
     f_fetch = copy_bytes / cf
     f_write = copy_bytes / cw
-    kf, nf = per_dispatch(fetch, args.summarize_kernel, "FETCH_SIZE")
-    kw, nw = per_dispatch(write, args.summarize_kernel, "WRITE_SIZE")
+    kernels = {}
+    for kn in CALLS[call][0]:
+        kf, nf = per_dispatch(fetch, kn, "FETCH_SIZE")
+        kw, nw = per_dispatch(write, kn, "WRITE_SIZE")
+        kernels[kn] = {"fetch_size_kib_mean": kf, "write_size_kib_mean": kw,
+                       "dispatches": [nf, nw],
+                       "fetch_bytes": kf * f_fetch, "write_bytes": kw * f_write}
     out = {
-        "kernel": args.summarize_kernel, "workload": args.workload,
-        "fetch_size_kib_mean": kf, "write_size_kib_mean": kw,
-        "dispatches": [nf, nw],
+        "call": call, "workload": args.workload, "kernels": kernels,
         "copy_calibration": {"bytes": copy_bytes, "fetch_kib": cf, "write_kib": cw,
                              "fetch_bytes_per_unit": f_fetch,
                              "write_bytes_per_unit": f_write},
-        "fetch_bytes_per_launch": kf * f_fetch,
-        "write_bytes_per_launch": kw * f_write,
-        "traffic_bytes_per_launch": round(kf * f_fetch + kw * f_write),
-        "source_digest": source_digest(args.summarize_kernel),
+        "traffic_bytes_per_call": round(sum(k["fetch_bytes"] + k["write_bytes"]
+                                            for k in kernels.values())),
+        "source_digest": source_digest(call),
     }
-    with open(traffic_path(args.summarize_kernel, args.workload), "w") as fh:
+    with open(traffic_path(call, args.workload), "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out))
 
@@ -143,7 +153,7 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=4, metavar="DIR",
                     help="write the traffic summary from the FETCH_SIZE and "
                          "WRITE_SIZE runs of the bench and of the copy")
-    ap.add_argument("--summarize-kernel", default="draft_step_kernel")
+    ap.add_argument("--summarize-call", default="draft_step", choices=sorted(CALLS))
     return ap.parse_args()
 
 
@@ -332,26 +342,24 @@ def main():
     # later step reads k rows per sequence
     fr = [w.batch] + [w.batch * w.topk] * (w.depth - 1)
     alg = algorithmic(w, n_kept, fr)
+    # The dominant call (the draft step at the default workload) is the
+    # unit of the roofline: its launches (a vocab scan and a small merge)
+    # run back to back and the events time them together.
     dominant = max(names, key=lambda n: per_cycle_us[n])
-    if dominant == "draft":
-        bytes_per_launch = float(np.mean(alg["draft"]))
-        kernel = "draft_step_kernel"
-    elif dominant == "accept":
-        bytes_per_launch = alg["accept"]
-        kernel = "accept_kernel"
-    elif dominant == "attention":
-        bytes_per_launch = alg["attention"]
-        kernel = "tree_attn_bf16_kernel" if w.qkv_dtype == "bf16" else "tree_attn_f32_kernel"
-    else:
-        bytes_per_launch = 0.0
-        kernel = dominant
-    achieved = bytes_per_launch / (avg_us[dominant] * 1e-6) / 1e9
+    call = {"draft": "draft_step", "accept": "accept",
+            "attention": "tree_attention"}.get(dominant)
+    bytes_per_call = {"draft": float(np.mean(alg["draft"])),
+                      "accept": alg["accept"],
+                      "attention": alg["attention"]}.get(dominant, 0.0)
+    achieved = bytes_per_call / (avg_us[dominant] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(kernel, w.name),
-                "kernel": kernel, "avg_us": round(avg_us[dominant], 3),
-                "bytes_per_launch": bytes_per_launch}
+                "traffic": measured_traffic(call, w.name) if call else None,
+                "call": call or dominant,
+                "kernels": CALLS[call][0] if call else [],
+                "avg_us": round(avg_us[dominant], 3),
+                "bytes_per_call": bytes_per_call}
 
     # ---- CPU oracle baseline ---------------------------------------------
     cpu = None
