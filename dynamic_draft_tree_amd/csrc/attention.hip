@@ -141,14 +141,18 @@ __device__ __forceinline__ void barrier_no_fence() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int HD, int WR>
-__global__ __launch_bounds__(512, 1) void tree_attn_bf16_kernel(AttnArgs a) {
+// NB LDS tile buffers, prefetch distance NB - 1.  NB = 2 halves the LDS
+// so that two blocks share a compute unit (four waves per SIMD, which hide
+// each other's LDS and matrix latencies) when the registers allow it.
+template <int HD, int WR, int NB>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NB == 2 ? 4 : 2)))
+void tree_attn_bf16_kernel(AttnArgs a) {
   constexpr int KSTEPS = HD / 32;  // 32-wide d steps of K . Q^T
   constexpr int DT = HD / 16;      // 16-wide d tiles of O
   constexpr int TE = kAttnTile * HD;  // elements of one K (or V) tile
   constexpr int CPR = HD / 8;      // 16-byte chunks per key row
   constexpr int CH = kAttnTile * CPR / 64 / 8;  // 1 KB slabs per wave per tile
-  constexpr int NB = 3;            // LDS tile buffers: prefetch distance 2
+  constexpr int PD = NB - 1;       // prefetch distance
   constexpr int BR = 64 * WR;      // query rows per block
   __shared__ __attribute__((aligned(16))) uint16_t sKV[NB][2][TE];
   __shared__ uint64_t sMask[4][BR];  // [tree tile][row of the block]
@@ -262,9 +266,9 @@ __global__ __launch_bounds__(512, 1) void tree_attn_bf16_kernel(AttnArgs a) {
   } while (0)
 
   if (cnt > 0) ET_ISSUE_TILE(t_begin, 0);
-  if (cnt > 1) ET_ISSUE_TILE(t_begin + 1, 1);
+  if (PD > 1 && cnt > 1) ET_ISSUE_TILE(t_begin + 1, 1);
   // Q, the mask word and tile 0 have landed; tile 1 may still be in flight
-  if (cnt > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * CH));
+  if (PD > 1 && cnt > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * CH));
   else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   if (tid < 4 * BR) {
     const int rr = me % BR, q = me / BR;
@@ -275,8 +279,8 @@ __global__ __launch_bounds__(512, 1) void tree_attn_bf16_kernel(AttnArgs a) {
   const int sw = r16 & (CPR - 1);  // swizzle of the K rows this lane reads
   for (int it = 0; it < cnt; ++it) {
     const int cur = it % NB;
-    // buffer (it+2) % NB was last read in iteration it-1, before its barrier
-    if (it + 2 < cnt) ET_ISSUE_TILE(t_begin + it + 2, (it + 2) % NB);
+    // buffer (it+PD) % NB was last read in iteration it-1, before its barrier
+    if (it + PD < cnt) ET_ISSUE_TILE(t_begin + it + PD, (it + PD) % NB);
 
     const int t = t_begin + it;
     const bool tree = t >= tp;
@@ -386,7 +390,7 @@ __global__ __launch_bounds__(512, 1) void tree_attn_bf16_kernel(AttnArgs a) {
     for (int w = 0; w < WR; ++w)
       lacc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[w], lacc[w], 0, 0, 0);
     // tile it+1 must have landed before the barrier; tile it+2 may fly on
-    if (it + 2 < cnt) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * CH));
+    if (PD > 1 && it + 2 < cnt) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * CH));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     barrier_no_fence();
   }
@@ -596,6 +600,12 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnArgs a, int HD) 
   if (tid < HD) out[tid] = o / l_run;
 }
 
+// 64-row blocks fit two per compute unit with two tile buffers (127
+// registers, 66 KB of LDS); 128-row blocks need more registers than four
+// waves per SIMD allow, so they keep three buffers and one block per CU.
+#ifndef ET_ATTN_NB
+#define ET_ATTN_NB(WR) ((WR) == 1 ? 2 : 3)
+#endif
 hipError_t launch_tree_attention(const Plan& p, const AttnWs& w,
                                  const void* q, const void* kc,
                                  const void* vc, const void* kt,
@@ -634,7 +644,7 @@ hipError_t launch_tree_attention(const Plan& p, const AttnWs& w,
   const int blocks = units8 * p.attn_nqb * p.attn_splits;
 #define ET_ATTN(HD, WR)                                                          \
   do {                                                                           \
-    tree_attn_bf16_kernel<HD, WR><<<blocks, 512, 0, s>>>(a);                     \
+    tree_attn_bf16_kernel<HD, WR, ET_ATTN_NB(WR)><<<blocks, 512, 0, s>>>(a);     \
     hipError_t e = hipGetLastError();                                            \
     if (e != hipSuccess || p.attn_splits == 1) return e;                         \
     tree_attn_merge_kernel<HD, WR>                                               \
