@@ -109,6 +109,26 @@ __device__ __forceinline__ void lds_wait_all(u32x2_t (&x)[4], u32x2_t (&y)[4]) {
                  "+v"(y[1]), "+v"(y[2]), "+v"(y[3]));
 }
 
+// ds_read_b128 at an LDS byte address plus an immediate offset (assembly,
+// like the transpose reads, so the compiler does not hold it behind the
+// direct loads still filling another buffer).
+template <int OFF>
+__device__ __forceinline__ bf16x8_t ds_read_b128_at(uint32_t addr) {
+  bf16x8_t v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
+// s_waitcnt lgkmcnt(0) that the compiler sees as producing the K fragments.
+__device__ __forceinline__ void lds_wait_k(bf16x8_t (&x)[4][2]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[1][0]), "+v"(x[1][1]),
+                 "+v"(x[2][0]), "+v"(x[2][1]), "+v"(x[3][0]), "+v"(x[3][1]));
+}
+__device__ __forceinline__ void lds_wait_k(bf16x8_t (&x)[2][2]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[1][0]), "+v"(x[1][1]));
+}
+
 // 16 bytes per lane from global memory straight into a 1 KB LDS slab
 // (lane i writes bytes 16i..16i+15; `slab` must be wave-uniform).  A plain
 // device function, so that kernel templates calling it still instantiate
@@ -289,24 +309,55 @@ void tree_attn_bf16_kernel(AttnArgs a) {
     const uint16_t* Vs = sKV[cur][1];
 
     // S^T = K . Q^T over this wave's 32 keys: lane holds row r16 and keys
-    // kh*32 + s2*16 + 4g + e.  kk outermost for independent accumulators.
+    // kh*32 + s2*16 + 4g + e.  Every K fragment of the tile is read before
+    // one wait, then the matrix instructions run back to back, kk outermost
+    // for independent accumulators.
     f32x4_t sacc[WR][2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int w = 0; w < WR; ++w) sacc[w][s2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    {
+      bf16x8_t af[KSTEPS][2];
+      const uint32_t kb = lds_addr(Ks) + (kh * 32 + r16) * (HD * 2);
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      bf16x8_t af[2];
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        const uint32_t ka = kb + (((kk * 4 + g) ^ sw) * 16);
+        af[kk][0] = ds_read_b128_at<0>(ka);
+        af[kk][1] = ds_read_b128_at<16 * HD * 2>(ka);  // 16 key rows below
+      }
+      lds_wait_k(af);
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-        af[s2] = *(const bf16x8_t*)&Ks[(kh * 32 + s2 * 16 + r16) * HD + (((kk * 4 + g) ^ sw) * 8)];
+      for (int kk = 0; kk < KSTEPS; ++kk)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
+        for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int w = 0; w < WR; ++w)
-          sacc[w][s2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s2], qf[w][kk], sacc[w][s2], 0, 0, 0);
+          for (int w = 0; w < WR; ++w)
+            sacc[w][s2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kk][s2], qf[w][kk], sacc[w][s2], 0, 0, 0);
     }
+
+    // V^T by transpose reads, issued from inline assembly: the compiler
+    // cannot tell them apart from the direct loads still filling another
+    // buffer, and would otherwise wait for those loads (vmcnt(0)) before
+    // each read.  The wait for them (lgkmcnt(0)) ties their registers, so
+    // no use can be scheduled before it.  With three buffers (128-row
+    // blocks, registers to spare) they are issued before the softmax, whose
+    // vector work then hides their latency; 64-row blocks issue them after
+    // it, keeping four waves per SIMD within the register budget.
+    u32x2_t vlo[DT], vhi[DT];
+    const int vrow = kh * 32 + g * 4 + (r16 >> 2);
+    const uint32_t vbase = lds_addr(Vs + vrow * HD) + (r16 & 1) * 8;
+    const int vsw = vrow & (CPR - 1);
+    auto issue_v = [&]() {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        // this lane's source word: key row vrow (+16), d = dt*16 + 4*(r16%4)
+        const uint32_t va = vbase + (((dt * 2 + ((r16 >> 1) & 1)) ^ vsw) * 16);
+        vlo[dt] = ds_read_tr16(va);
+        vhi[dt] = HD == 128 ? ds_read_tr16_off4k(va) : ds_read_tr16_off2k(va);
+      }
+    };
+    if constexpr (NB == 3) issue_v();
 
     // Softmax in base 2 on unscaled scores: p = 2^(s*c - m).  The running
     // max m is raised only when some row's tile max exceeds it by more
@@ -356,35 +407,18 @@ void tree_attn_bf16_kernel(AttnArgs a) {
           pf[w][s2 * 4 + e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sv[s2][e], c, -mu));
     }
 
-    // O^T += V^T . P^T over the wave's 32 keys; V^T by transpose reads.
-    // The reads are issued from inline assembly: the compiler cannot tell
-    // them apart from the direct loads still filling another buffer, and
-    // would otherwise wait for those loads (vmcnt(0)) before each read.
-    // The block waits for its own reads (lgkmcnt(0)) through in/out operands,
-    // so no use of the values can be scheduled before that wait.
-    {
-      u32x2_t vlo[DT], vhi[DT];
-      const int vrow = kh * 32 + g * 4 + (r16 >> 2);
-      const uint32_t vbase = lds_addr(Vs + vrow * HD) + (r16 & 1) * 8;
-      const int vsw = vrow & (CPR - 1);
+    if constexpr (NB != 3) issue_v();
+    // O^T += V^T . P^T over the wave's 32 keys.
+    lds_wait_all(vlo, vhi);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        // this lane's source word: key row vrow (+16), d = dt*16 + 4*(r16%4)
-        const uint32_t va = vbase + (((dt * 2 + ((r16 >> 1) & 1)) ^ vsw) * 16);
-        vlo[dt] = ds_read_tr16(va);
-        vhi[dt] = HD == 128 ? ds_read_tr16_off4k(va) : ds_read_tr16_off2k(va);
-      }
-      lds_wait_all(vlo, vhi);
+    for (int dt = 0; dt < DT; ++dt) {
+      bf16x8_t af;
+      u32x2_t* afh = (u32x2_t*)&af;
+      afh[0] = vlo[dt];
+      afh[1] = vhi[dt];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        bf16x8_t af;
-        u32x2_t* afh = (u32x2_t*)&af;
-        afh[0] = vlo[dt];
-        afh[1] = vhi[dt];
-#pragma unroll
-        for (int w = 0; w < WR; ++w)
-          oacc[w][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf[w], oacc[w][dt], 0, 0, 0);
-      }
+      for (int w = 0; w < WR; ++w)
+        oacc[w][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf[w], oacc[w][dt], 0, 0, 0);
     }
 #pragma unroll
     for (int w = 0; w < WR; ++w)
