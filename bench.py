@@ -157,17 +157,20 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic(w, n_kept, frontier_rows):
+def algorithmic(w, n_kept, frontier_rows, prefix_len):
     """Bytes (and flops) each call must move, per launch, from the shapes:
-    logits rows read once, K/V read once, Q/O/tree K/V once."""
+    logits rows read once; K/V of every prefix and kept tree position read
+    once; q and out of every kept slot once; q.k and p.v over the prefix
+    for every kept slot and head (the few tree keys are left out)."""
     esz = 2 if w.logits_dtype == "bf16" else 4
     qsz = 2 if w.qkv_dtype == "bf16" else 4
-    draft = [rows * w.vocab * esz for rows in frontier_rows]
-    accept = float(np.sum(n_kept + 1)) * w.vocab * esz
-    P = w.prefix_range[0]  # fixed-prefix workloads
-    kv = w.batch * w.n_kv_heads * (P + w.T) * w.head_dim * 2 * qsz
-    qo = 2 * w.batch * w.T * w.n_q_heads * w.head_dim * qsz
-    flops = 4.0 * w.batch * w.n_q_heads * w.T * P * w.head_dim
+    rows = n_kept.astype(np.float64) + 1.0   # kept slots incl. the root
+    P = prefix_len.astype(np.float64)
+    draft = [r * w.vocab * esz for r in frontier_rows]
+    accept = float(np.sum(rows)) * w.vocab * esz
+    kv = float(np.sum(w.n_kv_heads * (P + rows) * w.head_dim * 2 * qsz))
+    qo = float(np.sum(2 * rows * w.n_q_heads * w.head_dim * qsz))
+    flops = float(np.sum(4.0 * w.n_q_heads * rows * P * w.head_dim))
     return dict(draft=draft, accept=accept, attention=kv + qo,
                 attention_flops=flops)
 
@@ -341,7 +344,7 @@ def main():
     # frontier rows per step: 1 at step 1; with the threshold off every
     # later step reads k rows per sequence
     fr = [w.batch] + [w.batch * w.topk] * (w.depth - 1)
-    alg = algorithmic(w, n_kept, fr)
+    alg = algorithmic(w, n_kept, fr, host0["prefix"])
     # The dominant call (the draft step at the default workload) is the
     # unit of the roofline: its launches (a vocab scan and a small merge)
     # run back to back and the events time them together.
@@ -360,6 +363,16 @@ def main():
                 "kernels": CALLS[call][0] if call else [],
                 "avg_us": round(avg_us[dominant], 3),
                 "bytes_per_call": bytes_per_call}
+    if dominant == "attention" and w.qkv_dtype == "bf16":
+        # above the ridge (flops per byte > peak flops / peak bytes) the
+        # matrix cores, not HBM, bound the call
+        flops = alg["attention_flops"]
+        if flops / bytes_per_call > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+            tf = flops / (avg_us[dominant] * 1e-6) / 1e12
+            roofline.update({"bound": "mfma", "achieved": round(tf, 1),
+                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "flops_per_call": flops})
 
     # ---- CPU oracle baseline ---------------------------------------------
     cpu = None
