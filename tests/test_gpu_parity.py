@@ -71,6 +71,13 @@ VARIANTS = {
                             sharpness=(2.5, 0.8), n_q_heads=4, n_kv_heads=1,
                             head_dim=128, prefix_cap=128,
                             prefix_range=(64, 128), qkv_dtype="bf16", seed=13),
+    # more than 6000 one-chunk scan blocks: two chunks per block, fp32
+    # logits with per-block partials (the scan loop's barrier path)
+    "f32_multi_chunk": TINY.with_(batch=16, vocab=100000, topk=16, depth=2,
+                                  budget_n=16, threshold=0.0,
+                                  sharpness=tuple([2.5, 0.8] * 8),
+                                  n_q_heads=2, n_kv_heads=1, head_dim=64,
+                                  prefix_cap=64, prefix_range=(1, 64), seed=14),
     "f32_gqa": TINY.with_(batch=2, vocab=1500, topk=3, depth=4, budget_n=10,
                           threshold=0.0, sharpness=(2.0, 1.0), n_q_heads=4,
                           n_kv_heads=2, head_dim=128, prefix_cap=100,
@@ -300,6 +307,33 @@ def test_unaligned_rows_take_scalar_path():
     for step in range(1, w.depth + 1):
         plan_a.draft_step(step, dev["root_tokens"], dev["draft"][:, step - 1])
         plan_b.draft_step(step, dev["root_tokens"], padded[:, step - 1, :, :V])
+    plan_a.rerank()
+    plan_b.rerank()
+    torch.cuda.synchronize()
+    assert torch.equal(plan_a.tokens, plan_b.tokens)
+    assert torch.equal(plan_a.parent_slot, plan_b.parent_slot)
+    assert torch.equal(plan_a.value, plan_b.value)
+
+
+def test_unaligned_rows_multi_chunk_scan():
+    """Rows not 16-byte aligned at batch 64 (two chunks per scan block, the
+    element-wise loads of the next chunk issued in the loop) give the same
+    tree as the aligned rows."""
+    d = _lib()
+    w = WORKLOADS["llama8b_b64"].with_(depth=3)
+    inp = make_inputs(w)
+    dev = dev_inputs(inp)
+    plan_a = d.Plan(w)
+    plan_b = d.Plan(w)
+    V = w.vocab
+    padded = torch.zeros((w.batch, w.depth, w.topk, V + 1), dtype=torch.bfloat16,
+                         device="cuda")
+    padded[..., :V] = dev["draft"]
+    for step in range(1, w.depth + 1):
+        plan_a.draft_step(step, dev["root_tokens"], dev["draft"][:, step - 1])
+        plan_b.draft_step(step, dev["root_tokens"], padded[:, step - 1, :, :V])
+        torch.cuda.synchronize()
+        assert torch.equal(plan_a.next_tokens, plan_b.next_tokens), step
     plan_a.rerank()
     plan_b.rerank()
     torch.cuda.synchronize()
