@@ -337,6 +337,33 @@ def main():
                 cnt[n] += w.depth if n == "draft" else 1
         done += nb
     avg_us = {n: acc[n] / cnt[n] for n in names}
+
+    # ---- the step after the cycle (not part of the metric): KV commit ----
+    # The last cycle's accepted paths are appended to copies of input set
+    # 0's caches, with the prefix lengths lowered to leave room (the
+    # workloads fill their caches); each call is timed on its own, the
+    # prefix lengths restored before it, the GPU held as above.
+    ds0 = sets[0]
+    kc = ds0["attn"]["k_cache"].clone()
+    vc = ds0["attn"]["v_cache"].clone()
+    plen0 = torch.clamp(ds0["prefix"], max=w.prefix_cap - w.depth - 1)
+    plen = plen0.clone()
+    commit_us = []
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(hold_ms * spin_per_ms))
+    ev = []
+    for _ in range(20):
+        plen.copy_(plen0)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        plan.kv_commit(kc, vc, ds0["attn"]["k_tree"], ds0["attn"]["v_tree"], plen,
+                       stream)
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    commit_us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+    del kc, vc
     per_cycle_us = {n: acc[n] / K for n in names}
 
     # algorithmic bytes of the last cycle's shapes
@@ -417,6 +444,7 @@ def main():
         "roofline": roofline,
         "per_call_us": {n: round(avg_us[n], 3) for n in names},
         "per_cycle_us": {n: round(per_cycle_us[n], 3) for n in names},
+        "next_calls_us": {"kv_commit": round(commit_us, 3)},
         "cpu_baseline": cpu,
         "gen_seconds": round(gen_s, 1),
     }

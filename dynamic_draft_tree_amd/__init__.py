@@ -5,7 +5,8 @@ this package holds its HIP sources (csrc/), the build step and a thin
 ctypes binding that passes torch device pointers and streams through.
 """
 from .binding import (EXPORTS, EtError, Plan, et_accept, et_config,  # noqa: F401
-                      et_draft_step, et_plan_create, et_plan_destroy,
+                      et_draft_step, et_kv_commit, et_plan_create,
+                      et_plan_destroy,
                       et_pool_capacity, et_pool_export, et_rerank,
                       et_tree_attention, et_tree_mask, et_workspace_bytes,
                       et_workspace_init, lib, make_config)

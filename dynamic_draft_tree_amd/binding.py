@@ -23,7 +23,7 @@ _STATUS = {ET_EINVAL: "ET_EINVAL", ET_EUNSUPPORTED: "ET_EUNSUPPORTED",
 EXPORTS = ("et_plan_create", "et_plan_destroy", "et_workspace_bytes",
            "et_pool_capacity", "et_workspace_init", "et_draft_step",
            "et_rerank", "et_tree_mask", "et_tree_attention", "et_accept",
-           "et_pool_export", "et_last_error")
+           "et_kv_commit", "et_pool_export", "et_last_error")
 
 
 class et_config(ctypes.Structure):
@@ -69,6 +69,7 @@ def lib():
             "et_tree_attention": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp],
                                   ctypes.c_int),
             "et_accept": ([vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+            "et_kv_commit": ([vp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "et_pool_export": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "et_last_error": ([], ctypes.c_char_p),
         }
@@ -183,6 +184,16 @@ def et_accept(plan, ws, target_logits, tokens, parent_slot, n_kept,
                            _ptr(out_tokens), _stream(stream)))
 
 
+def et_kv_commit(plan, k_cache, v_cache, k_tree, v_tree, prefix_len,
+                 path_slots, accept_len, stream=None):
+    for t in (k_cache, v_cache, k_tree, v_tree):
+        if not t.is_contiguous():
+            raise ValueError("K/V tensors must be contiguous")
+    _check(lib().et_kv_commit(plan, _ptr(k_cache), _ptr(v_cache), _ptr(k_tree),
+                              _ptr(v_tree), _ptr(prefix_len), _ptr(path_slots),
+                              _ptr(accept_len), _stream(stream)))
+
+
 def et_pool_export(plan, ws, token=None, parent=None, depth=None, conf=None,
                    value=None, pool_count=None, frontier=None,
                    frontier_count=None, stream=None):
@@ -256,6 +267,12 @@ class Plan:
         et_accept(self.handle, self.ws, target_logits, self.tokens,
                   self.parent_slot, self.n_kept, self.accept_len,
                   self.path_slots, self.out_tokens, stream)
+
+    def kv_commit(self, k_cache, v_cache, k_tree, v_tree, prefix_len,
+                  stream=None):
+        """Append the last accept's path to the cache; advances prefix_len."""
+        et_kv_commit(self.handle, k_cache, v_cache, k_tree, v_tree, prefix_len,
+                     self.path_slots, self.accept_len, stream)
 
     def cycle(self, root_tokens, draft, prefix_len, attn, target,
               stream=None):

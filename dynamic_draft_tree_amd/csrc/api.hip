@@ -396,6 +396,29 @@ int et_accept(et_plan_t plan, void* ws, const void* target_logits,
       fn);
 }
 
+int et_kv_commit(et_plan_t plan, void* k_cache, void* v_cache,
+                 const void* k_tree, const void* v_tree, int32_t* prefix_len,
+                 const int32_t* path_slots, const int32_t* accept_len,
+                 et_stream_t stream) {
+  const char* fn = "et_kv_commit";
+  CHECK_PTR(plan);
+  CHECK_PTR(k_cache);
+  CHECK_PTR(v_cache);
+  CHECK_PTR(k_tree);
+  CHECK_PTR(v_tree);
+  CHECK_PTR(prefix_len);
+  CHECK_PTR(path_slots);
+  CHECK_PTR(accept_len);
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_tree) ||
+      !aligned16(v_tree))
+    return fail(ET_EINVAL, "%s: K/V buffers must be 16-byte aligned", fn);
+  et::Plan& p = *as_plan(plan);
+  return hip_status(
+      et::launch_kv_commit(p, k_cache, v_cache, k_tree, v_tree, prefix_len,
+                           path_slots, accept_len, (hipStream_t)stream),
+      fn);
+}
+
 int et_pool_export(et_plan_t plan, const void* ws, int32_t* token,
                    int32_t* parent, int32_t* depth, float* conf, float* value,
                    int32_t* pool_count, int32_t* frontier,

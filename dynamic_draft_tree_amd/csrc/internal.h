@@ -128,6 +128,10 @@ hipError_t launch_accept(const Plan& p, const AcceptWs& w, const void* target,
                          const int32_t* n_kept, int32_t* accept_len,
                          int32_t* path_slots, int32_t* out_tokens,
                          hipStream_t s);
+hipError_t launch_kv_commit(const Plan& p, void* k_cache, void* v_cache,
+                            const void* k_tree, const void* v_tree,
+                            int32_t* prefix_len, const int32_t* path_slots,
+                            const int32_t* accept_len, hipStream_t s);
 hipError_t launch_pool_export(const Plan& p, const DraftWs& w, int32_t* token,
                               int32_t* parent, int32_t* depth, float* conf,
                               float* value, int32_t* pool_count,

@@ -22,6 +22,7 @@
  *     et_tree_mask                   -- flatten: ancestor mask, depth, pos
  *     et_tree_attention              -- tree-masked attention (verify)
  *     et_accept                      -- greedy longest accepted path
+ *     et_kv_commit                   -- append the accepted path's K/V
  * Between draft steps the caller runs its draft model on `next_tokens`
  * and hands the resulting vocab logits to the next step.
  *
@@ -212,6 +213,26 @@ int et_accept(et_plan_t plan, void* ws, const void* target_logits,
               const int32_t* tokens, const int32_t* parent_slot,
               const int32_t* n_kept, int32_t* accept_len,
               int32_t* path_slots, int32_t* out_tokens, et_stream_t stream);
+
+/* Commit the verified path to the KV cache (the step after acceptance:
+ * [P1] s2.1, the accepted tokens extend the sequence in path order; the
+ * one verify pass, [P1] s4.2, computed K/V for every tree slot).  The
+ * root (slot 0, the first token not yet in the cache) and the accepted
+ * slots path_slots[b][1..L], L = accept_len[b], in path order, are
+ * appended to the prefix cache: for every kv head, row i of the path goes
+ * to cache position prefix_len[b] + i, copied bit for bit from k_tree /
+ * v_tree; then prefix_len[b] += L + 1.
+ * Layouts (dtype = qkv_dtype): k_cache, v_cache [B][Hkv][prefix_cap][d]
+ * (in/out), k_tree, v_tree [B][Hkv][T][d], prefix_len [B] int32 (in/out),
+ * path_slots [B][D+1] and accept_len [B] int32 as written by et_accept.
+ * Device precondition: prefix_len[b] + accept_len[b] + 1 <= prefix_cap;
+ * rows that would pass prefix_cap are not written and prefix_len[b] stops
+ * at prefix_cap.  No workspace.  Errors: ET_EINVAL (null pointer, K/V
+ * buffer not 16-byte aligned). */
+int et_kv_commit(et_plan_t plan, void* k_cache, void* v_cache,
+                 const void* k_tree, const void* v_tree, int32_t* prefix_len,
+                 const int32_t* path_slots, const int32_t* accept_len,
+                 et_stream_t stream);
 
 /* Inspection: copy the workspace's candidate pool (after any draft step)
  * into caller device buffers, for tests and debugging.  Pool arrays are

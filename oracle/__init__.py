@@ -42,6 +42,7 @@ def lib():
         _lib = ctypes.CDLL(_SO)
         _lib.etref_attention_row.restype = None
         _lib.etref_tree_attention.restype = None
+        _lib.etref_kv_commit.restype = None
     return _lib
 
 
@@ -194,6 +195,21 @@ def accept(w, target, tokens, parent_slot, n_kept):
     if rc != 0:
         raise RuntimeError(f"etref_accept failed: {rc}")
     return dict(accept_len=alen, path_slots=path, out_tokens=otok)
+
+
+def kv_commit(w, attn, prefix_len, path_slots, accept_len):
+    """Commit the accepted paths to copies of the K/V caches (see
+    etref_kv_commit); returns (k_cache, v_cache, prefix_len)."""
+    kc = np.array(attn["k_cache"], copy=True, order="C")
+    vc = np.array(attn["v_cache"], copy=True, order="C")
+    kt = np.ascontiguousarray(attn["k_tree"])
+    vt = np.ascontiguousarray(attn["v_tree"])
+    plen = np.array(prefix_len, dtype=np.int32, copy=True)
+    path, alen = _i32(path_slots), _i32(accept_len)
+    lib().etref_kv_commit(w.batch, w.T, w.n_kv_heads, w.head_dim, w.prefix_cap,
+                          w.depth, kc.dtype.itemsize, _p(kc), _p(vc), _p(kt),
+                          _p(vt), _p(plen), _p(path), _p(alen))
+    return kc, vc, plen
 
 
 def num_threads() -> int:

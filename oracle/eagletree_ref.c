@@ -462,6 +462,41 @@ int etref_accept(int B, int T, int V, int D, int dtype, const void* target,
   return 0;
 }
 
+/* -------------------------------------------------------------------
+ * Commit the verified path to the KV cache: the step after acceptance.
+ * [P1] s2.1: the accepted draft tokens extend the sequence in path order;
+ * [P1] s4.2: the one verify pass computed K/V for every tree slot.
+ * Readings: the root (slot 0) is the first token not yet in the cache, so
+ * the committed tokens are slot 0 and the accepted slots path[1..L]; for
+ * every kv head they become cache positions P_b .. P_b + L, row i being
+ * the K (and V) row of path[i]; P_b becomes P_b + L + 1.  Rows that would
+ * pass prefix_cap are dropped and P_b stops at prefix_cap.  Rows are
+ * copied as raw elements of esz bytes (2 for bf16, 4 for fp32).
+ * ------------------------------------------------------------------- */
+void etref_kv_commit(int B, int T, int Hkv, int dh, int Pcap, int D, int esz,
+                     void* k_cache, void* v_cache, const void* k_tree,
+                     const void* v_tree, int32_t* prefix_len,
+                     const int32_t* path_slots, const int32_t* accept_len) {
+  const size_t row = (size_t)dh * (size_t)esz;
+  for (int b = 0; b < B; ++b) {
+    const int P = prefix_len[b];
+    const int L = accept_len[b];
+    int rows = L + 1;
+    if (P + rows > Pcap) rows = Pcap - P;
+    if (rows < 0) rows = 0;
+    for (int h = 0; h < Hkv; ++h) {
+      for (int i = 0; i < rows; ++i) {
+        const int slot = path_slots[(int64_t)b * (D + 1) + i];
+        const size_t src = (((size_t)b * Hkv + h) * T + slot) * row;
+        const size_t dst = (((size_t)b * Hkv + h) * Pcap + P + i) * row;
+        memcpy((char*)k_cache + dst, (const char*)k_tree + src, row);
+        memcpy((char*)v_cache + dst, (const char*)v_tree + src, row);
+      }
+    }
+    prefix_len[b] = P + rows;
+  }
+}
+
 /* Threads the OpenMP loop above may use (1 without OpenMP). */
 int etref_num_threads(void) {
 #ifdef _OPENMP

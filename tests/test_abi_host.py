@@ -108,4 +108,9 @@ def test_calls_validate_before_launch():
                        fake, nul) == binding.ET_EINVAL
     assert L.et_tree_mask(h, fake, nul, fake, fake, fake, fake,
                           nul) == binding.ET_EINVAL
+    assert L.et_kv_commit(h, fake, fake, fake, fake, fake, fake, nul,
+                          nul) == binding.ET_EINVAL
+    assert L.et_kv_commit(h, fake, ctypes.c_void_p((1 << 20) + 4), fake, fake,
+                          fake, fake, fake, nul) == binding.ET_EINVAL
+    assert b"aligned" in L.et_last_error()
     d.et_plan_destroy(h)

@@ -272,6 +272,45 @@ def test_target_rows_past_n_kept_are_ignored(name):
         assert torch.equal(a, t.cpu())
 
 
+@pytest.mark.parametrize("name", ["tiny", "small_bf16", "f32_gqa", "odd_vocab",
+                                  "llama8b", "llama8b_b64"])
+def test_kv_commit_exact(name):
+    """KV commit after a GPU accept on long planted paths: the caches and
+    the advanced prefix lengths equal the oracle's commit of the same path
+    bit for bit.  Prefix lengths are lowered to leave room (the workloads
+    fill their caches), except one sequence one row short of the cap and,
+    with batch > 2, one at the cap (rows dropped)."""
+    r = _run(name)
+    w, plan, dev, inp = r["w"], r["plan"], r["dev"], r["inp"]
+    g = r["gpu_rr"]
+    rng = np.random.default_rng(7)
+    planted = random_path_targets(w, g, rng, hit=1.0)
+    tgt = gen.target_logits(w, planted=planted, boost=300.0)
+    plan.accept(to_dev(tgt))
+    torch.cuda.synchronize()
+    path = plan.path_slots.cpu().numpy()
+    alen = plan.accept_len.cpu().numpy()
+    prefix = np.minimum(inp["prefix_len"], w.prefix_cap - w.depth - 1).astype(np.int32)
+    prefix = np.maximum(prefix, 0)
+    prefix[0] = w.prefix_cap - 1
+    if w.batch > 2:
+        prefix[1] = w.prefix_cap
+    ref_k, ref_v, ref_p = oracle.kv_commit(w, inp["attn"], prefix, path, alen)
+    kc = dev["attn"]["k_cache"].clone()
+    vc = dev["attn"]["v_cache"].clone()
+    plen = to_dev(prefix)
+    plan.kv_commit(kc, vc, dev["attn"]["k_tree"], dev["attn"]["v_tree"], plen)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(plen.cpu().numpy(), ref_p)
+    view = (lambda t: t.view(torch.int16)) if kc.dtype == torch.bfloat16 else (lambda t: t)
+    ek = np.ascontiguousarray(ref_k).view(np.int16) if ref_k.dtype == np.uint16 else ref_k
+    ev = np.ascontiguousarray(ref_v).view(np.int16) if ref_v.dtype == np.uint16 else ref_v
+    assert np.array_equal(view(kc).cpu().numpy(), ek)
+    assert np.array_equal(view(vc).cpu().numpy(), ev)
+    assert (alen > 0).any()
+    print(f"{name}: committed rows {(ref_p - prefix)[:8]}")
+
+
 def test_cycle_is_deterministic():
     """Two cycles (second on a fresh workspace) give identical bits."""
     d = _lib()

@@ -380,6 +380,67 @@ def test_attention_equals_per_path_causal(dtype):
                                            atol=1e-12)
 
 
+@pytest.mark.parametrize("dtype,seed,Pcap", [("f32", 3, 40), ("bf16", 4, 40),
+                                              ("f32", 5, 12), ("bf16", 6, 12)])
+def test_kv_commit_is_the_path_in_depth_order(dtype, seed, Pcap):
+    """KV commit ([P1] s2.1: accepted tokens extend the sequence in path
+    order): the appended rows are the K/V rows of the root->leaf path, one
+    per depth (depth and ancestry from the independent mask walk, rows
+    matched bit for bit); nothing else in the cache changes; P advances by
+    L + 1 unless prefix_cap stops it; and when nothing is dropped the leaf's
+    tree attention equals dense causal attention over the committed cache
+    (torch fp64 SDPA)."""
+    w, inp, prefix, parent, n_kept, mk = _attn_case(seed, Pcap=Pcap, dtype=dtype)
+    g = np.random.default_rng(seed)
+    path_slots = np.full((w.batch, w.depth + 1), -1, np.int32)
+    accept_len = np.zeros(w.batch, np.int32)
+    leaf = np.zeros(w.batch, np.int64)
+    for b in range(w.batch):
+        # the deepest kept slot that a depth-w.depth walk can reach
+        cands = [s for s in range(n_kept[b] + 1) if mk["depth"][b, s] <= w.depth]
+        leaf[b] = int(g.choice(cands))
+        path, cur = [], int(leaf[b])
+        while cur > 0:
+            path.append(cur)
+            cur = int(parent[b, cur])
+        path = [0] + path[::-1]
+        path_slots[b, :len(path)] = path
+        accept_len[b] = len(path) - 1
+    kc2, vc2, p2 = oracle.kv_commit(w, inp, prefix, path_slots, accept_len)
+    kc, vc, kt, vt = (inp[n] for n in ("k_cache", "v_cache", "k_tree", "v_tree"))
+    q64, kc64, vc64 = (_f64(a, dtype) for a in (inp["q"], kc2, vc2))
+    for b in range(w.batch):
+        P, L = int(prefix[b]), int(accept_len[b])
+        assert p2[b] == min(P + L + 1, w.prefix_cap)
+        new = int(p2[b])
+        for h in range(w.n_kv_heads):
+            assert np.array_equal(kc2[b, h, :P], kc[b, h, :P])
+            assert np.array_equal(kc2[b, h, new:], kc[b, h, new:])
+            assert np.array_equal(vc2[b, h, :P], vc[b, h, :P])
+            assert np.array_equal(vc2[b, h, new:], vc[b, h, new:])
+            for i in range(new - P):
+                hits = [s for s in range(n_kept[b] + 1)
+                        if np.array_equal(kt[b, h, s], kc2[b, h, P + i])]
+                assert len(hits) == 1
+                s = hits[0]
+                assert mk["depth"][b, s] == i
+                word = int(mk["mask"][b, leaf[b], s // 64])
+                assert (word >> (s % 64)) & 1
+                assert np.array_equal(vt[b, h, s], vc2[b, h, P + i])
+        if P + L + 1 > w.prefix_cap:
+            continue
+        out = oracle.tree_attention(w, inp, prefix, mk["mask"], n_kept)
+        for hq in range(w.n_q_heads):
+            kv = hq // w.G
+            qs = np.zeros((new, w.head_dim))
+            qs[-1] = q64[b, leaf[b], hq]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(qs)[None], torch.from_numpy(kc64[b, kv, :new])[None],
+                torch.from_numpy(vc64[b, kv, :new])[None], is_causal=True,
+                scale=w.scale)[0, -1].numpy()
+            np.testing.assert_allclose(out[b, leaf[b], hq], ref, rtol=0, atol=1e-12)
+
+
 def test_attention_equal_keys_is_mean_of_visible_values():
     """Closed form: with every key equal the softmax is uniform, so the
     output is the mean of the visible values (prefix + ancestors + self)."""
