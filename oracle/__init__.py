@@ -197,6 +197,31 @@ def accept(w, target, tokens, parent_slot, n_kept):
     return dict(accept_len=alen, path_slots=path, out_tokens=otok)
 
 
+def accept_sample(w, target, tokens, parent_slot, n_kept, temperature,
+                  uniforms):
+    """Stochastic acceptance at temperature > 0 (see etref_accept_sample);
+    uniforms is fp32 [B][T] in [0, 1).  Also returns the smallest decision
+    margin per sequence (relative to the row's total target mass)."""
+    B, D = w.batch, w.depth
+    ptr, bs, rs = _rows(target)
+    tokens, parent_slot, n_kept = map(_i32, (tokens, parent_slot, n_kept))
+    u = np.ascontiguousarray(uniforms, dtype=np.float32)
+    assert u.shape == (B, w.T)
+    alen = np.empty(B, np.int32)
+    path = np.empty((B, D + 1), np.int32)
+    otok = np.empty((B, D + 1), np.int32)
+    margin = np.empty(B, np.float64)
+    rc = lib().etref_accept_sample(
+        B, w.T, w.vocab, D, _DT[w.logits_dtype], ptr, ctypes.c_int64(bs),
+        ctypes.c_int64(rs), _p(tokens), _p(parent_slot), _p(n_kept),
+        ctypes.c_double(float(temperature)), _p(u), _p(alen), _p(path),
+        _p(otok), _p(margin))
+    if rc != 0:
+        raise RuntimeError(f"etref_accept_sample failed: {rc}")
+    return dict(accept_len=alen, path_slots=path, out_tokens=otok,
+                margin=margin)
+
+
 def kv_commit(w, attn, prefix_len, path_slots, accept_len):
     """Commit the accepted paths to copies of the K/V caches (see
     etref_kv_commit); returns (k_cache, v_cache, prefix_len)."""

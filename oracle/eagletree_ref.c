@@ -497,6 +497,137 @@ void etref_kv_commit(int B, int T, int Hkv, int dh, int Pcap, int D, int esz,
   }
 }
 
+/* ---------------------------------------------------------------------
+ * Stochastic acceptance at temperature tau > 0 ([P1] s2.1: draft tokens
+ * are accepted one after another by the ratio of target to draft
+ * probability; [P1] s2.2: on a rejection the tree lets a sibling branch be
+ * tried; [P1] s1: the output distribution stays the target's).
+ * Readings, since the pages give only the chain rule:
+ *  - the draft tokens of a node are its top-k (chosen, not sampled), so
+ *    as a proposal each is a point mass: the ratio for child token t is
+ *    p(t) / 1, and rejecting t leaves the residual max(p - delta_t, 0),
+ *    i.e. p with t removed and renormalised;
+ *  - p = softmax(target row / tau) over the whole vocabulary;
+ *  - a node's children are tried in slot order (highest value first);
+ *    child c is accepted iff u[c] * R < p(token c), R being the target
+ *    mass not yet rejected at this node (unnormalised weights below);
+ *  - when every child of the final node is rejected (or it has none), the
+ *    bonus token is drawn from the residual by inverse CDF in token-id
+ *    order with u[0]: the first id whose running residual mass exceeds
+ *    u[0] * R (no such id: the last id of positive residual mass; none
+ *    of those either: the lowest id not rejected).
+ * uniforms: fp32 [B][T] in [0, 1); u[b][s] is used when slot s is tried
+ * (each slot at most once per cycle), u[b][0] for the bonus draw.
+ * margin[b]: the smallest |u*R - p| (ratio tests) or distance of u[0]*R
+ * to the chosen id's mass interval (bonus), over every decision taken,
+ * relative to the row's total mass; a run with a small margin may flip
+ * under a different rounding order of the same sums.
+ * ------------------------------------------------------------------- */
+int etref_accept_sample(int B, int T, int V, int D, int dtype,
+                        const void* target, int64_t bstride, int64_t rstride,
+                        const int32_t* tokens, const int32_t* parent_slot,
+                        const int32_t* n_kept, double tau,
+                        const float* uniforms, int32_t* accept_len,
+                        int32_t* path_slots, int32_t* out_tokens,
+                        double* margin) {
+  double* wgt = (double*)malloc(sizeof(double) * (size_t)V);
+  char* rejected = (char*)malloc((size_t)V);
+  if (!wgt || !rejected) {
+    free(wgt);
+    free(rejected);
+    return -2;
+  }
+  for (int b = 0; b < B; ++b) {
+    const int n = n_kept[b];
+    const int32_t* tk = tokens + (int64_t)b * T;
+    const int32_t* ps = parent_slot + (int64_t)b * T;
+    const float* u = uniforms + (int64_t)b * T;
+    int32_t* pth = path_slots + (int64_t)b * (D + 1);
+    int32_t* ot = out_tokens + (int64_t)b * (D + 1);
+    for (int i = 0; i <= D; ++i) {
+      pth[i] = -1;
+      ot[i] = -1;
+    }
+    pth[0] = 0;
+    int cur = 0, len = 0;
+    double mg = INFINITY;
+    for (;;) {
+      /* target weights exp((x - max) / tau) of the current slot's row */
+      const char* row = (const char*)target +
+                        (b * bstride + cur * rstride) * (dtype == REF_F32 ? 4 : 2);
+      double m = -INFINITY;
+      for (int v = 0; v < V; ++v) {
+        double x = ref_load(row, dtype, v);
+        if (x > m) m = x;
+      }
+      double Z = 0.0;
+      for (int v = 0; v < V; ++v) {
+        wgt[v] = exp((ref_load(row, dtype, v) - m) / tau);
+        Z += wgt[v];
+      }
+      memset(rejected, 0, (size_t)V);
+      /* ratio tests of the children, in slot order */
+      double R = Z;
+      int next = -1;
+      if (len < D) {
+        for (int c = 1; c <= n; ++c) {
+          if (ps[c] != cur) continue;
+          const double p = wgt[tk[c]];
+          const double lhs = (double)u[c] * R;
+          const double d = fabs(lhs - p) / Z;
+          if (d < mg) mg = d;
+          if (lhs < p) {
+            next = c;
+            break;
+          }
+          R -= p;
+          rejected[tk[c]] = 1;
+        }
+      }
+      if (next >= 0) {
+        ot[len] = tk[next];
+        ++len;
+        pth[len] = next;
+        cur = next;
+        continue;
+      }
+      /* bonus: inverse CDF of the residual in id order */
+      const double t = (double)u[0] * R;
+      double C = 0.0;
+      int pick = -1, last = -1;
+      for (int v = 0; v < V; ++v) {
+        if (rejected[v] || !(wgt[v] > 0.0)) continue;
+        const double Cn = C + wgt[v];
+        last = v;
+        if (Cn > t) {
+          const double d = fmin(t - C, Cn - t) / Z;
+          if (d < mg) mg = d;
+          pick = v;
+          break;
+        }
+        C = Cn;
+      }
+      if (pick < 0 && last >= 0) {
+        const double d = fabs(t - C) / Z;
+        if (d < mg) mg = d;
+        pick = last;
+      }
+      if (pick < 0) {
+        pick = 0;
+        while (pick < V - 1 && rejected[pick]) ++pick;
+        mg = 0.0;
+      }
+      ot[len] = pick;
+      break;
+    }
+    accept_len[b] = len;
+    margin[b] = mg;
+  }
+  free(wgt);
+  free(rejected);
+  return 0;
+}
+
 /* Threads the OpenMP loop above may use (1 without OpenMP). */
 int etref_num_threads(void) {
 #ifdef _OPENMP

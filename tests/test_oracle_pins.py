@@ -559,6 +559,149 @@ def test_expected_accept_equals_sum_of_values():
     assert abs(L.mean() - expect) < 2.576 * L.std() / math.sqrt(trials) + 1e-3
 
 
+# ------------------------------------------------- sampled accept (T > 0)
+def _tree_targets(w, rr, g, planted_boost, gap=0.0):
+    """Target rows [1][T][V] ~ 1.5 N(0,1); every kept slot's token gets
+    planted_boost at its parent's row (so children carry real mass); with
+    gap > 0 each row's maximum is raised by gap above the runner-up."""
+    target = g.standard_normal((1, w.T, w.vocab)) * 1.5
+    n = int(rr["n_kept"][0])
+    for c in range(1, n + 1):
+        if g.random() < 0.8:
+            target[0, rr["parent_slot"][0, c], rr["tokens"][0, c]] += planted_boost
+    if gap > 0:
+        for s in range(w.T):
+            r = target[0, s]
+            i = int(np.argmax(r))
+            r[i] += gap
+    return target.astype(np.float32)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_sampled_accept_low_temperature_is_greedy(seed):
+    """As the temperature goes to 0 the target softmax becomes the argmax
+    point mass, so the ratio tests accept exactly the greedy path ([P1]
+    s2.1 and [P4] s五: greedy decoding) and the bonus is the argmax: equal
+    to the greedy walk, itself pinned by brute force."""
+    w = _small(vocab=40, topk=3, depth=4, budget_n=12, sharpness=(2.0,))
+    w, st, _, _ = _random_tree(w, 100 + seed)
+    rr = oracle.rerank(w, st)
+    g = np.random.default_rng(seed)
+    target = _tree_targets(w, rr, g, planted_boost=6.0, gap=0.5)
+    u = g.uniform(1e-3, 1.0, (1, w.T)).astype(np.float32)
+    greedy = oracle.accept(w, target, rr["tokens"], rr["parent_slot"],
+                           rr["n_kept"])
+    samp = oracle.accept_sample(w, target, rr["tokens"], rr["parent_slot"],
+                                rr["n_kept"], 1e-3, u)
+    for k in ("accept_len", "path_slots", "out_tokens"):
+        np.testing.assert_array_equal(samp[k], greedy[k])
+    assert samp["margin"][0] > 1e-6
+
+
+def _chi2_ok(counts, probs, alpha=1e-4):
+    """Pearson chi-square of counts against probs, bins with expected
+    count < 5 pooled into one."""
+    from scipy.stats import chisquare
+    n = counts.sum()
+    exp = probs * n
+    big = exp >= 5
+    obs = np.append(counts[big], counts[~big].sum())
+    ex = np.append(exp[big], exp[~big].sum())
+    if ex[-1] < 5:
+        obs[-2] += obs[-1]
+        ex[-2] += ex[-1]
+        obs, ex = obs[:-1], ex[:-1]
+    return chisquare(obs, ex * (obs.sum() / ex.sum())).pvalue > alpha
+
+
+@pytest.mark.parametrize("tau", [0.7, 1.3])
+def test_sampled_accept_preserves_the_target_distribution(tau):
+    """Losslessness ([P1] s1: the generated text keeps the target model's
+    distribution).  Over many uniform draws on one tree, the first output
+    token follows softmax(target[root] / tau) exactly, and given that it
+    is the token of root child c, the second output token follows
+    softmax(target[c] / tau), and so on one level deeper (chi-square)."""
+    w = _small(vocab=10, topk=3, depth=3, budget_n=8, sharpness=(1.0,))
+    w, st, _, _ = _random_tree(w, 3)
+    rr = oracle.rerank(w, st)
+    g = np.random.default_rng(11)
+    target = _tree_targets(w, rr, g, planted_boost=1.5)
+    trials = 60000
+    wt = w.with_(batch=trials)
+    rep = {k: np.repeat(rr[k], trials, axis=0)
+           for k in ("tokens", "parent_slot", "n_kept")}
+    tb = np.broadcast_to(target, (trials, w.T, w.vocab))
+    u = g.random((trials, w.T), dtype=np.float32)
+    acc = oracle.accept_sample(wt, tb, rep["tokens"], rep["parent_slot"],
+                               rep["n_kept"], tau, u)
+    out = acc["out_tokens"]
+    tok, par = rr["tokens"][0], rr["parent_slot"][0]
+    n = int(rr["n_kept"][0])
+
+    def sm(s):
+        x = target[0, s].astype(np.float64) / tau
+        e = np.exp(x - x.max())
+        return e / e.sum()
+
+    assert _chi2_ok(np.bincount(out[:, 0], minlength=w.vocab), sm(0))
+    checked = 0
+    for c in range(1, n + 1):
+        if par[c] != 0:
+            continue
+        sel = out[:, 0] == tok[c]
+        assert (acc["accept_len"][sel] >= 1).all()
+        if sel.sum() < 500:
+            continue
+        assert _chi2_ok(np.bincount(out[sel, 1], minlength=w.vocab), sm(c))
+        checked += 1
+        for c2 in range(1, n + 1):
+            if par[c2] != c:
+                continue
+            sel2 = sel & (out[:, 1] == tok[c2])
+            if sel2.sum() < 500:
+                continue
+            assert _chi2_ok(np.bincount(out[sel2, 2], minlength=w.vocab), sm(c2))
+            checked += 1
+    assert checked >= 2
+    # the bonus is never a rejected sibling: when the walk stops at slot
+    # s, out_tokens[L] is not the token of any child of s
+    L = acc["accept_len"]
+    last = acc["path_slots"][np.arange(trials), L]
+    bonus = out[np.arange(trials), L]
+    for s in range(n + 1):
+        kids = {int(tok[c]) for c in range(1, n + 1) if par[c] == s}
+        at = last == s
+        assert not np.isin(bonus[at], list(kids)).any()
+
+
+def test_sampled_accept_zero_uniforms_take_first_child():
+    """u = 0: every ratio test passes for a child of positive mass, so the
+    walk follows the first (highest-value) child of each slot to a leaf,
+    and the bonus is id 0 (the residual's first id of positive mass)."""
+    w = _small(vocab=30, topk=3, depth=4, budget_n=12, sharpness=(2.0,))
+    for seed in range(10):
+        w, st, _, _ = _random_tree(w, 200 + seed)
+        rr = oracle.rerank(w, st)
+        g = np.random.default_rng(seed)
+        target = _tree_targets(w, rr, g, planted_boost=0.0)
+        u = np.zeros((1, w.T), np.float32)
+        acc = oracle.accept_sample(w, target, rr["tokens"], rr["parent_slot"],
+                                   rr["n_kept"], 1.0, u)
+        n = int(rr["n_kept"][0])
+        par = rr["parent_slot"][0]
+        cur, path = 0, [0]
+        while True:
+            kids = [c for c in range(1, n + 1) if par[c] == cur]
+            if not kids:
+                break
+            cur = min(kids)
+            path.append(cur)
+        L = len(path) - 1
+        assert acc["accept_len"][0] == L
+        np.testing.assert_array_equal(acc["path_slots"][0, :L + 1], path)
+        assert acc["out_tokens"][0, L] == 0
+
+
 # ---------------------------------------------------------------- generator
 def test_bf16_rounding_is_nearest_even():
     x = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, -2.5, 3.0e38],
