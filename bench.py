@@ -338,32 +338,42 @@ def main():
         done += nb
     avg_us = {n: acc[n] / cnt[n] for n in names}
 
-    # ---- the step after the cycle (not part of the metric): KV commit ----
-    # The last cycle's accepted paths are appended to copies of input set
-    # 0's caches, with the prefix lengths lowered to leave room (the
-    # workloads fill their caches); each call is timed on its own, the
-    # prefix lengths restored before it, the GPU held as above.
+    # ---- calls beside the cycle (not part of the metric) ----
+    # KV commit: the last cycle's accepted paths are appended to copies of
+    # input set 0's caches, with the prefix lengths lowered to leave room
+    # (the workloads fill their caches), restored before each call.
+    # Sampled acceptance (temperature 1) of the last cycle's tree on set
+    # 0's targets, in place of the greedy walk.  Each call is timed on its
+    # own, 20 times, the GPU held as above; the median is reported.
+    def time_next(call, before=None):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(hold_ms * spin_per_ms))
+        ev = []
+        for _ in range(20):
+            if before is not None:
+                before()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+
     ds0 = sets[0]
     kc = ds0["attn"]["k_cache"].clone()
     vc = ds0["attn"]["v_cache"].clone()
     plen0 = torch.clamp(ds0["prefix"], max=w.prefix_cap - w.depth - 1)
     plen = plen0.clone()
-    commit_us = []
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(hold_ms * spin_per_ms))
-    ev = []
-    for _ in range(20):
-        plen.copy_(plen0)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        plan.kv_commit(kc, vc, ds0["attn"]["k_tree"], ds0["attn"]["v_tree"], plen,
-                       stream)
-        e1.record(stream)
-        ev.append((e0, e1))
-    torch.cuda.synchronize()
-    commit_us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+    commit_us = time_next(
+        lambda: plan.kv_commit(kc, vc, ds0["attn"]["k_tree"], ds0["attn"]["v_tree"],
+                               plen, stream),
+        lambda: plen.copy_(plen0))
     del kc, vc
+    uni = torch.rand((w.batch, w.T), device="cuda",
+                     generator=torch.Generator(device="cuda").manual_seed(w.seed))
+    sample_us = time_next(lambda: plan.accept_sample(ds0["target"], 1.0, uni, stream))
     per_cycle_us = {n: acc[n] / K for n in names}
 
     # algorithmic bytes of the last cycle's shapes
@@ -444,7 +454,8 @@ def main():
         "roofline": roofline,
         "per_call_us": {n: round(avg_us[n], 3) for n in names},
         "per_cycle_us": {n: round(per_cycle_us[n], 3) for n in names},
-        "next_calls_us": {"kv_commit": round(commit_us, 3)},
+        "next_calls_us": {"kv_commit": round(commit_us, 3),
+                          "accept_sample": round(sample_us, 3)},
         "cpu_baseline": cpu,
         "gen_seconds": round(gen_s, 1),
     }

@@ -4,7 +4,8 @@ The product is the C-ABI library libeagletree.so (include/eagletree.h);
 this package holds its HIP sources (csrc/), the build step and a thin
 ctypes binding that passes torch device pointers and streams through.
 """
-from .binding import (EXPORTS, EtError, Plan, et_accept, et_config,  # noqa: F401
+from .binding import (EXPORTS, EtError, Plan, et_accept,  # noqa: F401
+                      et_accept_sample, et_config,
                       et_draft_step, et_kv_commit, et_plan_create,
                       et_plan_destroy,
                       et_pool_capacity, et_pool_export, et_rerank,

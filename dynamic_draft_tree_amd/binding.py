@@ -23,7 +23,8 @@ _STATUS = {ET_EINVAL: "ET_EINVAL", ET_EUNSUPPORTED: "ET_EUNSUPPORTED",
 EXPORTS = ("et_plan_create", "et_plan_destroy", "et_workspace_bytes",
            "et_pool_capacity", "et_workspace_init", "et_draft_step",
            "et_rerank", "et_tree_mask", "et_tree_attention", "et_accept",
-           "et_kv_commit", "et_pool_export", "et_last_error")
+           "et_accept_sample", "et_kv_commit", "et_pool_export",
+           "et_last_error")
 
 
 class et_config(ctypes.Structure):
@@ -69,6 +70,8 @@ def lib():
             "et_tree_attention": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp],
                                   ctypes.c_int),
             "et_accept": ([vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+            "et_accept_sample": ([vp, vp, vp, i64, i64, vp, vp, vp, f32, vp, vp, vp, vp,
+                                  vp], ctypes.c_int),
             "et_kv_commit": ([vp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "et_pool_export": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "et_last_error": ([], ctypes.c_char_p),
@@ -184,6 +187,20 @@ def et_accept(plan, ws, target_logits, tokens, parent_slot, n_kept,
                            _ptr(out_tokens), _stream(stream)))
 
 
+def et_accept_sample(plan, ws, target_logits, tokens, parent_slot, n_kept,
+                     temperature, uniforms, accept_len, path_slots, out_tokens,
+                     stream=None):
+    bs, rs = _rows(target_logits)
+    if not uniforms.is_contiguous() or uniforms.dtype != torch.float32:
+        raise ValueError("uniforms must be contiguous float32 [B][T]")
+    _check(lib().et_accept_sample(plan, _ptr(ws), _ptr(target_logits), bs, rs,
+                                  _ptr(tokens), _ptr(parent_slot),
+                                  _ptr(n_kept), float(temperature),
+                                  _ptr(uniforms), _ptr(accept_len),
+                                  _ptr(path_slots), _ptr(out_tokens),
+                                  _stream(stream)))
+
+
 def et_kv_commit(plan, k_cache, v_cache, k_tree, v_tree, prefix_len,
                  path_slots, accept_len, stream=None):
     for t in (k_cache, v_cache, k_tree, v_tree):
@@ -267,6 +284,13 @@ class Plan:
         et_accept(self.handle, self.ws, target_logits, self.tokens,
                   self.parent_slot, self.n_kept, self.accept_len,
                   self.path_slots, self.out_tokens, stream)
+
+    def accept_sample(self, target_logits, temperature, uniforms, stream=None):
+        """Ratio-test acceptance at temperature > 0; uniforms [B][T] f32."""
+        et_accept_sample(self.handle, self.ws, target_logits, self.tokens,
+                         self.parent_slot, self.n_kept, temperature, uniforms,
+                         self.accept_len, self.path_slots, self.out_tokens,
+                         stream)
 
     def kv_commit(self, k_cache, v_cache, k_tree, v_tree, prefix_len,
                   stream=None):

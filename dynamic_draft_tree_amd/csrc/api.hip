@@ -1,6 +1,7 @@
 // api.hip -- the extern "C" boundary of libeagletree: argument validation,
 // plan creation, workspace layout and kernel launches.  Every check runs
 // on the host before anything is launched; kernels never allocate.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -59,7 +60,9 @@ void layout(et::Plan& p) {
   const size_t W4 = et::kScanThreads / 64;
   sz[R_PART_M] = sz[R_PART_S] = B * k * S * W4 * 4;
   sz[R_PART_KEYS] = B * k * S * W4 * et::kMaxTopk * 8;
-  sz[R_ACC_PART] = B * T * p.s_accept * W4 * 8;
+  // accept partials: per (slot row, chunk, wave) an 8-byte argmax key
+  // (greedy) or a 16-byte (max, fp64 mass) pair (sampled)
+  sz[R_ACC_PART] = B * T * p.s_accept * W4 * 16;
   sz[R_ATT_O] = att_rows * p.HD * 4;
   sz[R_ATT_M] = sz[R_ATT_L] = att_rows * 4;
   size_t off = 0;
@@ -393,6 +396,47 @@ int et_accept(et_plan_t plan, void* ws, const void* target_logits,
                         row_stride, vec, tokens, parent_slot, n_kept,
                         accept_len, path_slots, out_tokens,
                         (hipStream_t)stream),
+      fn);
+}
+
+int et_accept_sample(et_plan_t plan, void* ws, const void* target_logits,
+                     int64_t batch_stride, int64_t row_stride,
+                     const int32_t* tokens, const int32_t* parent_slot,
+                     const int32_t* n_kept, float temperature,
+                     const float* uniforms, int32_t* accept_len,
+                     int32_t* path_slots, int32_t* out_tokens,
+                     et_stream_t stream) {
+  const char* fn = "et_accept_sample";
+  CHECK_PTR(plan);
+  CHECK_PTR(ws);
+  CHECK_PTR(target_logits);
+  CHECK_PTR(tokens);
+  CHECK_PTR(parent_slot);
+  CHECK_PTR(n_kept);
+  CHECK_PTR(uniforms);
+  CHECK_PTR(accept_len);
+  CHECK_PTR(path_slots);
+  CHECK_PTR(out_tokens);
+  et::Plan& p = *as_plan(plan);
+  if (row_stride < p.V)
+    return fail(ET_EINVAL, "%s: row_stride %lld < vocab %d", fn,
+                (long long)row_stride, p.V);
+  if (batch_stride < 0)
+    return fail(ET_EINVAL, "%s: negative batch_stride", fn);
+  if (((uintptr_t)ws & 255u) != 0)
+    return fail(ET_EINVAL, "%s: workspace not 256-byte aligned", fn);
+  // weights are exp2((x - max) * c); c must be a finite positive float
+  const double c = 1.4426950408889634 / (double)temperature;
+  if (!(temperature > 0.0f) || !std::isfinite(temperature) || !std::isfinite((float)c))
+    return fail(ET_EINVAL, "%s: temperature %g out of range", fn, (double)temperature);
+  const int per = p.ldt == ET_BF16 ? 8 : 4;
+  const bool vec = aligned16(target_logits) && batch_stride % per == 0 &&
+                   row_stride % per == 0 && p.V >= per;
+  return hip_status(
+      et::launch_accept_sample(p, et::accept_ws(p, ws), target_logits,
+                               batch_stride, row_stride, vec, tokens,
+                               parent_slot, n_kept, c, uniforms, accept_len,
+                               path_slots, out_tokens, (hipStream_t)stream),
       fn);
 }
 

@@ -1,8 +1,6 @@
 // internal.h -- plan, workspace layout and kernel launchers of libeagletree.
 //
 // Workspace (device, caller-allocated, 256-byte aligned regions):
-//   counters     u32   arrival tickets of the last-block merges; cleared by
-//                      et_workspace_init and reset by every consumer
 //   pool         SoA   token/parent/depth i32, conf/value f32  [B][cap]
 //   pool_count, root_token                                     [B]
 //   frontier     i32   [2][B][k] pool indices (and f32 values), double-
@@ -11,7 +9,8 @@
 //   frontier_count i32 [2][B]
 //   draft partials     per (row, chunk, wave): max, sum, top-k logit keys
 //   draft rows         per row: max, fp64 sum, top-k logit keys
-//   accept partials    per (slot row, chunk): argmax key; per row argmax
+//   accept partials    per (slot row, chunk, wave): argmax key (greedy) or
+//                      (max, mass) of the wave's id range (sampled)
 //   attention partials per (b, kv head, q block, split): O, m, l
 #pragma once
 
@@ -71,7 +70,8 @@ struct DraftWs {
 };
 
 struct AcceptWs {
-  uint64_t* part;         // [B][T][S][waves] (max logit, lowest id) keys
+  uint64_t* part;         // [B][T][S][waves] (max logit, lowest id) keys, or
+                          // double2 (max, mass) per id range when sampling
 };
 
 struct AttnWs {
@@ -128,6 +128,12 @@ hipError_t launch_accept(const Plan& p, const AcceptWs& w, const void* target,
                          const int32_t* n_kept, int32_t* accept_len,
                          int32_t* path_slots, int32_t* out_tokens,
                          hipStream_t s);
+hipError_t launch_accept_sample(const Plan& p, const AcceptWs& w, const void* target,
+                                int64_t bstride, int64_t rstride, bool vec,
+                                const int32_t* tokens, const int32_t* parent_slot,
+                                const int32_t* n_kept, double c, const float* uniforms,
+                                int32_t* accept_len, int32_t* path_slots,
+                                int32_t* out_tokens, hipStream_t s);
 hipError_t launch_kv_commit(const Plan& p, void* k_cache, void* v_cache,
                             const void* k_tree, const void* v_tree,
                             int32_t* prefix_len, const int32_t* path_slots,

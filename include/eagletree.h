@@ -22,6 +22,7 @@
  *     et_tree_mask                   -- flatten: ancestor mask, depth, pos
  *     et_tree_attention              -- tree-masked attention (verify)
  *     et_accept                      -- greedy longest accepted path
+ *       (or et_accept_sample           -- ratio tests at temperature > 0)
  *     et_kv_commit                   -- append the accepted path's K/V
  * Between draft steps the caller runs its draft model on `next_tokens`
  * and hands the resulting vocab logits to the next step.
@@ -213,6 +214,41 @@ int et_accept(et_plan_t plan, void* ws, const void* target_logits,
               const int32_t* tokens, const int32_t* parent_slot,
               const int32_t* n_kept, int32_t* accept_len,
               int32_t* path_slots, int32_t* out_tokens, et_stream_t stream);
+
+/* Stochastic acceptance at temperature > 0 ([P1] s2.1: draft tokens are
+ * accepted one after another by the ratio of target to draft probability;
+ * [P1] s2.2: the tree lets the siblings of a rejected token be tried;
+ * [P1] s1: the output keeps the target model's distribution).  The pages
+ * give the chain rule only; the tree form used here: a node's children
+ * are its top-k, chosen rather than sampled, so each is a point-mass
+ * proposal.  With p = softmax(target row of the current slot /
+ * temperature), the children of the current slot are tried in slot order
+ * (highest value first); child c is accepted iff
+ *     uniforms[b][c] * R < p(tokens[c]),
+ * R being the target mass not yet rejected at this slot (1 before the
+ * first try, minus p of each rejected sibling); the walk moves to the
+ * accepted child.  When every child is rejected (or there is none, or
+ * the walk reached depth D), the bonus token is drawn from the residual
+ * (p without the rejected tokens) by inverse CDF in id order with
+ * uniforms[b][0]: the first id whose running residual mass exceeds
+ * uniforms[b][0] * R.  Every decision compares fp32-computed masses
+ * (fp64 sums), so a run whose u lies within about 1e-6 of a decision
+ * boundary may go either way; otherwise the result is the exact rule.
+ * Inputs as et_accept (all T rows readable; rows past n_kept ignored;
+ * every kept row has a finite maximum), plus:
+ *   temperature  finite and > 0, with log2(e) / temperature a finite float
+ *   uniforms     device fp32 [B][T], each in [0, 1); entry s is used when
+ *                slot s is tried (at most once per call), entry 0 for the
+ *                bonus
+ * Outputs as et_accept; the bonus is never a rejected child's token.
+ * Shares the accept region of the workspace with et_accept. */
+int et_accept_sample(et_plan_t plan, void* ws, const void* target_logits,
+                     int64_t batch_stride, int64_t row_stride,
+                     const int32_t* tokens, const int32_t* parent_slot,
+                     const int32_t* n_kept, float temperature,
+                     const float* uniforms, int32_t* accept_len,
+                     int32_t* path_slots, int32_t* out_tokens,
+                     et_stream_t stream);
 
 /* Commit the verified path to the KV cache (the step after acceptance:
  * [P1] s2.1, the accepted tokens extend the sequence in path order; the

@@ -113,4 +113,14 @@ def test_calls_validate_before_launch():
     assert L.et_kv_commit(h, fake, ctypes.c_void_p((1 << 20) + 4), fake, fake,
                           fake, fake, fake, nul) == binding.ET_EINVAL
     assert b"aligned" in L.et_last_error()
+    f = ctypes.c_float
+    assert L.et_accept_sample(h, fake, fake, 0, 1024, fake, fake, fake, f(1.0),
+                              nul, fake, fake, fake, nul) == binding.ET_EINVAL
+    assert L.et_accept_sample(h, fake, fake, 0, 1000, fake, fake, fake, f(1.0),
+                              fake, fake, fake, fake, nul) == binding.ET_EINVAL
+    for bad in (0.0, -1.0, 1e-40, float("nan"), float("inf")):
+        assert L.et_accept_sample(h, fake, fake, 0, 1024, fake, fake, fake,
+                                  f(bad), fake, fake, fake, fake,
+                                  nul) == binding.ET_EINVAL, bad
+        assert b"temperature" in L.et_last_error()
     d.et_plan_destroy(h)

@@ -250,10 +250,148 @@ def test_accept_exact(name):
     print(f"{name}: accept_len {plan.accept_len.cpu().numpy()[:8]}")
 
 
+# Sampled acceptance: the GPU's masses carry one fp32 rounding per weight
+# (fp64 sums), the oracle's none; a decision whose oracle margin is below
+# this fraction of the row's mass may go either way (the GPU's running-mass
+# error is at most about 6e-8 of it).  Outside such near-ties the outputs
+# must be identical, and such mismatches must stay rare.
+SAMPLE_TOL = 1e-6
+
+
+def _check_sampled(w, g, gpu, ref):
+    """GPU sampled accept vs the oracle on the same inputs; returns the
+    number of sequences excused as near-ties (each still a valid walk)."""
+    ga, gp, go = gpu
+    near = 0
+    for b in range(w.batch):
+        if (ga[b] == ref["accept_len"][b] and (gp[b] == ref["path_slots"][b]).all()
+                and (go[b] == ref["out_tokens"][b]).all()):
+            continue
+        assert ref["margin"][b] < SAMPLE_TOL, (b, ref["margin"][b], ga[b],
+                                               ref["accept_len"][b])
+        near += 1
+        L, n = int(ga[b]), int(g["n_kept"][b])
+        assert 0 <= L <= w.depth and gp[b, 0] == 0
+        for i in range(1, L + 1):
+            s = int(gp[b, i])
+            assert 1 <= s <= n and g["parent_slot"][b, s] == gp[b, i - 1]
+            assert go[b, i - 1] == g["tokens"][b, s]
+        last = int(gp[b, L])
+        kids = {int(g["tokens"][b, c]) for c in range(1, n + 1)
+                if g["parent_slot"][b, c] == last}
+        assert 0 <= go[b, L] < w.vocab
+        if L < w.depth:
+            assert int(go[b, L]) not in kids
+        assert (gp[b, L + 1:] == -1).all() and (go[b, L + 1:] == -1).all()
+    return near
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_accept_sample_parity(name):
+    """Ratio-test acceptance at temperature 0.3 and 1 on the generated
+    targets and on calibrated targets planted along a random kept path,
+    with random, all-zero and all-near-one uniforms."""
+    r = _run(name)
+    w, plan, inp = r["w"], r["plan"], r["inp"]
+    g = r["gpu_rr"]
+    rng = np.random.default_rng(3)
+    planted = random_path_targets(w, g, rng)
+    cases, near, total = 0, 0, 0
+    for ti, tgt in enumerate((inp["target"], gen.target_logits(w, planted=planted))):
+        td = to_dev(tgt)
+        for tau in (0.3, 1.0):
+            draws = [rng.random((w.batch, w.T), dtype=np.float32)]
+            if ti == 0 and tau == 1.0:
+                draws.append(np.zeros((w.batch, w.T), np.float32))
+                draws.append(np.full((w.batch, w.T), np.nextafter(np.float32(1), np.float32(0)),
+                                     np.float32))
+            for u in draws:
+                print(f"[parity] {name}: sampled accept target {ti} tau {tau}",
+                      flush=True)
+                plan.accept_sample(td, tau, to_dev(u))
+                torch.cuda.synchronize()
+                gpu = (plan.accept_len.cpu().numpy(), plan.path_slots.cpu().numpy(),
+                       plan.out_tokens.cpu().numpy())
+                ref = oracle.accept_sample(w, tgt, g["tokens"], g["parent_slot"],
+                                           g["n_kept"], tau, u)
+                near += _check_sampled(w, g, gpu, ref)
+                total += w.batch
+                cases += 1
+    assert near <= max(2, total // 200), (near, total)
+    print(f"{name}: {cases} sampled-accept cases, {near}/{total} near-ties")
+
+
+def _chi2_ok(counts, probs, alpha=1e-4):
+    """Pearson chi-square of counts against probs (bins expecting < 5
+    pooled)."""
+    from scipy.stats import chisquare
+    exp = probs * counts.sum()
+    big = exp >= 5
+    obs = np.append(counts[big], counts[~big].sum())
+    ex = np.append(exp[big], exp[~big].sum())
+    if ex[-1] < 5:
+        obs[-2] += obs[-1]
+        ex[-2] += ex[-1]
+        obs, ex = obs[:-1], ex[:-1]
+    return chisquare(obs, ex * (obs.sum() / ex.sum())).pvalue > alpha
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_accept_sample_distribution(dtype):
+    """Losslessness of the GPU path on its own: one tree replicated over
+    16384 sequences with independent uniforms; the first output token
+    follows softmax(target[root] / tau), and given root child c the second
+    follows softmax(target[c] / tau) (chi-square at 1e-4)."""
+    d = _lib()
+    B, tau = 16384, 0.8
+    w1 = TINY.with_(batch=1, vocab=40, topk=3, depth=3, budget_n=8,
+                    threshold=0.0, sharpness=(1.0,), logits_dtype=dtype, seed=31)
+    st = oracle.build_tree(w1, gen.root_tokens(w1), gen.draft_logits(w1))
+    rr = oracle.rerank(w1, st)
+    n = int(rr["n_kept"][0])
+    rng = np.random.default_rng(4)
+    target = rng.standard_normal((1, w1.T, w1.vocab)) * 1.5
+    for c in range(1, n + 1):
+        target[0, rr["parent_slot"][0, c], rr["tokens"][0, c]] += 1.5
+    if dtype == "bf16":
+        bits = gen.f32_to_bf16_bits(target.astype(np.float32))
+        target = gen.bf16_bits_to_f32(bits).astype(np.float64)
+        tdev = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    else:
+        target = target.astype(np.float32).astype(np.float64)
+        tdev = torch.from_numpy(target.astype(np.float32))
+    tdev = tdev.cuda().expand(B, w1.T, w1.vocab).contiguous()
+    wB = w1.with_(batch=B, sharpness=tuple([1.0] * B))
+    plan = d.Plan(wB)
+    for k in ("tokens", "parent_slot", "n_kept"):
+        getattr(plan, k).copy_(torch.from_numpy(np.repeat(rr[k], B, axis=0)).cuda())
+    u = torch.rand((B, w1.T), device="cuda",
+                   generator=torch.Generator(device="cuda").manual_seed(9))
+    plan.accept_sample(tdev, tau, u)
+    torch.cuda.synchronize()
+    out = plan.out_tokens.cpu().numpy()
+
+    def sm(s):
+        x = target[0, s] / tau
+        e = np.exp(x - x.max())
+        return e / e.sum()
+
+    assert _chi2_ok(np.bincount(out[:, 0], minlength=w1.vocab), sm(0))
+    checked = 0
+    for c in range(1, n + 1):
+        if rr["parent_slot"][0, c] != 0:
+            continue
+        sel = out[:, 0] == rr["tokens"][0, c]
+        if sel.sum() >= 400:
+            assert _chi2_ok(np.bincount(out[sel, 1], minlength=w1.vocab), sm(c))
+            checked += 1
+    assert checked >= 1
+
+
 @pytest.mark.parametrize("name", ["tiny", "odd_vocab", "small_bf16"])
 def test_target_rows_past_n_kept_are_ignored(name):
     """Target rows s > n_kept are loaded before n_kept is known but never
-    used: NaN there changes no output bit."""
+    used: NaN there changes no output bit (greedy and sampled walks)."""
     r = _run(name)
     w, plan, inp = r["w"], r["plan"], r["inp"]
     n_kept = r["gpu_rr"]["n_kept"]
@@ -270,6 +408,37 @@ def test_target_rows_past_n_kept_are_ignored(name):
     torch.cuda.synchronize()
     for a, t in zip(ref, (plan.accept_len, plan.path_slots, plan.out_tokens)):
         assert torch.equal(a, t.cpu())
+    # the same for the sampled walk
+    u = to_dev(np.random.default_rng(2).random((w.batch, w.T), dtype=np.float32))
+    plan.accept_sample(td, 1.0, u)
+    torch.cuda.synchronize()
+    ref = [t.cpu().clone() for t in (plan.accept_len, plan.path_slots, plan.out_tokens)]
+    plan.accept_sample(poisoned, 1.0, u)
+    torch.cuda.synchronize()
+    for a, t in zip(ref, (plan.accept_len, plan.path_slots, plan.out_tokens)):
+        assert torch.equal(a, t.cpu())
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "f32_gqa", "max_vocab"])
+def test_accept_sample_unaligned_rows(name):
+    """Target rows with stride V + 1 (not 16-byte aligned: element loads)
+    give the same sampled walk, bonus included, as aligned rows."""
+    r = _run(name)
+    w, plan, inp = r["w"], r["plan"], r["inp"]
+    td = to_dev(inp["target"])
+    V = w.vocab
+    padded = torch.zeros((w.batch, w.T, V + 1), dtype=td.dtype, device="cuda")
+    padded[..., :V] = td
+    for seed in range(3):
+        u = to_dev(np.random.default_rng(seed).random((w.batch, w.T), dtype=np.float32))
+        plan.accept_sample(td, 0.7, u)
+        torch.cuda.synchronize()
+        ref = [t.cpu().clone() for t in (plan.accept_len, plan.path_slots,
+                                         plan.out_tokens)]
+        plan.accept_sample(padded[..., :V], 0.7, u)
+        torch.cuda.synchronize()
+        for a, t in zip(ref, (plan.accept_len, plan.path_slots, plan.out_tokens)):
+            assert torch.equal(a, t.cpu())
 
 
 @pytest.mark.parametrize("name", ["tiny", "small_bf16", "f32_gqa", "odd_vocab",
