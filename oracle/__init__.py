@@ -222,6 +222,34 @@ def accept_sample(w, target, tokens, parent_slot, n_kept, temperature,
                 margin=margin)
 
 
+def static_tree(w, root_tokens, draft, shape_parent, shape_rank):
+    """The fixed-shape tree (see etref_static_tree) on draft logits
+    [B][D][k][V]; shape_parent / shape_rank are [M + 1] with entry 0 (the
+    root) ignored.  Returns the rerank-style slot arrays."""
+    B, T = w.batch, w.T
+    if draft.strides[-1] != draft.itemsize:
+        raise ValueError("last axis must be contiguous")
+    es = draft.itemsize
+    bs, ls, rs = (draft.strides[0] // es, draft.strides[1] // es,
+                  draft.strides[2] // es)
+    sp, sr = _i32(shape_parent), _i32(shape_rank)
+    M = len(sp) - 1
+    out = dict(tokens=np.empty((B, T), np.int32),
+               parent_slot=np.empty((B, T), np.int32),
+               conf=np.empty((B, T), np.float32),
+               value=np.empty((B, T), np.float32),
+               n_kept=np.empty(B, np.int32))
+    rc = lib().etref_static_tree(
+        B, w.vocab, w.topk, w.depth, T, _DT[w.logits_dtype],
+        _p(_i32(root_tokens)), _p(draft), ctypes.c_int64(bs),
+        ctypes.c_int64(ls), ctypes.c_int64(rs), M, _p(sp), _p(sr),
+        _p(out["tokens"]), _p(out["parent_slot"]), _p(out["conf"]),
+        _p(out["value"]), _p(out["n_kept"]))
+    if rc != 0:
+        raise ValueError(f"etref_static_tree rejected the shape: {rc}")
+    return out
+
+
 def kv_commit(w, attn, prefix_len, path_slots, accept_len):
     """Commit the accepted paths to copies of the K/V caches (see
     etref_kv_commit); returns (k_cache, v_cache, prefix_len)."""

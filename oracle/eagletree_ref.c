@@ -628,6 +628,93 @@ int etref_accept_sample(int B, int T, int V, int D, int dtype,
   return 0;
 }
 
+/* ---------------------------------------------------------------------
+ * Static draft tree: the fixed-shape baseline the dynamic tree is compared
+ * with ([P2] "Watch the Budget Being Spent": an EAGLE-1-style fixed shape
+ * spends the same node budget; [P3] EAGLE: one static prior tree is used
+ * for every input).  The shape: nodes s = 1..M, parent sp[s] in [0, s)
+ * (0 = root), child rank sr[s] in [0, k), distinct among siblings,
+ * depth <= D.  Readings: at step l, row j of layer l-1 belongs to the j-th
+ * slot, in slot order, of depth l-1 with a child in the shape (at most k
+ * such slots); a node's children are its row's top-k by (logit desc, id
+ * asc) with conf and value exactly as in the draft step, and the shape
+ * keeps the child of rank sr[s].  Slot order is the shape's order.
+ * logits: element (b, l, j, v) at b*bstride + l*lstride + j*rstride + v.
+ * Outputs as etref_rerank (slot 0 the root; pad slots -1/-1/0/0), with
+ * n_kept[b] = M.  Returns -1 for a shape that breaks the rules above.
+ * ------------------------------------------------------------------- */
+int etref_static_tree(int B, int V, int k, int D, int T, int dtype,
+                      const int32_t* root_tokens, const void* logits,
+                      int64_t bstride, int64_t lstride, int64_t rstride,
+                      int M, const int32_t* sp, const int32_t* sr,
+                      int32_t* tokens, int32_t* parent_slot, float* conf,
+                      float* value, int32_t* n_kept) {
+  if (M < 0 || M > T - 1 || k < 1 || V < k) return -1;
+  int32_t* dep = (int32_t*)malloc(sizeof(int32_t) * (size_t)(M + 1));
+  int32_t* row = (int32_t*)malloc(sizeof(int32_t) * (size_t)(M + 1));
+  int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+  double* xs = (double*)malloc(sizeof(double) * (size_t)k);
+  unsigned char* taken = (unsigned char*)malloc((size_t)V);
+  if (!dep || !row || !ids || !xs || !taken) return -2;
+  int rc = 0;
+  /* depths, rank rules, and the row each expanded slot reads */
+  dep[0] = 0;
+  for (int s = 1; s <= M && rc == 0; ++s) {
+    if (sp[s] < 0 || sp[s] >= s || sr[s] < 0 || sr[s] >= k) rc = -1;
+    else dep[s] = dep[sp[s]] + 1;
+    if (rc == 0 && dep[s] > D) rc = -1;
+    for (int t = 1; t < s && rc == 0; ++t)
+      if (sp[t] == sp[s] && sr[t] == sr[s]) rc = -1;
+  }
+  for (int l = 0; l < D && rc == 0; ++l) {
+    int j = 0;
+    for (int s = 0; s <= M; ++s) {
+      if (dep[s] != l) continue;
+      int has_child = 0;
+      for (int c = s + 1; c <= M; ++c) has_child |= sp[c] == s;
+      row[s] = has_child ? j++ : -1;
+    }
+    if (j > k) rc = -1;
+  }
+  for (int b = 0; b < B && rc == 0; ++b) {
+    int32_t* tk = tokens + (int64_t)b * T;
+    int32_t* ps = parent_slot + (int64_t)b * T;
+    float* cf = conf + (int64_t)b * T;
+    float* vl = value + (int64_t)b * T;
+    tk[0] = root_tokens[b];
+    ps[0] = -1;
+    cf[0] = 1.0f;
+    vl[0] = 1.0f;
+    for (int s = 1; s <= M; ++s) {
+      const int p = sp[s];
+      const char* x = (const char*)logits +
+                      (b * bstride + dep[p] * lstride + row[p] * rstride) *
+                          (dtype == REF_F32 ? 4 : 2);
+      double m, sum;
+      ref_row_softmax(x, dtype, V, &m, &sum);
+      ref_row_topk(x, dtype, V, k, ids, xs, taken);
+      const float c = (float)(exp(xs[sr[s]] - m) / sum);
+      tk[s] = ids[sr[s]];
+      ps[s] = p;
+      cf[s] = c;
+      vl[s] = vl[p] * c;
+    }
+    for (int s = M + 1; s < T; ++s) {
+      tk[s] = -1;
+      ps[s] = -1;
+      cf[s] = 0.0f;
+      vl[s] = 0.0f;
+    }
+    n_kept[b] = M;
+  }
+  free(dep);
+  free(row);
+  free(ids);
+  free(xs);
+  free(taken);
+  return rc;
+}
+
 /* Threads the OpenMP loop above may use (1 without OpenMP). */
 int etref_num_threads(void) {
 #ifdef _OPENMP

@@ -138,3 +138,42 @@ def attention_inputs(w: Workload, seed: int | None = None) -> dict:
             out[name][b] = _normal(seed, comp, b, out[name].shape[1:],
                                    w.qkv_dtype)
     return out
+
+
+def static_shape(w: Workload, q0: float = 0.6, decay: float = 0.4):
+    """A fixed tree shape of w.budget_n nodes for the static-tree baseline:
+    nodes taken best first by the product, along their path, of a fixed
+    per-rank weight q_r = q0 * decay^r (rank r < k, depth <= D, at most k
+    nodes with children per depth); ties go to the earlier-created
+    candidate.  Returns (parent, rank), int32 [M + 1] in slot order (entry
+    0 is the root)."""
+    import heapq
+    k, D, N = w.topk, w.depth, w.budget_n
+    parent, rank, depth, weight = [-1], [-1], [0], [1.0]
+    expanded = [0] * (D + 1)      # nodes with a child, per depth
+    has_child = [False]
+    heap, made = [], 0
+
+    def offer(p):
+        nonlocal made
+        if depth[p] >= D:
+            return
+        for r in range(k):
+            heapq.heappush(heap, (-weight[p] * q0 * decay ** r, made, p, r))
+            made += 1
+
+    offer(0)
+    while heap and len(parent) - 1 < N:
+        _, _, p, r = heapq.heappop(heap)
+        if not has_child[p]:
+            if expanded[depth[p]] >= k:
+                continue
+            expanded[depth[p]] += 1
+            has_child[p] = True
+        parent.append(p)
+        rank.append(r)
+        depth.append(depth[p] + 1)
+        weight.append(weight[p] * q0 * decay ** r)
+        has_child.append(False)
+        offer(len(parent) - 1)
+    return np.array(parent, np.int32), np.array(rank, np.int32)

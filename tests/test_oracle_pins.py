@@ -702,6 +702,94 @@ def test_sampled_accept_zero_uniforms_take_first_child():
         assert acc["out_tokens"][0, L] == 0
 
 
+# ------------------------------------------------------------ static tree
+def _dynamic_shape(w, st, rr, b=0):
+    """(parent, rank) of the kept dynamic tree in slot order; a node's rank
+    among its parent's children comes from its pool index (children are
+    appended per frontier row in rank order)."""
+    n = int(rr["n_kept"][b])
+    P = int(st.count[b])
+    start = {}
+    for i in range(P):
+        start.setdefault(int(st.depth[b, i]), i)
+    slot_of = {}
+    order = sorted(range(P), key=lambda i: (-float(st.value[b, i]),
+                                            int(st.depth[b, i]),
+                                            int(st.token[b, i]), i))
+    for s_, i in enumerate(order[:n], start=1):
+        slot_of[i] = s_
+    parent, rank = [-1], [-1]
+    for s_, i in enumerate(order[:n], start=1):
+        par = int(st.parent[b, i])
+        parent.append(0 if par < 0 else slot_of[par])
+        rank.append((i - start[int(st.depth[b, i])]) % w.topk)
+    return np.array(parent, np.int32), np.array(rank, np.int32)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_static_tree_with_the_full_dynamic_shape_is_the_dynamic_tree(seed):
+    """With a budget that keeps the whole pool, the dynamic tree's own
+    shape, run as a static shape on the same logits, reads the same rows
+    (its expanded nodes are the dynamic frontiers, in the same order) and
+    must give the dynamic tree bit for bit: tokens, parents, conf, value."""
+    w = _small(vocab=300, topk=3, depth=3, threshold=0.0, sharpness=(1.5,))
+    w = w.with_(budget_n=w.pool_cap)
+    w, st, draft, roots = _random_tree(w, 300 + seed)
+    rr = oracle.rerank(w, st)
+    assert int(rr["n_kept"][0]) == w.pool_cap
+    p, r = _dynamic_shape(w, st, rr)
+    sr = oracle.static_tree(w, roots, draft, p, r)
+    for key in ("tokens", "parent_slot", "conf", "value", "n_kept"):
+        np.testing.assert_array_equal(sr[key], rr[key])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_static_chain_is_the_product_of_top1_confidences(dtype):
+    """A chain of rank-0 children reads row 0 of every layer: slot d holds
+    that row's argmax (lowest id on ties) with conf = its numpy fp64
+    softmax probability and value = the running fp32 product."""
+    w = _small(batch=2, vocab=500, topk=4, depth=5, budget_n=5,
+               logits_dtype=dtype, sharpness=(2.0, 0.9))
+    draft = gen.draft_logits(w)
+    roots = gen.root_tokens(w)
+    p = np.arange(-1, w.depth, dtype=np.int32)
+    r = np.zeros(w.depth + 1, np.int32)
+    sr = oracle.static_tree(w, roots, draft, p, r)
+    for b in range(w.batch):
+        val = np.float32(1.0)
+        for d in range(1, w.depth + 1):
+            row = _rows_of(draft[b, d - 1, 0], dtype).astype(np.float64)
+            tok = int(np.argmax(row))
+            conf = np.float32(_np_softmax64(row)[tok])
+            val = np.float32(val * conf)
+            assert sr["tokens"][b, d] == tok and sr["parent_slot"][b, d] == d - 1
+            assert abs(float(sr["conf"][b, d]) - float(conf)) <= 1e-6 * float(conf)
+            assert abs(float(sr["value"][b, d]) - float(val)) <= 1e-5 * float(val)
+
+
+def test_static_shape_rules_are_enforced():
+    """Rank out of range, a repeated sibling rank, a forward parent, depth
+    past D and more than k rows in one layer are all rejected."""
+    w = _small(vocab=64, topk=2, depth=2, budget_n=6)
+    draft, roots = gen.draft_logits(w), gen.root_tokens(w)
+    bad = [([-1, 0], [-1, 2]),                    # rank >= k
+           ([-1, 0, 0], [-1, 1, 1]),              # repeated sibling rank
+           ([-1, 2, 0], [-1, 0, 0]),              # parent after the node
+           ([-1, 0, 1, 2], [-1, 0, 0, 0])]        # depth 3 > D
+    for p, r in bad:
+        with pytest.raises(ValueError):
+            oracle.static_tree(w, roots, draft, np.array(p), np.array(r))
+    w3 = _small(vocab=64, topk=2, depth=3, budget_n=10)
+    d3, r3 = gen.draft_logits(w3), gen.root_tokens(w3)
+    # three depth-2 nodes with children: more than k = 2 rows in layer 2
+    p = [-1, 0, 0, 1, 1, 2, 3, 4, 5]
+    r = [-1, 0, 1, 0, 1, 0, 0, 0, 0]
+    with pytest.raises(ValueError):
+        oracle.static_tree(w3, r3, d3, np.array(p), np.array(r))
+    sr = oracle.static_tree(w3, r3, d3, np.array(p[:8]), np.array(r[:8]))
+    assert int(sr["n_kept"][0]) == 7
+
+
 # ---------------------------------------------------------------- generator
 def test_bf16_rounding_is_nearest_even():
     x = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, -2.5, 3.0e38],
