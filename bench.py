@@ -10,7 +10,9 @@ exceeds the 256 MB MALL and every cycle reads HBM.
 Prints one JSON line: cycles/s, the roofline of the dominant call
 (algorithmic bytes / its average duration, HIP events on the launch
 stream; a call is one or two back-to-back launches) and the CPU oracle
-timed on this host as a reported baseline.
+timed on this host as a reported baseline.  Beside the metric, timed
+after it: KV commit, sampled acceptance, and the fixed-shape tree build
+against the dynamic one with each tree's expected accepted tokens.
 """
 from __future__ import annotations
 
@@ -374,6 +376,31 @@ def main():
     uni = torch.rand((w.batch, w.T), device="cuda",
                      generator=torch.Generator(device="cuda").manual_seed(w.seed))
     sample_us = time_next(lambda: plan.accept_sample(ds0["target"], 1.0, uni, stream))
+    # Fixed-shape baseline against the dynamic tree on set 0's draft logits
+    # (a plan of its own): each build (D steps, then the slot gather or the
+    # rerank) timed as one call, and each tree's readout, the mean over
+    # sequences of the kept values' sum (expected accepted tokens).
+    splan = d.Plan(w)
+    shape_p, shape_r = gen.static_shape(w)
+    splan.set_static_shape(shape_p[1:], shape_r[1:])
+
+    def build(static):
+        for step in range(1, w.depth + 1):
+            if static:
+                splan.draft_step_static(step, ds0["roots"], ds0["draft"][:, step - 1], stream)
+            else:
+                splan.draft_step(step, ds0["roots"], ds0["draft"][:, step - 1], stream)
+        if static:
+            splan.static_tree(stream)
+        else:
+            splan.rerank(stream)
+
+    readout = {}
+    build_us = {}
+    for static in (True, False):
+        name = "static" if static else "dynamic"
+        build_us[name] = time_next(lambda: build(static))
+        readout[name] = round(float(splan.value[:, 1:].double().sum(1).mean()), 5)
     per_cycle_us = {n: acc[n] / K for n in names}
 
     # algorithmic bytes of the last cycle's shapes
@@ -455,7 +482,12 @@ def main():
         "per_call_us": {n: round(avg_us[n], 3) for n in names},
         "per_cycle_us": {n: round(per_cycle_us[n], 3) for n in names},
         "next_calls_us": {"kv_commit": round(commit_us, 3),
-                          "accept_sample": round(sample_us, 3)},
+                          "accept_sample": round(sample_us, 3),
+                          "static_tree_build": round(build_us["static"], 3),
+                          "dynamic_tree_build": round(build_us["dynamic"], 3)},
+        "tree_readout": {"expected_accepted_dynamic": readout["dynamic"],
+                         "expected_accepted_static": readout["static"],
+                         "static_nodes": int(len(shape_p) - 1)},
         "cpu_baseline": cpu,
         "gen_seconds": round(gen_s, 1),
     }

@@ -24,6 +24,7 @@ EXPORTS = ("et_plan_create", "et_plan_destroy", "et_workspace_bytes",
            "et_pool_capacity", "et_workspace_init", "et_draft_step",
            "et_rerank", "et_tree_mask", "et_tree_attention", "et_accept",
            "et_accept_sample", "et_kv_commit", "et_pool_export",
+           "et_set_static_shape", "et_draft_step_static", "et_static_tree",
            "et_last_error")
 
 
@@ -73,6 +74,9 @@ def lib():
             "et_accept_sample": ([vp, vp, vp, i64, i64, vp, vp, vp, f32, vp, vp, vp, vp,
                                   vp], ctypes.c_int),
             "et_kv_commit": ([vp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+            "et_set_static_shape": ([vp, vp, vp, i32], ctypes.c_int),
+            "et_draft_step_static": ([vp, vp, i32, vp, vp, i64, i64, vp, vp, vp], ctypes.c_int),
+            "et_static_tree": ([vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "et_pool_export": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "et_last_error": ([], ctypes.c_char_p),
         }
@@ -151,6 +155,33 @@ def et_draft_step(plan, ws, step, root_tokens, logits, next_tokens,
     _check(lib().et_draft_step(plan, _ptr(ws), int(step), _ptr(root_tokens),
                                _ptr(logits), bs, rs, _ptr(next_tokens),
                                _ptr(next_count), _stream(stream)))
+
+
+def et_draft_step_static(plan, ws, step, root_tokens, logits, next_tokens,
+                         next_count, stream=None):
+    bs, rs = _rows(logits)
+    _check(lib().et_draft_step_static(plan, _ptr(ws), int(step),
+                                      _ptr(root_tokens), _ptr(logits), bs, rs,
+                                      _ptr(next_tokens), _ptr(next_count),
+                                      _stream(stream)))
+
+
+def et_set_static_shape(plan, parent, rank):
+    """parent / rank: host int sequences for slots 1..n (parent slot 0 is
+    the root)."""
+    n = len(parent)
+    if len(rank) != n:
+        raise ValueError("parent and rank differ in length")
+    pa = (ctypes.c_int32 * max(n, 1))(*[int(x) for x in parent])
+    ra = (ctypes.c_int32 * max(n, 1))(*[int(x) for x in rank])
+    _check(lib().et_set_static_shape(plan, pa, ra, n))
+
+
+def et_static_tree(plan, ws, tokens, parent_slot, conf, value, n_kept,
+                   stream=None):
+    _check(lib().et_static_tree(plan, _ptr(ws), _ptr(tokens),
+                                _ptr(parent_slot), _ptr(conf), _ptr(value),
+                                _ptr(n_kept), _stream(stream)))
 
 
 def et_rerank(plan, ws, tokens, parent_slot, conf, value, n_kept,
@@ -268,6 +299,18 @@ class Plan:
     def rerank(self, stream=None):
         et_rerank(self.handle, self.ws, self.tokens, self.parent_slot,
                   self.conf, self.value, self.n_kept, stream)
+
+    def set_static_shape(self, parent, rank):
+        """Fixed shape for slots 1..n: parent slot and child rank each."""
+        et_set_static_shape(self.handle, parent, rank)
+
+    def draft_step_static(self, step, root_tokens, logits, stream=None):
+        et_draft_step_static(self.handle, self.ws, step, root_tokens, logits,
+                             self.next_tokens, self.next_count, stream)
+
+    def static_tree(self, stream=None):
+        et_static_tree(self.handle, self.ws, self.tokens, self.parent_slot,
+                       self.conf, self.value, self.n_kept, stream)
 
     def tree_mask(self, prefix_len, stream=None):
         et_tree_mask(self.handle, self.parent_slot, self.n_kept, prefix_len,

@@ -177,6 +177,7 @@ int et_plan_create(const et_config* cfg, et_plan_t* out) {
   et::Plan* p = new (std::nothrow) et::Plan();
   if (!p) return fail(ET_EINVAL, "%s: out of host memory", fn);
   p->cfg = c;
+  p->static_m = -1;
   p->B = c.batch;
   p->V = c.vocab;
   p->k = c.topk;
@@ -251,12 +252,12 @@ int et_workspace_init(et_plan_t plan, void* ws, et_stream_t stream) {
   return ET_OK;
 }
 
-int et_draft_step(et_plan_t plan, void* ws, int32_t step,
-                  const int32_t* root_tokens, const void* logits,
-                  int64_t batch_stride, int64_t row_stride,
-                  int32_t* next_tokens, int32_t* next_count,
-                  et_stream_t stream) {
-  const char* fn = "et_draft_step";
+namespace {
+
+int draft_step(const char* fn, et_plan_t plan, void* ws, int32_t step,
+               const int32_t* root_tokens, const void* logits,
+               int64_t batch_stride, int64_t row_stride, int32_t* next_tokens,
+               int32_t* next_count, et_stream_t stream, bool fixed) {
   CHECK_PTR(plan);
   CHECK_PTR(ws);
   CHECK_PTR(logits);
@@ -273,22 +274,134 @@ int et_draft_step(et_plan_t plan, void* ws, int32_t step,
     return fail(ET_EINVAL, "%s: negative batch_stride", fn);
   if (((uintptr_t)ws & 255u) != 0)
     return fail(ET_EINVAL, "%s: workspace not 256-byte aligned", fn);
-  if (step != 1 && (p.last_ws != ws || p.last_step != step - 1))
-    return fail(ET_ESTATE, "%s: step %d does not follow step %d on this "
-                "workspace", fn, step, p.last_step);
+  if (step != 1 && (p.last_ws != ws || p.last_step != step - 1 || p.last_fixed != fixed))
+    return fail(ET_ESTATE, "%s: step %d does not follow step %d of the same "
+                "policy on this workspace", fn, step, p.last_step);
+  if (fixed && p.static_m < 0)
+    return fail(ET_ESTATE, "%s: no fixed shape set (et_set_static_shape)", fn);
+  et::FixedFrontier ff;
+  if (fixed) {
+    ff.n = step < p.D ? p.static_nf[step + 1] : 0;
+    for (int i = 0; i < et::kMaxTopk; ++i) ff.ci[i] = p.static_next[step][i];
+  }
   const int per = p.ldt == ET_BF16 ? 8 : 4;
   const bool vec = aligned16(logits) && batch_stride % per == 0 &&
                    row_stride % per == 0 && p.V >= per;
   int rc = hip_status(
       et::launch_draft_step(p, et::draft_ws(p, ws), step, root_tokens, logits,
-                            batch_stride, row_stride, vec, next_tokens,
-                            next_count, (hipStream_t)stream),
+                            batch_stride, row_stride, vec, fixed ? &ff : nullptr,
+                            next_tokens, next_count, (hipStream_t)stream),
       fn);
   if (rc == ET_OK) {
     p.last_ws = ws;
     p.last_step = step;
+    p.last_fixed = fixed;
   }
   return rc;
+}
+
+}  // namespace
+
+int et_draft_step(et_plan_t plan, void* ws, int32_t step,
+                  const int32_t* root_tokens, const void* logits,
+                  int64_t batch_stride, int64_t row_stride,
+                  int32_t* next_tokens, int32_t* next_count,
+                  et_stream_t stream) {
+  return draft_step("et_draft_step", plan, ws, step, root_tokens, logits,
+                    batch_stride, row_stride, next_tokens, next_count, stream,
+                    false);
+}
+
+int et_draft_step_static(et_plan_t plan, void* ws, int32_t step,
+                         const int32_t* root_tokens, const void* logits,
+                         int64_t batch_stride, int64_t row_stride,
+                         int32_t* next_tokens, int32_t* next_count,
+                         et_stream_t stream) {
+  return draft_step("et_draft_step_static", plan, ws, step, root_tokens,
+                    logits, batch_stride, row_stride, next_tokens, next_count,
+                    stream, true);
+}
+
+int et_set_static_shape(et_plan_t plan, const int32_t* parent,
+                        const int32_t* rank, int32_t n_nodes) {
+  const char* fn = "et_set_static_shape";
+  CHECK_PTR(plan);
+  et::Plan& p = *as_plan(plan);
+  if (n_nodes < 0 || n_nodes > p.N)
+    return fail(ET_EINVAL, "%s: %d nodes outside 0..%d", fn, n_nodes, p.N);
+  if (n_nodes > 0) {
+    CHECK_PTR(parent);
+    CHECK_PTR(rank);
+  }
+  // slot s = node s - 1 of the arrays; slot 0 is the root
+  int dep[et::kMaxBudget + 1], row[et::kMaxBudget + 1];
+  bool has_child[et::kMaxBudget + 1] = {};
+  dep[0] = 0;
+  for (int s = 1; s <= n_nodes; ++s) {
+    const int ps = parent[s - 1], r = rank[s - 1];
+    if (ps < 0 || ps >= s)
+      return fail(ET_EINVAL, "%s: slot %d: parent %d not an earlier slot", fn, s, ps);
+    if (r < 0 || r >= p.k)
+      return fail(ET_EINVAL, "%s: slot %d: rank %d outside 0..%d", fn, s, r, p.k - 1);
+    dep[s] = dep[ps] + 1;
+    if (dep[s] > p.D)
+      return fail(ET_EINVAL, "%s: slot %d: depth %d > %d", fn, s, dep[s], p.D);
+    for (int t = 1; t < s; ++t)
+      if (parent[t - 1] == ps && rank[t - 1] == r)
+        return fail(ET_EINVAL, "%s: slots %d and %d: same rank under one parent", fn, t, s);
+    has_child[ps] = true;
+  }
+  // rows of each step: the slots of the layer above with a child, in slot
+  // order (at most k)
+  int nf[et::kMaxDepth + 2] = {};
+  for (int s = 0; s <= n_nodes; ++s) {
+    row[s] = -1;
+    if (!has_child[s]) continue;
+    const int l = dep[s] + 1;
+    if (nf[l] == p.k)
+      return fail(ET_EINVAL, "%s: more than %d slots of depth %d have children", fn,
+                  p.k, dep[s]);
+    row[s] = nf[l]++;
+  }
+  int base[et::kMaxDepth + 2] = {};
+  for (int l = 2; l <= p.D; ++l) base[l] = base[l - 1] + nf[l - 1] * p.k;
+  for (int l = 0; l <= p.D; ++l)
+    for (int i = 0; i < et::kMaxTopk; ++i) p.static_next[l][i] = -1;
+  for (int s = 1; s <= n_nodes; ++s) {
+    const int ps = parent[s - 1], l = dep[s];
+    const int ci = row[ps] * p.k + rank[s - 1];  // child index within step l
+    p.static_slot[s] = (base[l] + ci) | (ps << 16);
+    if (has_child[s]) p.static_next[l][row[s]] = ci;
+  }
+  for (int l = 0; l <= p.D + 1; ++l) p.static_nf[l] = nf[l];
+  p.static_m = n_nodes;
+  return ET_OK;
+}
+
+int et_static_tree(et_plan_t plan, void* ws, int32_t* tokens,
+                   int32_t* parent_slot, float* conf, float* value,
+                   int32_t* n_kept, et_stream_t stream) {
+  const char* fn = "et_static_tree";
+  CHECK_PTR(plan);
+  CHECK_PTR(ws);
+  CHECK_PTR(tokens);
+  CHECK_PTR(parent_slot);
+  CHECK_PTR(conf);
+  CHECK_PTR(value);
+  CHECK_PTR(n_kept);
+  et::Plan& p = *as_plan(plan);
+  if (p.static_m < 0)
+    return fail(ET_ESTATE, "%s: no fixed shape set (et_set_static_shape)", fn);
+  if (p.last_ws != ws || p.last_step != p.D || !p.last_fixed)
+    return fail(ET_ESTATE, "%s: the fixed-shape tree is not complete (last "
+                "step %d of %d on this workspace)", fn, p.last_step, p.D);
+  et::FixedSlots fs;
+  fs.m = p.static_m;
+  for (int s = 0; s <= et::kMaxBudget; ++s) fs.slot[s] = s <= p.static_m ? p.static_slot[s] : 0;
+  return hip_status(et::launch_static_tree(p, et::draft_ws(p, ws), fs, tokens,
+                                           parent_slot, conf, value, n_kept,
+                                           (hipStream_t)stream),
+                    fn);
 }
 
 int et_rerank(et_plan_t plan, void* ws, int32_t* tokens, int32_t* parent_slot,

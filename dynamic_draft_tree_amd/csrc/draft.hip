@@ -297,8 +297,11 @@ __device__ __forceinline__ void empty_frontier(const DraftArgs& a, int b) {
 // With many short lists (64 per row) four keys per list almost always
 // hold every candidate; with 16 lists per row eight are needed.
 constexpr int kMergeWaves = 4;
-template <bool BF16, int LPLM, int KST>
-__device__ __forceinline__ void merge_sequence(const DraftArgs& a, int b) {
+// FIXED: the next frontier comes from a fixed shape (fx) instead of the
+// children's values.
+template <bool BF16, int LPLM, int KST, bool FIXED>
+__device__ __forceinline__ void merge_sequence(const DraftArgs& a, const FixedFrontier* fx,
+                                               int b) {
   constexpr int kLPL = LPLM;
   constexpr int kStage = KST;
   constexpr float kLog2e = 1.4426950408889634f;
@@ -506,69 +509,88 @@ __device__ __forceinline__ void merge_sequence(const DraftArgs& a, int b) {
   // and the top k, in value order, become the frontier (those below the
   // expansion threshold, a suffix, stay unexpanded).
   int nf = 0;
-  if (a.step < a.D) {
-    uint64_t ck[4];
-    uint32_t hmax = 0;
+  if constexpr (FIXED) {
+    // Fixed shape: next-frontier node i is child fx->ci[i] of this step.
+    bool kept = false;
+    if (lane < k) {
+      int ci = -1;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = lane + 64 * u;
-      ck[u] = t < n_new ? s_aux[t] : 0;
-      const uint32_t hi = (uint32_t)(ck[u] >> 32);
-      hmax = hi > hmax ? hi : hmax;
+      for (int i = 0; i < kMaxTopk; ++i)
+        if (lane == i && i < fx->n) ci = fx->ci[i];
+      kept = ci >= 0 && ci < n_new;
+      const uint64_t key = kept ? s_aux[ci] : 0;
+      const int fb = (cur * a.B + b) * k;
+      a.ws.frontier[fb + lane] = kept ? pool_index_of(key) : -1;
+      a.ws.frontier_val[fb + lane] = kept ? pool_value_of(key) : 0.0f;
+      a.next_tokens[(int64_t)b * k + lane] =
+          kept ? (int)((1u << 18) - 1u - (uint32_t)((key >> 12) & 0x3FFFFu)) : -1;
     }
-    const uint32_t T = wave_kth_largest_u32(hmax, k, 0);
-    int cq = 0;
+    nf = __popcll(__ballot(kept));
+  } else {
+    if (a.step < a.D) {
+      uint64_t ck[4];
+      uint32_t hmax = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) cq += (ck[u] != 0 && (uint32_t)(ck[u] >> 32) >= T) ? 1 : 0;
-    int n;
-    const int off = wave_excl_prefix_small(cq, &n);
-    uint64_t* wbuf = &s_fb[0];
-    const int fb = (cur * a.B + b) * k;
-    if (n <= kWaveCap) {
-      int o = off;
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (ck[u] != 0 && (uint32_t)(ck[u] >> 32) >= T) wbuf[o++] = ck[u];
-      wave_lds_fence();
-      bool kept = false;
-      if (lane < n) {
-        const uint64_t me = wbuf[lane];
-        int rank = 0;
-#pragma unroll 8
-        for (int q = 0; q < n; ++q) rank += wbuf[q] > me;
-        if (rank < k) {
-          kept = !(pool_value_of(me) < a.thr);
-          a.ws.frontier[fb + rank] = kept ? pool_index_of(me) : -1;
-          a.ws.frontier_val[fb + rank] = pool_value_of(me);
-          // token field of the pool key: bits 12..29 hold 2^18 - 1 - token
-          a.next_tokens[(int64_t)b * k + rank] =
-              kept ? (int)((1u << 18) - 1u - (uint32_t)((me >> 12) & 0x3FFFFu)) : -1;
-        }
+      for (int u = 0; u < 4; ++u) {
+        const int t = lane + 64 * u;
+        ck[u] = t < n_new ? s_aux[t] : 0;
+        const uint32_t hi = (uint32_t)(ck[u] >> 32);
+        hmax = hi > hmax ? hi : hmax;
       }
-      nf = __popcll(__ballot(kept));
-    } else {
-      // Many equal values: k rounds of wave maximum.
-      uint64_t prevk = ~0ull;
-      for (int r = 0; r < k; ++r) {
-        uint64_t best = 0;
+      const uint32_t T = wave_kth_largest_u32(hmax, k, 0);
+      int cq = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) cq += (ck[u] != 0 && (uint32_t)(ck[u] >> 32) >= T) ? 1 : 0;
+      int n;
+      const int off = wave_excl_prefix_small(cq, &n);
+      uint64_t* wbuf = &s_fb[0];
+      const int fb = (cur * a.B + b) * k;
+      if (n <= kWaveCap) {
+        int o = off;
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          if (ck[u] < prevk && ck[u] > best) best = ck[u];
-        const uint64_t w = wave_max_u64(best);
-        const bool kept = w != 0 && !(pool_value_of(w) < a.thr);
-        if (lane == 0) {
-          a.ws.frontier[fb + r] = kept ? pool_index_of(w) : -1;
-          a.ws.frontier_val[fb + r] = pool_value_of(w);
-          a.next_tokens[(int64_t)b * k + r] =
-              kept ? (int)((1u << 18) - 1u - (uint32_t)((w >> 12) & 0x3FFFFu)) : -1;
+          if (ck[u] != 0 && (uint32_t)(ck[u] >> 32) >= T) wbuf[o++] = ck[u];
+        wave_lds_fence();
+        bool kept = false;
+        if (lane < n) {
+          const uint64_t me = wbuf[lane];
+          int rank = 0;
+#pragma unroll 8
+          for (int q = 0; q < n; ++q) rank += wbuf[q] > me;
+          if (rank < k) {
+            kept = !(pool_value_of(me) < a.thr);
+            a.ws.frontier[fb + rank] = kept ? pool_index_of(me) : -1;
+            a.ws.frontier_val[fb + rank] = pool_value_of(me);
+            // token field of the pool key: bits 12..29 hold 2^18 - 1 - token
+            a.next_tokens[(int64_t)b * k + rank] =
+                kept ? (int)((1u << 18) - 1u - (uint32_t)((me >> 12) & 0x3FFFFu)) : -1;
+          }
         }
-        nf += kept ? 1 : 0;
-        prevk = w;
+        nf = __popcll(__ballot(kept));
+      } else {
+        // Many equal values: k rounds of wave maximum.
+        uint64_t prevk = ~0ull;
+        for (int r = 0; r < k; ++r) {
+          uint64_t best = 0;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (ck[u] < prevk && ck[u] > best) best = ck[u];
+          const uint64_t w = wave_max_u64(best);
+          const bool kept = w != 0 && !(pool_value_of(w) < a.thr);
+          if (lane == 0) {
+            a.ws.frontier[fb + r] = kept ? pool_index_of(w) : -1;
+            a.ws.frontier_val[fb + r] = pool_value_of(w);
+            a.next_tokens[(int64_t)b * k + r] =
+                kept ? (int)((1u << 18) - 1u - (uint32_t)((w >> 12) & 0x3FFFFu)) : -1;
+          }
+          nf += kept ? 1 : 0;
+          prevk = w;
+        }
       }
+    } else if (lane < k) {
+      a.ws.frontier[(cur * a.B + b) * k + lane] = -1;
+      a.next_tokens[(int64_t)b * k + lane] = -1;
     }
-  } else if (lane < k) {
-    a.ws.frontier[(cur * a.B + b) * k + lane] = -1;
-    a.next_tokens[(int64_t)b * k + lane] = -1;
   }
   if (lane == 0) {
     a.ws.frontier_count[cur * a.B + b] = nf;
@@ -602,14 +624,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? 3 : 1
 // Merge launch: one block per sequence.
 template <bool BF16, int LPLM, int KST>
 __global__ __launch_bounds__(kMergeWaves * 64) void draft_merge_kernel(DraftArgs a) {
-  merge_sequence<BF16, LPLM, KST>(a, blockIdx.x);
+  merge_sequence<BF16, LPLM, KST, false>(a, nullptr, blockIdx.x);
+}
+template <bool BF16, int LPLM, int KST>
+__global__ __launch_bounds__(kMergeWaves * 64) void draft_merge_fixed_kernel(DraftArgs a,
+                                                                            FixedFrontier fx) {
+  merge_sequence<BF16, LPLM, KST, true>(a, &fx, blockIdx.x);
 }
 
 hipError_t launch_draft_step(const Plan& p, const DraftWs& w, int step,
                              const int32_t* root_tokens, const void* logits,
                              int64_t bstride, int64_t rstride, bool vec,
-                             int32_t* next_tokens, int32_t* next_count,
-                             hipStream_t s) {
+                             const FixedFrontier* fixed, int32_t* next_tokens,
+                             int32_t* next_count, hipStream_t s) {
   DraftArgs a;
   a.ws = w;
   a.logits = logits;
@@ -646,10 +673,16 @@ hipError_t launch_draft_step(const Plan& p, const DraftWs& w, int step,
   int RW = 1;
   while (kMergeWaves * RW < p.k) RW <<= 1;
   const bool many = a.parts > 64 / RW;
-  if (bf && many) draft_merge_kernel<true, 4, 4><<<p.B, kMergeWaves * 64, 0, s>>>(a);
-  else if (bf) draft_merge_kernel<true, 1, 8><<<p.B, kMergeWaves * 64, 0, s>>>(a);
-  else if (many) draft_merge_kernel<false, 4, 4><<<p.B, kMergeWaves * 64, 0, s>>>(a);
-  else draft_merge_kernel<false, 1, 8><<<p.B, kMergeWaves * 64, 0, s>>>(a);
+#define ET_MERGE(BF, L, K)                                                               \
+  do {                                                                                   \
+    if (fixed) draft_merge_fixed_kernel<BF, L, K><<<p.B, kMergeWaves * 64, 0, s>>>(a, *fixed); \
+    else draft_merge_kernel<BF, L, K><<<p.B, kMergeWaves * 64, 0, s>>>(a);               \
+  } while (0)
+  if (bf && many) ET_MERGE(true, 4, 4);
+  else if (bf) ET_MERGE(true, 1, 8);
+  else if (many) ET_MERGE(false, 4, 4);
+  else ET_MERGE(false, 1, 8);
+#undef ET_MERGE
   return hipGetLastError();
 }
 

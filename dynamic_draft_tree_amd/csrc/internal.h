@@ -97,6 +97,25 @@ struct Plan {
   // call-order check
   const void* last_ws;
   int last_step;
+  bool last_fixed;        // the steps so far followed the fixed shape
+  // fixed tree shape (et_set_static_shape); static_m < 0: none
+  int static_m;
+  int static_nf[kMaxDepth + 2];                  // frontier rows at step l
+  int32_t static_next[kMaxDepth + 1][kMaxTopk];  // step l: child j * k + r of each next-frontier node
+  int32_t static_slot[kMaxBudget + 1];           // slot s >= 1: pool index | parent slot << 16
+};
+
+// The next frontier of one step under a fixed shape: node i is child ci[i]
+// (j * k + r: rank r of the step's row j), for i < n.
+struct FixedFrontier {
+  int n;
+  int32_t ci[kMaxTopk];
+};
+// A fixed tree's slots: slot s >= 1 is pool node slot[s] & 0xFFFF with
+// parent slot slot[s] >> 16, for s <= m.
+struct FixedSlots {
+  int m;
+  int32_t slot[kMaxBudget + 1];
 };
 
 DraftWs draft_ws(const Plan& p, void* ws);
@@ -107,11 +126,14 @@ AttnWs attn_ws(const Plan& p, void* ws);
 hipError_t launch_draft_step(const Plan& p, const DraftWs& w, int step,
                              const int32_t* root_tokens, const void* logits,
                              int64_t bstride, int64_t rstride, bool vec,
-                             int32_t* next_tokens, int32_t* next_count,
-                             hipStream_t s);
+                             const FixedFrontier* fixed, int32_t* next_tokens,
+                             int32_t* next_count, hipStream_t s);
 hipError_t launch_rerank(const Plan& p, const DraftWs& w, int32_t* tokens,
                          int32_t* parent_slot, float* conf, float* value,
                          int32_t* n_kept, hipStream_t s);
+hipError_t launch_static_tree(const Plan& p, const DraftWs& w, const FixedSlots& fs,
+                              int32_t* tokens, int32_t* parent_slot, float* conf,
+                              float* value, int32_t* n_kept, hipStream_t s);
 hipError_t launch_tree_mask(const Plan& p, const int32_t* parent_slot,
                             const int32_t* n_kept, const int32_t* prefix_len,
                             uint64_t* mask, int32_t* depth, int32_t* pos,

@@ -197,6 +197,46 @@ hipError_t launch_rerank(const Plan& p, const DraftWs& w, int32_t* tokens,
   return hipGetLastError();
 }
 
+// Fixed-shape tree (the static baseline): slot s >= 1 is a given pool
+// node with a given parent slot; one thread per slot gathers the node.
+// Slot 0 is the root (value 1); slots past the shape are pads, as rerank
+// writes them.
+__global__ __launch_bounds__(256) void static_tree_kernel(
+    DraftWs ws, FixedSlots fs, int32_t* tokens, int32_t* parent_slot,
+    float* conf, float* value, int32_t* n_kept, int T, int cap) {
+  const int b = blockIdx.x;
+  for (int s = threadIdx.x; s < T; s += blockDim.x) {
+    int tok = -1, par = -1;
+    float c = 0.0f, v = 0.0f;
+    if (s == 0) {
+      tok = ws.root_token[b];
+      c = v = 1.0f;
+    } else if (s <= fs.m) {
+      const int e = fs.slot[s];
+      const int pi = min(e & 0xFFFF, cap - 1);
+      const int64_t g = (int64_t)b * cap + pi;
+      tok = ws.pool_token[g];
+      par = e >> 16;
+      c = ws.pool_conf[g];
+      v = ws.pool_value[g];
+    }
+    const int64_t o = (int64_t)b * T + s;
+    tokens[o] = tok;
+    parent_slot[o] = par;
+    conf[o] = c;
+    value[o] = v;
+  }
+  if (threadIdx.x == 0) n_kept[b] = fs.m;
+}
+
+hipError_t launch_static_tree(const Plan& p, const DraftWs& w, const FixedSlots& fs,
+                              int32_t* tokens, int32_t* parent_slot, float* conf,
+                              float* value, int32_t* n_kept, hipStream_t s) {
+  static_tree_kernel<<<p.B, 256, 0, s>>>(w, fs, tokens, parent_slot, conf, value,
+                                         n_kept, p.T, p.cap);
+  return hipGetLastError();
+}
+
 // One thread per slot: walk the parent pointers (staged in LDS) to the root.
 __global__ __launch_bounds__(256) void tree_mask_kernel(
     const int32_t* parent_slot, const int32_t* n_kept,

@@ -24,6 +24,8 @@
  *     et_accept                      -- greedy longest accepted path
  *       (or et_accept_sample           -- ratio tests at temperature > 0)
  *     et_kv_commit                   -- append the accepted path's K/V
+ * A fixed-shape baseline replaces the first two with et_draft_step_static
+ * x D and et_static_tree (after et_set_static_shape).
  * Between draft steps the caller runs its draft model on `next_tokens`
  * and hands the resulting vocab logits to the next step.
  *
@@ -249,6 +251,43 @@ int et_accept_sample(et_plan_t plan, void* ws, const void* target_logits,
                      const float* uniforms, int32_t* accept_len,
                      int32_t* path_slots, int32_t* out_tokens,
                      et_stream_t stream);
+
+/* Static (fixed-shape) tree: the baseline the dynamic tree is compared
+ * with ([P2] "Watch the Budget Being Spent": an EAGLE-1-style fixed shape
+ * spends the same node budget on every context; [P3] EAGLE: one static
+ * prior tree for every input).  Readout of either tree: the sum of the
+ * kept values, the expected number of accepted tokens ([P2] value
+ * equation).
+ *
+ * et_set_static_shape stores a shape in the plan (host only, no device
+ * work): slot s = 1 .. n_nodes has parent slot parent[s - 1] (0 = root,
+ * earlier slots only) and child rank rank[s - 1] in 0 .. topk - 1
+ * (distinct among siblings), depth <= depth, n_nodes <= budget_n, and at
+ * most topk slots of one depth have children.  ET_EINVAL otherwise (the
+ * plan keeps its previous shape).
+ *
+ * et_draft_step_static is et_draft_step with the next frontier taken from
+ * the shape instead of by value (no threshold): at step l the rows belong,
+ * in slot order, to the shape's slots of depth l - 1 that have children;
+ * each row's top-k children, conf and value are formed as in
+ * et_draft_step.  Same arguments, layouts and call order (steps 1..D on
+ * one workspace, all of the same policy); ET_ESTATE without a shape.
+ *
+ * et_static_tree (after step D of et_draft_step_static) writes the shape's
+ * slots in the layout of et_rerank: slot 0 the root (conf = value = 1),
+ * slot s the kept child, parent_slot from the shape; n_kept[b] = n_nodes;
+ * pad slots token -1, parent -1, conf 0, value 0.  The result feeds
+ * et_tree_mask, et_tree_attention and the accept calls unchanged. */
+int et_set_static_shape(et_plan_t plan, const int32_t* parent,
+                        const int32_t* rank, int32_t n_nodes);
+int et_draft_step_static(et_plan_t plan, void* ws, int32_t step,
+                         const int32_t* root_tokens, const void* logits,
+                         int64_t batch_stride, int64_t row_stride,
+                         int32_t* next_tokens, int32_t* next_count,
+                         et_stream_t stream);
+int et_static_tree(et_plan_t plan, void* ws, int32_t* tokens,
+                   int32_t* parent_slot, float* conf, float* value,
+                   int32_t* n_kept, et_stream_t stream);
 
 /* Commit the verified path to the KV cache (the step after acceptance:
  * [P1] s2.1, the accepted tokens extend the sequence in path order; the

@@ -118,6 +118,19 @@ def test_calls_validate_before_launch():
                               nul, fake, fake, fake, nul) == binding.ET_EINVAL
     assert L.et_accept_sample(h, fake, fake, 0, 1000, fake, fake, fake, f(1.0),
                               fake, fake, fake, fake, nul) == binding.ET_EINVAL
+    # fixed shapes: tiny has topk 2, depth 3, budget 8
+    i32a = lambda xs: (ctypes.c_int32 * max(len(xs), 1))(*xs)
+    for par, rk in (([1], [0]), ([0], [2]), ([0, 0], [1, 1]),
+                    ([0, 1, 2, 3], [0, 0, 0, 0]),
+                    ([0, 0, 1, 1, 2, 3, 4, 5], [0, 1, 0, 1, 0, 0, 0, 0])):
+        assert L.et_set_static_shape(h, i32a(par), i32a(rk),
+                                     len(par)) == binding.ET_EINVAL, (par, rk)
+    assert L.et_draft_step_static(h, fake, 1, fake, fake, 1024, 1024, fake,
+                                  fake, nul) == binding.ET_ESTATE
+    assert b"shape" in L.et_last_error()
+    assert L.et_set_static_shape(h, i32a([0, 0, 1]), i32a([0, 1, 0]), 3) == 0
+    assert L.et_static_tree(h, fake, fake, fake, fake, fake, fake,
+                            nul) == binding.ET_ESTATE
     for bad in (0.0, -1.0, 1e-40, float("nan"), float("inf")):
         assert L.et_accept_sample(h, fake, fake, 0, 1024, fake, fake, fake,
                                   f(bad), fake, fake, fake, fake,

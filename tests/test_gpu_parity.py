@@ -321,6 +321,88 @@ def test_accept_sample_parity(name):
     print(f"{name}: {cases} sampled-accept cases, {near}/{total} near-ties")
 
 
+STATIC = ["tiny", "chain_k1", "small_bf16", "odd_vocab", "wide_w3", "max_pool",
+          "wide_f32", "max_vocab", "f32_gqa", "vicuna7b_flat", "llama8b",
+          "llama8b_b64", "llama70b_b8"]
+
+
+@pytest.mark.parametrize("name", STATIC)
+def test_static_tree_exact(name):
+    """Fixed-shape tree (the static baseline): D fixed-frontier draft steps
+    and the slot gather against the oracle on the same logits; ids and
+    topology bit-exact, conf and value within 1e-5 relative.  Prints the
+    readout: mean kept-value sum of the static and the dynamic tree."""
+    r = _run(name)
+    w, inp, dev = r["w"], r["inp"], r["dev"]
+    d = _lib()
+    plan = d.Plan(w)
+    p, rk = gen.static_shape(w)
+    plan.set_static_shape(p[1:], rk[1:])
+    for step in range(1, w.depth + 1):
+        plan.draft_step_static(step, dev["root_tokens"], dev["draft"][:, step - 1])
+    plan.static_tree()
+    torch.cuda.synchronize()
+    ref = oracle.static_tree(w, inp["root_tokens"], inp["draft"], p, rk)
+    for key in ("tokens", "parent_slot", "n_kept"):
+        np.testing.assert_array_equal(getattr(plan, key).cpu().numpy(), ref[key])
+    for key in ("conf", "value"):
+        g = getattr(plan, key).cpu().numpy().astype(np.float64)
+        e = ref[key].astype(np.float64)
+        assert (np.abs(g - e) <= 1e-5 * np.abs(e) + 1e-30).all(), key
+    dyn = r["gpu_rr"]["value"][:, 1:].astype(np.float64).sum(1).mean()
+    sta = plan.value.cpu().numpy()[:, 1:].astype(np.float64).sum(1).mean()
+    print(f"{name}: readout dynamic {dyn:.4f} static {sta:.4f}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "small_bf16", "llama8b"])
+def test_static_tree_feeds_the_cycle(name):
+    """The fixed-shape tree goes through mask and greedy accept like the
+    dynamic one: both equal the oracle's on the oracle's static tree."""
+    r = _run(name)
+    w, inp, dev = r["w"], r["inp"], r["dev"]
+    d = _lib()
+    plan = d.Plan(w)
+    p, rk = gen.static_shape(w)
+    plan.set_static_shape(p[1:], rk[1:])
+    for step in range(1, w.depth + 1):
+        plan.draft_step_static(step, dev["root_tokens"], dev["draft"][:, step - 1])
+    plan.static_tree()
+    plan.tree_mask(dev["prefix_len"])
+    ref = oracle.static_tree(w, inp["root_tokens"], inp["draft"], p, rk)
+    rng = np.random.default_rng(5)
+    planted = random_path_targets(w, ref, rng, hit=1.0)
+    tgt = gen.target_logits(w, planted=planted, boost=300.0)
+    plan.accept(to_dev(tgt))
+    torch.cuda.synchronize()
+    mk = oracle.tree_mask(w, ref["parent_slot"], ref["n_kept"], inp["prefix_len"])
+    np.testing.assert_array_equal(plan.mask.cpu().numpy().view(np.uint64), mk["mask"])
+    acc = oracle.accept(w, tgt, ref["tokens"], ref["parent_slot"], ref["n_kept"])
+    np.testing.assert_array_equal(plan.accept_len.cpu().numpy(), acc["accept_len"])
+    np.testing.assert_array_equal(plan.out_tokens.cpu().numpy(), acc["out_tokens"])
+    assert (acc["accept_len"] > 0).any()
+
+
+def test_static_and_dynamic_steps_do_not_mix():
+    """A dynamic step after fixed-shape steps (or the reverse) on one
+    workspace is refused, and et_static_tree needs a complete fixed build."""
+    d = _lib()
+    w = VARIANTS["tiny"]
+    inp = make_inputs(w)
+    dev = dev_inputs(inp)
+    plan = d.Plan(w)
+    p, rk = gen.static_shape(w)
+    plan.set_static_shape(p[1:], rk[1:])
+    plan.draft_step_static(1, dev["root_tokens"], dev["draft"][:, 0])
+    with pytest.raises(d.EtError):
+        plan.draft_step(2, dev["root_tokens"], dev["draft"][:, 1])
+    with pytest.raises(d.EtError):
+        plan.static_tree()
+    plan.draft_step(1, dev["root_tokens"], dev["draft"][:, 0])
+    with pytest.raises(d.EtError):
+        plan.draft_step_static(2, dev["root_tokens"], dev["draft"][:, 1])
+    torch.cuda.synchronize()
+
+
 def _chi2_ok(counts, probs, alpha=1e-4):
     """Pearson chi-square of counts against probs (bins expecting < 5
     pooled)."""
