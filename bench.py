@@ -148,6 +148,10 @@ def parse():
                          "one HIP graph per input set")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the CPU oracle baseline (0 = skip)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="leave out the calls measured beside the cycle (KV "
+                         "commit, sampled acceptance, the two tree builds), "
+                         "so a counter run sees only the cycle's dispatches")
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets to rotate (0 = enough to pass the MALL)")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -347,60 +351,63 @@ def main():
     # Sampled acceptance (temperature 1) of the last cycle's tree on set
     # 0's targets, in place of the greedy walk.  Each call is timed on its
     # own, 20 times, the GPU held as above; the median is reported.
-    def time_next(call, before=None):
-        torch.cuda.synchronize()
-        torch.cuda._sleep(int(hold_ms * spin_per_ms))
-        ev = []
-        for _ in range(20):
-            if before is not None:
-                before()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            call()
-            e1.record(stream)
-            ev.append((e0, e1))
-        torch.cuda.synchronize()
-        return float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+    commit_us = sample_us = None
+    build_us, readout, shape_p = {}, {}, []
+    if not args.no_extras:
+        def time_next(call, before=None):
+            torch.cuda.synchronize()
+            torch.cuda._sleep(int(hold_ms * spin_per_ms))
+            ev = []
+            for _ in range(20):
+                if before is not None:
+                    before()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                call()
+                e1.record(stream)
+                ev.append((e0, e1))
+            torch.cuda.synchronize()
+            return float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
 
-    ds0 = sets[0]
-    kc = ds0["attn"]["k_cache"].clone()
-    vc = ds0["attn"]["v_cache"].clone()
-    plen0 = torch.clamp(ds0["prefix"], max=w.prefix_cap - w.depth - 1)
-    plen = plen0.clone()
-    commit_us = time_next(
-        lambda: plan.kv_commit(kc, vc, ds0["attn"]["k_tree"], ds0["attn"]["v_tree"],
-                               plen, stream),
-        lambda: plen.copy_(plen0))
-    del kc, vc
-    uni = torch.rand((w.batch, w.T), device="cuda",
-                     generator=torch.Generator(device="cuda").manual_seed(w.seed))
-    sample_us = time_next(lambda: plan.accept_sample(ds0["target"], 1.0, uni, stream))
-    # Fixed-shape baseline against the dynamic tree on set 0's draft logits
-    # (a plan of its own): each build (D steps, then the slot gather or the
-    # rerank) timed as one call, and each tree's readout, the mean over
-    # sequences of the kept values' sum (expected accepted tokens).
-    splan = d.Plan(w)
-    shape_p, shape_r = gen.static_shape(w)
-    splan.set_static_shape(shape_p[1:], shape_r[1:])
+        ds0 = sets[0]
+        kc = ds0["attn"]["k_cache"].clone()
+        vc = ds0["attn"]["v_cache"].clone()
+        plen0 = torch.clamp(ds0["prefix"], max=w.prefix_cap - w.depth - 1)
+        plen = plen0.clone()
+        commit_us = time_next(
+            lambda: plan.kv_commit(kc, vc, ds0["attn"]["k_tree"], ds0["attn"]["v_tree"],
+                                   plen, stream),
+            lambda: plen.copy_(plen0))
+        del kc, vc
+        uni = torch.rand((w.batch, w.T), device="cuda",
+                         generator=torch.Generator(device="cuda").manual_seed(w.seed))
+        sample_us = time_next(lambda: plan.accept_sample(ds0["target"], 1.0, uni, stream))
+        # Fixed-shape baseline against the dynamic tree on set 0's draft logits
+        # (a plan of its own): each build (D steps, then the slot gather or the
+        # rerank) timed as one call, and each tree's readout, the mean over
+        # sequences of the kept values' sum (expected accepted tokens).
+        splan = d.Plan(w)
+        shape_p, shape_r = gen.static_shape(w)
+        splan.set_static_shape(shape_p[1:], shape_r[1:])
 
-    def build(static):
-        for step in range(1, w.depth + 1):
+        def build(static):
+            for step in range(1, w.depth + 1):
+                if static:
+                    splan.draft_step_static(step, ds0["roots"], ds0["draft"][:, step - 1], stream)
+                else:
+                    splan.draft_step(step, ds0["roots"], ds0["draft"][:, step - 1], stream)
             if static:
-                splan.draft_step_static(step, ds0["roots"], ds0["draft"][:, step - 1], stream)
+                splan.static_tree(stream)
             else:
-                splan.draft_step(step, ds0["roots"], ds0["draft"][:, step - 1], stream)
-        if static:
-            splan.static_tree(stream)
-        else:
-            splan.rerank(stream)
+                splan.rerank(stream)
 
-    readout = {}
-    build_us = {}
-    for static in (True, False):
-        name = "static" if static else "dynamic"
-        build_us[name] = time_next(lambda: build(static))
-        readout[name] = round(float(splan.value[:, 1:].double().sum(1).mean()), 5)
+        readout = {}
+        build_us = {}
+        for static in (True, False):
+            name = "static" if static else "dynamic"
+            build_us[name] = time_next(lambda: build(static))
+            readout[name] = round(float(splan.value[:, 1:].double().sum(1).mean()), 5)
     per_cycle_us = {n: acc[n] / K for n in names}
 
     # algorithmic bytes of the last cycle's shapes
@@ -481,13 +488,15 @@ def main():
         "roofline": roofline,
         "per_call_us": {n: round(avg_us[n], 3) for n in names},
         "per_cycle_us": {n: round(per_cycle_us[n], 3) for n in names},
-        "next_calls_us": {"kv_commit": round(commit_us, 3),
-                          "accept_sample": round(sample_us, 3),
-                          "static_tree_build": round(build_us["static"], 3),
-                          "dynamic_tree_build": round(build_us["dynamic"], 3)},
-        "tree_readout": {"expected_accepted_dynamic": readout["dynamic"],
-                         "expected_accepted_static": readout["static"],
-                         "static_nodes": int(len(shape_p) - 1)},
+        "next_calls_us": None if args.no_extras else {
+            "kv_commit": round(commit_us, 3),
+            "accept_sample": round(sample_us, 3),
+            "static_tree_build": round(build_us["static"], 3),
+            "dynamic_tree_build": round(build_us["dynamic"], 3)},
+        "tree_readout": None if args.no_extras else {
+            "expected_accepted_dynamic": readout["dynamic"],
+            "expected_accepted_static": readout["static"],
+            "static_nodes": int(len(shape_p) - 1)},
         "cpu_baseline": cpu,
         "gen_seconds": round(gen_s, 1),
     }
