@@ -352,7 +352,7 @@ def main():
     # 0's targets, in place of the greedy walk.  Each call is timed on its
     # own, 20 times, the GPU held as above; the median is reported.
     commit_us = sample_us = None
-    build_us, readout, shape_p = {}, {}, []
+    build_us, readout, shape_p, lm_step = {}, {}, [], None
     if not args.no_extras:
         def time_next(call, before=None):
             torch.cuda.synchronize()
@@ -408,6 +408,36 @@ def main():
             name = "static" if static else "dynamic"
             build_us[name] = time_next(lambda: build(static))
             readout[name] = round(float(splan.value[:, 1:].double().sum(1).mean()), 5)
+        del splan
+        # Draft steps from hidden states (hidden size 4096, the draft model
+        # reusing this vocabulary's LM head): fused (et_draft_step_hidden)
+        # against the plain pipeline, torch's GEMM writing bf16 logits then
+        # et_draft_step; D steps timed as one call, reported per step.
+        H = 4096
+        lm = gen.lm_head_inputs(w, H)
+        hid = dev(lm["hidden"])
+        wlm = dev(lm["lm_head"])
+        del lm
+        lplan = d.Plan(w)
+
+        def fused():
+            for step in range(1, w.depth + 1):
+                lplan.draft_step_hidden(step, ds0["roots"], hid[:, step - 1], wlm, stream)
+
+        def unfused():
+            for step in range(1, w.depth + 1):
+                logits = torch.nn.functional.linear(hid[:, step - 1], wlm)
+                lplan.draft_step(step, ds0["roots"], logits, stream)
+
+        fused_us = time_next(fused) / w.depth
+        unfused_us = time_next(unfused) / w.depth
+        w_bytes = float(w.vocab) * H * 2
+        lm_step = {"hidden_dim": H, "fused_us": round(fused_us, 2),
+                   "unfused_us": round(unfused_us, 2),
+                   "weight_bytes": int(w_bytes),
+                   "fused_gbs": round(w_bytes / fused_us / 1e3, 1),
+                   "fused_frac_hbm": round(w_bytes / fused_us / 1e3 / HBM_PEAK_GBS, 4)}
+        del hid, wlm, lplan
     per_cycle_us = {n: acc[n] / K for n in names}
 
     # algorithmic bytes of the last cycle's shapes
@@ -493,6 +523,7 @@ def main():
             "accept_sample": round(sample_us, 3),
             "static_tree_build": round(build_us["static"], 3),
             "dynamic_tree_build": round(build_us["dynamic"], 3)},
+        "lm_head_step": lm_step,
         "tree_readout": None if args.no_extras else {
             "expected_accepted_dynamic": readout["dynamic"],
             "expected_accepted_static": readout["static"],

@@ -25,7 +25,7 @@ EXPORTS = ("et_plan_create", "et_plan_destroy", "et_workspace_bytes",
            "et_rerank", "et_tree_mask", "et_tree_attention", "et_accept",
            "et_accept_sample", "et_kv_commit", "et_pool_export",
            "et_set_static_shape", "et_draft_step_static", "et_static_tree",
-           "et_last_error")
+           "et_draft_step_hidden", "et_last_error")
 
 
 class et_config(ctypes.Structure):
@@ -75,6 +75,8 @@ def lib():
                                   vp], ctypes.c_int),
             "et_kv_commit": ([vp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "et_set_static_shape": ([vp, vp, vp, i32], ctypes.c_int),
+            "et_draft_step_hidden": ([vp, vp, i32, vp, vp, i64, i64, vp, i32, vp, vp, vp],
+                                     ctypes.c_int),
             "et_draft_step_static": ([vp, vp, i32, vp, vp, i64, i64, vp, vp, vp], ctypes.c_int),
             "et_static_tree": ([vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "et_pool_export": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
@@ -164,6 +166,21 @@ def et_draft_step_static(plan, ws, step, root_tokens, logits, next_tokens,
                                       _ptr(root_tokens), _ptr(logits), bs, rs,
                                       _ptr(next_tokens), _ptr(next_count),
                                       _stream(stream)))
+
+
+def et_draft_step_hidden(plan, ws, step, root_tokens, hidden, lm_head,
+                         next_tokens, next_count, stream=None):
+    """hidden: bf16 [B][rows][H]; lm_head: bf16 [V][H], contiguous."""
+    if hidden.stride(-1) != 1 or not lm_head.is_contiguous():
+        raise ValueError("hidden rows and lm_head must be contiguous")
+    H = int(lm_head.shape[1])
+    if int(hidden.shape[-1]) != H:
+        raise ValueError("hidden and lm_head disagree on the hidden size")
+    _check(lib().et_draft_step_hidden(plan, _ptr(ws), int(step),
+                                      _ptr(root_tokens), _ptr(hidden),
+                                      hidden.stride(0), hidden.stride(1),
+                                      _ptr(lm_head), H, _ptr(next_tokens),
+                                      _ptr(next_count), _stream(stream)))
 
 
 def et_set_static_shape(plan, parent, rank):
@@ -299,6 +316,11 @@ class Plan:
     def rerank(self, stream=None):
         et_rerank(self.handle, self.ws, self.tokens, self.parent_slot,
                   self.conf, self.value, self.n_kept, stream)
+
+    def draft_step_hidden(self, step, root_tokens, hidden, lm_head, stream=None):
+        """Draft step from hidden states [B][rows][H] through lm_head [V][H]."""
+        et_draft_step_hidden(self.handle, self.ws, step, root_tokens, hidden,
+                             lm_head, self.next_tokens, self.next_count, stream)
 
     def set_static_shape(self, parent, rank):
         """Fixed shape for slots 1..n: parent slot and child rank each."""

@@ -41,7 +41,7 @@ et::Plan* as_plan(et_plan_t p) { return reinterpret_cast<et::Plan*>(p); }
 enum {
   R_POOL_TOKEN, R_POOL_PARENT, R_POOL_DEPTH, R_POOL_CONF, R_POOL_VALUE,
   R_POOL_COUNT, R_ROOT, R_FRONTIER, R_FRONTIER_VAL, R_FRONTIER_COUNT, R_PART_M, R_PART_S,
-  R_PART_KEYS, R_ACC_PART,
+  R_PART_KEYS, R_LM_M, R_LM_S, R_LM_KEYS, R_ACC_PART,
   R_ATT_O, R_ATT_M, R_ATT_L, R_COUNT
 };
 
@@ -60,6 +60,10 @@ void layout(et::Plan& p) {
   const size_t W4 = et::kScanThreads / 64;
   sz[R_PART_M] = sz[R_PART_S] = B * k * S * W4 * 4;
   sz[R_PART_KEYS] = B * k * S * W4 * et::kMaxTopk * 8;
+  // LM-head lists: per (row, 512-id vocab block)
+  const size_t L1 = et::lm_lists1(p.V);
+  sz[R_LM_M] = sz[R_LM_S] = B * k * L1 * 4;
+  sz[R_LM_KEYS] = B * k * L1 * et::kMaxTopk * 8;
   // accept partials: per (slot row, chunk, wave) an 8-byte argmax key
   // (greedy) or a 16-byte (max, fp64 mass) pair (sampled)
   sz[R_ACC_PART] = B * T * p.s_accept * W4 * 16;
@@ -107,6 +111,14 @@ DraftWs draft_ws(const Plan& p, void* ws) {
   w.part_m = at<float>(ws, p, R_PART_M);
   w.part_s = at<float>(ws, p, R_PART_S);
   w.part_keys = at<uint64_t>(ws, p, R_PART_KEYS);
+  return w;
+}
+
+LmWs lm_ws(const Plan& p, void* ws) {
+  LmWs w;
+  w.m = at<float>(ws, p, R_LM_M);
+  w.s = at<float>(ws, p, R_LM_S);
+  w.keys = at<uint64_t>(ws, p, R_LM_KEYS);
   return w;
 }
 
@@ -320,6 +332,52 @@ int et_draft_step_static(et_plan_t plan, void* ws, int32_t step,
   return draft_step("et_draft_step_static", plan, ws, step, root_tokens,
                     logits, batch_stride, row_stride, next_tokens, next_count,
                     stream, true);
+}
+
+int et_draft_step_hidden(et_plan_t plan, void* ws, int32_t step,
+                         const int32_t* root_tokens, const void* hidden,
+                         int64_t batch_stride, int64_t row_stride,
+                         const void* lm_head, int32_t hidden_dim,
+                         int32_t* next_tokens, int32_t* next_count,
+                         et_stream_t stream) {
+  const char* fn = "et_draft_step_hidden";
+  CHECK_PTR(plan);
+  CHECK_PTR(ws);
+  CHECK_PTR(hidden);
+  CHECK_PTR(lm_head);
+  CHECK_PTR(next_tokens);
+  CHECK_PTR(next_count);
+  et::Plan& p = *as_plan(plan);
+  if (step < 1 || step > p.D)
+    return fail(ET_EINVAL, "%s: step %d outside 1..%d", fn, step, p.D);
+  if (step == 1) CHECK_PTR(root_tokens);
+  if (hidden_dim < 128 || hidden_dim > 65536 || hidden_dim % 128 != 0)
+    return fail(ET_EUNSUPPORTED, "%s: hidden_dim %d not a multiple of 128 in 128..65536",
+                fn, hidden_dim);
+  if (row_stride < hidden_dim || batch_stride < 0 || row_stride % 8 != 0 ||
+      batch_stride % 8 != 0)
+    return fail(ET_EINVAL, "%s: strides %lld, %lld (elements) must be multiples of 8, "
+                "row_stride >= hidden_dim", fn, (long long)batch_stride,
+                (long long)row_stride);
+  if (!aligned16(hidden) || !aligned16(lm_head))
+    return fail(ET_EINVAL, "%s: hidden and lm_head must be 16-byte aligned", fn);
+  if (((uintptr_t)ws & 255u) != 0)
+    return fail(ET_EINVAL, "%s: workspace not 256-byte aligned", fn);
+  if (step != 1 && (p.last_ws != ws || p.last_step != step - 1 || p.last_fixed))
+    return fail(ET_ESTATE, "%s: step %d does not follow step %d of the same "
+                "policy on this workspace", fn, step, p.last_step);
+  int rc = hip_status(
+      et::launch_draft_step_hidden(p, et::draft_ws(p, ws), et::lm_ws(p, ws), step,
+                                   root_tokens, hidden, batch_stride, row_stride,
+                                   lm_head, hidden_dim, next_tokens, next_count,
+                                   (hipStream_t)stream),
+      fn);
+  if (rc == ET_OK) {
+    p.last_ws = ws;
+    p.last_step = step;
+    p.last_fixed = false;
+  }
+  return rc;
 }
 
 int et_set_static_shape(et_plan_t plan, const int32_t* parent,

@@ -632,6 +632,33 @@ __global__ __launch_bounds__(kMergeWaves * 64) void draft_merge_fixed_kernel(Dra
   merge_sequence<BF16, LPLM, KST, true>(a, &fx, blockIdx.x);
 }
 
+hipError_t launch_draft_merge(const Plan& p, const DraftWs& w, int step,
+                              const int32_t* root_tokens, int parts,
+                              int32_t* next_tokens, int32_t* next_count, hipStream_t s) {
+  DraftArgs a;
+  a.ws = w;
+  a.logits = nullptr;
+  a.bstride = a.rstride = 0;
+  a.root_tokens = root_tokens;
+  a.next_tokens = next_tokens;
+  a.next_count = next_count;
+  a.B = p.B;
+  a.V = p.V;
+  a.k = p.k;
+  a.D = p.D;
+  a.S = parts;
+  a.cpb = 1;
+  a.parts = parts;
+  a.step = step;
+  a.cap = p.cap;
+  a.thr = p.cfg.expand_threshold;
+  int RW = 1;
+  while (kMergeWaves * RW < p.k) RW <<= 1;
+  if (parts > 64 / RW) draft_merge_kernel<false, 4, 4><<<p.B, kMergeWaves * 64, 0, s>>>(a);
+  else draft_merge_kernel<false, 1, 8><<<p.B, kMergeWaves * 64, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_draft_step(const Plan& p, const DraftWs& w, int step,
                              const int32_t* root_tokens, const void* logits,
                              int64_t bstride, int64_t rstride, bool vec,

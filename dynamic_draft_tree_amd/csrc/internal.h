@@ -9,6 +9,7 @@
 //   frontier_count i32 [2][B]
 //   draft partials     per (row, chunk, wave): max, sum, top-k logit keys
 //   draft rows         per row: max, fp64 sum, top-k logit keys
+//   LM-head lists      per (row, 512-id vocab block): max, sum, top-k keys
 //   accept partials    per (slot row, chunk, wave): argmax key (greedy) or
 //                      (max, mass) of the wave's id range (sampled)
 //   attention partials per (b, kv head, q block, split): O, m, l
@@ -51,7 +52,10 @@ constexpr int chunk_elems(int dtype) {
 constexpr int kScanTargetBlocks = ET_SCAN_TARGET_BLOCKS;
 constexpr int kAttnTile = 64;            // keys per staged K/V tile
 constexpr int kAttnMaxSplits = 32;       // key splits per (kv head, row block)
-constexpr int kAttnTargetBlocks = 256;   // blocks the split count aims for
+#ifndef ET_ATTN_TARGET_BLOCKS
+#define ET_ATTN_TARGET_BLOCKS 256
+#endif
+constexpr int kAttnTargetBlocks = ET_ATTN_TARGET_BLOCKS;  // blocks the split count aims for
 
 struct DraftWs {
   int32_t* pool_token;    // [B][cap]
@@ -68,6 +72,16 @@ struct DraftWs {
   float* part_s;          // [B][k][lists]
   uint64_t* part_keys;    // [B][k][kMaxTopk][lists]: rank r of every list, contiguous
 };
+
+// Draft step from hidden states: level-1 lists, one per (row, 512-id
+// vocab block): max, sum of exp, top-k keys.
+struct LmWs {
+  float* m;               // [B][k][L1]
+  float* s;               // [B][k][L1]
+  uint64_t* keys;         // [B][k][L1][kMaxTopk]
+};
+constexpr int lm_lists1(int V) { return (V + 511) / 512; }
+constexpr int lm_lists2(int V) { return (lm_lists1(V) + 7) / 8; }
 
 struct AcceptWs {
   uint64_t* part;         // [B][T][S][waves] (max logit, lowest id) keys, or
@@ -119,6 +133,7 @@ struct FixedSlots {
 };
 
 DraftWs draft_ws(const Plan& p, void* ws);
+LmWs lm_ws(const Plan& p, void* ws);
 AcceptWs accept_ws(const Plan& p, void* ws);
 AttnWs attn_ws(const Plan& p, void* ws);
 
@@ -128,6 +143,16 @@ hipError_t launch_draft_step(const Plan& p, const DraftWs& w, int step,
                              int64_t bstride, int64_t rstride, bool vec,
                              const FixedFrontier* fixed, int32_t* next_tokens,
                              int32_t* next_count, hipStream_t s);
+// The draft step's merge alone, over `parts` partial lists per row already
+// in the workspace (fp32 logit keys).
+hipError_t launch_draft_merge(const Plan& p, const DraftWs& w, int step,
+                              const int32_t* root_tokens, int parts,
+                              int32_t* next_tokens, int32_t* next_count, hipStream_t s);
+hipError_t launch_draft_step_hidden(const Plan& p, const DraftWs& w, const LmWs& lm, int step,
+                                    const int32_t* root_tokens, const void* hidden,
+                                    int64_t hb, int64_t hr, const void* lm_head, int H,
+                                    int32_t* next_tokens, int32_t* next_count,
+                                    hipStream_t s);
 hipError_t launch_rerank(const Plan& p, const DraftWs& w, int32_t* tokens,
                          int32_t* parent_slot, float* conf, float* value,
                          int32_t* n_kept, hipStream_t s);

@@ -252,6 +252,29 @@ int et_accept_sample(et_plan_t plan, void* ws, const void* target_logits,
                      int32_t* path_slots, int32_t* out_tokens,
                      et_stream_t stream);
 
+/* Draft step from the draft model's final hidden states: the LM head
+ * (EAGLE notes, method section: the draft model reuses the target's LM
+ * head) fused with the step, so the logits never reach HBM.  For row j < F
+ * of sequence b,
+ *     logits[v] = sum_h hidden[b][j][h] * lm_head[v][h]
+ * on the matrix cores (bf16 inputs, fp32 sums in an unspecified order),
+ * then exactly et_draft_step on those fp32 logits (children, conf, value,
+ * next frontier; it is a dynamic-policy step and may be mixed with
+ * et_draft_step steps of the same cycle).
+ *   hidden     device bf16, row j of sequence b at hidden + b * batch_stride
+ *              + j * row_stride (elements, multiples of 8, 16-byte aligned
+ *              base); all topk rows of every sequence must be readable
+ *              (rows j >= F are loaded and ignored)
+ *   lm_head    device bf16 [vocab][hidden_dim], row-major, 16-byte aligned
+ *   hidden_dim a multiple of 128, 128 .. 65536
+ * ET_EUNSUPPORTED for another hidden_dim; other errors as et_draft_step. */
+int et_draft_step_hidden(et_plan_t plan, void* ws, int32_t step,
+                         const int32_t* root_tokens, const void* hidden,
+                         int64_t batch_stride, int64_t row_stride,
+                         const void* lm_head, int32_t hidden_dim,
+                         int32_t* next_tokens, int32_t* next_count,
+                         et_stream_t stream);
+
 /* Static (fixed-shape) tree: the baseline the dynamic tree is compared
  * with ([P2] "Watch the Budget Being Spent": an EAGLE-1-style fixed shape
  * spends the same node budget on every context; [P3] EAGLE: one static

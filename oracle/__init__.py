@@ -250,6 +250,25 @@ def static_tree(w, root_tokens, draft, shape_parent, shape_rank):
     return out
 
 
+def lm_head_logits(hidden_bits, weight_bits, block=8192):
+    """Logits of a draft step taken from hidden states: fp64 sums of the
+    exact bf16 products, logits[..., v] = sum_h hidden[..., h] * W[v, h]
+    (the draft model reusing the target's LM head).  hidden_bits
+    [..., H] and weight_bits [V][H] are bf16 bit patterns; the vocab is
+    done in blocks to bound memory.  Returns fp64 [..., V]."""
+    def widen(bits):  # bf16 bits -> exact fp64
+        return (np.asarray(bits).astype(np.uint32) << np.uint32(16)).view(
+            np.float32).astype(np.float64)
+
+    h = widen(hidden_bits)
+    V = weight_bits.shape[0]
+    out = np.empty(h.shape[:-1] + (V,), np.float64)
+    for v0 in range(0, V, block):
+        v1 = min(V, v0 + block)
+        out[..., v0:v1] = h @ widen(weight_bits[v0:v1]).T
+    return out
+
+
 def kv_commit(w, attn, prefix_len, path_slots, accept_len):
     """Commit the accepted paths to copies of the K/V caches (see
     etref_kv_commit); returns (k_cache, v_cache, prefix_len)."""

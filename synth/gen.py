@@ -140,6 +140,30 @@ def attention_inputs(w: Workload, seed: int | None = None) -> dict:
     return out
 
 
+LM_HIDDEN, LM_WEIGHT = 11, 12
+
+
+def lm_head_inputs(w: Workload, hidden: int, seed: int | None = None) -> dict:
+    """Synthetic draft-model hidden states and LM head (bf16 bits): rows
+    [B][D][k][H] ~ s_b * N(0, 1) per sequence, weight [V][H] ~ N(0, 1/H),
+    so every logit row is again an s_b * N(0, 1) landscape (no planted
+    token).  The weight is drawn in blocks of 4096 vocab rows."""
+    seed = w.seed if seed is None else seed
+    h = np.empty((w.batch, w.depth, w.topk, hidden), np.uint16)
+    for b in range(w.batch):
+        g = stream(seed, LM_HIDDEN, b)
+        x = g.standard_normal((w.depth, w.topk, hidden), dtype=np.float32)
+        h[b] = f32_to_bf16_bits(x * np.float32(w.sharpness[b]))
+    W = np.empty((w.vocab, hidden), np.uint16)
+    g = stream(seed, LM_WEIGHT)
+    scale = np.float32(1.0 / np.sqrt(hidden))
+    for v0 in range(0, w.vocab, 4096):
+        v1 = min(w.vocab, v0 + 4096)
+        W[v0:v1] = f32_to_bf16_bits(
+            g.standard_normal((v1 - v0, hidden), dtype=np.float32) * scale)
+    return dict(hidden=h, lm_head=W)
+
+
 def static_shape(w: Workload, q0: float = 0.6, decay: float = 0.4):
     """A fixed tree shape of w.budget_n nodes for the static-tree baseline:
     nodes taken best first by the product, along their path, of a fixed

@@ -118,6 +118,14 @@ def test_calls_validate_before_launch():
                               nul, fake, fake, fake, nul) == binding.ET_EINVAL
     assert L.et_accept_sample(h, fake, fake, 0, 1000, fake, fake, fake, f(1.0),
                               fake, fake, fake, fake, nul) == binding.ET_EINVAL
+    # draft step from hidden states: hidden size and alignment rules
+    assert L.et_draft_step_hidden(h, fake, 1, fake, fake, 0, 256, fake, 200,
+                                  fake, fake, nul) == binding.ET_EUNSUPPORTED
+    assert L.et_draft_step_hidden(h, fake, 1, fake, ctypes.c_void_p((1 << 20) + 8),
+                                  0, 256, fake, 256, fake, fake,
+                                  nul) == binding.ET_EINVAL
+    assert L.et_draft_step_hidden(h, fake, 1, fake, fake, 0, 100, fake, 256,
+                                  fake, fake, nul) == binding.ET_EINVAL
     # fixed shapes: tiny has topk 2, depth 3, budget 8
     i32a = lambda xs: (ctypes.c_int32 * max(len(xs), 1))(*xs)
     for par, rk in (([1], [0]), ([0], [2]), ([0, 0], [1, 1]),

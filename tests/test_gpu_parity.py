@@ -321,6 +321,84 @@ def test_accept_sample_parity(name):
     print(f"{name}: {cases} sampled-accept cases, {near}/{total} near-ties")
 
 
+# Draft step from hidden states through the LM head.  The GPU sums each
+# logit in fp32 over H / 32 matrix-core steps, so a logit may differ from
+# its fp64 value by up to about (H / 32) roundings of its magnitude (< 2e-4
+# for |logit| < 16, H <= 4096); conf and value then agree to 1e-4 relative,
+# and a child may swap with another whose fp64 logit is that close.
+LM_LOGIT_TOL = 2e-4
+LM_REL_TOL = 1e-4
+LM_CASES = {
+    "lm_small": (TINY.with_(batch=2, vocab=4099, topk=4, depth=3, budget_n=12,
+                            threshold=0.0, sharpness=(2.0, 1.0), seed=41), 256),
+    "lm_k16_h128": (TINY.with_(batch=3, vocab=5000, topk=16, depth=2, budget_n=40,
+                               threshold=0.0, sharpness=(2.5, 1.0, 0.8), seed=42), 128),
+    "lm_vicuna7b": (WORKLOADS["vicuna7b_sharp"].with_(logits_dtype="f32", seed=43), 4096),
+    "lm_llama8b": (WORKLOADS["llama8b"].with_(logits_dtype="f32", depth=3, seed=44), 4096),
+}
+
+
+def _lm_rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return np.abs(a - b) <= LM_REL_TOL * np.abs(b) + 1e-30
+
+
+@pytest.mark.parametrize("name", list(LM_CASES))
+def test_draft_step_hidden_replay(name):
+    """Each draft step from hidden states against the oracle (fp64 LM-head
+    sums, then the draft step on them as fp32 logits) from the GPU's own
+    state: parents and depths exact; children exact except a swap inside a
+    near tie of fp64 logits; conf and value within 1e-4 relative; the
+    frontier exact whenever the children are."""
+    w, H = LM_CASES[name]
+    d = _lib()
+    print(f"[parity] {name}: generating LM head {w.vocab} x {H}", flush=True)
+    lm = gen.lm_head_inputs(w, H)
+    roots = gen.root_tokens(w)
+    hdev, wdev, rdev = to_dev(lm["hidden"]), to_dev(lm["lm_head"]), to_dev(roots)
+    plan = d.Plan(w)
+    before = oracle.TreeState(w)
+    swaps = 0
+    for step in range(1, w.depth + 1):
+        plan.draft_step_hidden(step, rdev, hdev[:, step - 1], wdev)
+        torch.cuda.synchronize()
+        g = state_from_export(w, plan.export_pool(), roots)
+        gnext = (plan.next_tokens.cpu().numpy(), plan.next_count.cpu().numpy())
+        logits = oracle.lm_head_logits(lm["hidden"][:, step - 1], lm["lm_head"])
+        o = before.copy()
+        onext = oracle.draft_step(w, o, step, roots, logits.astype(np.float32))
+        for b in range(w.batch):
+            p0, p1 = int(before.count[b]), int(o.count[b])
+            assert int(g.count[b]) == p1, (step, b)
+            sl = slice(p0, p1)
+            np.testing.assert_array_equal(g.parent[b, sl], o.parent[b, sl])
+            np.testing.assert_array_equal(g.depth[b, sl], o.depth[b, sl])
+            gt, ot = g.token[b, sl], o.token[b, sl]
+            for i in np.nonzero(gt != ot)[0]:
+                row = logits[b, i // w.topk]
+                kth = np.sort(row)[-w.topk]
+                assert abs(row[gt[i]] - row[ot[i]]) <= LM_LOGIT_TOL, (step, b, i)
+                assert row[gt[i]] >= kth - LM_LOGIT_TOL
+                swaps += 1
+            assert _lm_rel(g.conf[b, sl], o.conf[b, sl]).all(), (step, b)
+            assert _lm_rel(g.value[b, sl], o.value[b, sl]).all(), (step, b)
+            if (gt == ot).all():
+                fg = list(g.frontier[b, :g.frontier_count[b]])
+                fo = list(o.frontier[b, :o.frontier_count[b]])
+                if fg != fo:  # only a near tie of values may reorder
+                    vo = o.value[b]
+                    a1 = sorted((float(vo[x]) for x in fg), reverse=True)
+                    a2 = sorted((float(vo[x]) for x in fo), reverse=True)
+                    assert len(a1) == len(a2) and _lm_rel(a1, a2).all()
+                    swaps += 1
+                np.testing.assert_array_equal(
+                    gnext[0][b][:len(fg)], [int(g.token[b, x]) for x in fg])
+        before = g
+    assert swaps <= 2, swaps
+    print(f"{name}: {w.depth} steps, near-tie swaps {swaps}")
+
+
 STATIC = ["tiny", "chain_k1", "small_bf16", "odd_vocab", "wide_w3", "max_pool",
           "wide_f32", "max_vocab", "f32_gqa", "vicuna7b_flat", "llama8b",
           "llama8b_b64", "llama70b_b8"]

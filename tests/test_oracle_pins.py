@@ -702,6 +702,25 @@ def test_sampled_accept_zero_uniforms_take_first_child():
         assert acc["out_tokens"][0, L] == 0
 
 
+# ------------------------------------------------------------ LM head
+def test_lm_head_logits_are_the_plain_sums():
+    """Logits from hidden states equal the sums written out term by term
+    (exact on bf16 inputs in fp64), for a tiny head in vocab blocks that
+    do not divide the vocabulary."""
+    g = np.random.default_rng(2)
+    hb = gen.f32_to_bf16_bits(g.standard_normal((2, 3, 8)).astype(np.float32))
+    wb = gen.f32_to_bf16_bits(g.standard_normal((7, 8)).astype(np.float32))
+    got = oracle.lm_head_logits(hb, wb, block=3)
+    h, W = gen.bf16_bits_to_f32(hb), gen.bf16_bits_to_f32(wb)
+    for b in range(2):
+        for j in range(3):
+            for v in range(7):
+                want = 0.0
+                for k in range(8):
+                    want += float(h[b, j, k]) * float(W[v, k])
+                assert got[b, j, v] == want
+
+
 # ------------------------------------------------------------ static tree
 def _dynamic_shape(w, st, rr, b=0):
     """(parent, rank) of the kept dynamic tree in slot order; a node's rank
