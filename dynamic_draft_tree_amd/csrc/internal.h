@@ -73,14 +73,18 @@ struct DraftWs {
   uint64_t* part_keys;    // [B][k][kMaxTopk][lists]: rank r of every list, contiguous
 };
 
-// Draft step from hidden states: level-1 lists, one per (row, 512-id
+// Draft step from hidden states: level-1 lists, one per (row, kLmCols-id
 // vocab block): max, sum of exp, top-k keys.
 struct LmWs {
   float* m;               // [B][k][L1]
   float* s;               // [B][k][L1]
   uint64_t* keys;         // [B][k][L1][kMaxTopk]
 };
-constexpr int lm_lists1(int V) { return (V + 511) / 512; }
+#ifndef ET_LM_WAVES
+#define ET_LM_WAVES 8
+#endif
+constexpr int kLmCols = ET_LM_WAVES * 64;  // vocab ids per LM-head block
+constexpr int lm_lists1(int V) { return (V + kLmCols - 1) / kLmCols; }
 constexpr int lm_lists2(int V) { return (lm_lists1(V) + 7) / 8; }
 
 struct AcceptWs {

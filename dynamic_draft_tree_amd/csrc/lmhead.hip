@@ -35,8 +35,10 @@ struct LmArgs {
   int B, V, k, H, L1, L2, step;
 };
 
-constexpr int kLmWaves = 8;
-constexpr int kLmCols = kLmWaves * 64;  // vocab ids per GEMM block
+// Measured at 128256 x 4096 (per step): 8 waves 207.7 us, 4 waves (256-id
+// blocks, twice the lists) 235.2 us; two k-steps per load group 206.8 us;
+// non-temporal W loads 225.5 us.
+constexpr int kLmWaves = ET_LM_WAVES;   // kLmCols = 64 per wave
 constexpr int kLmGroup = 8;             // level-1 lists per level-2 list
 constexpr int kLmKG = 4;                // k-steps (of 32) per load group
 constexpr float kLmLog2e = 1.4426950408889634f;
