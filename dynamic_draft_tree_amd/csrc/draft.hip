@@ -117,14 +117,19 @@ __device__ __forceinline__ void scan_chunks(const DraftArgs& a, const char* row,
       return ((const float*)s_x)[((e >> 2) * NT + tid) * 4 + (e & 3)];
   };
 
-  // Lane max as a pairwise tree (short dependency chain).
+  // Lane max as a ternary tree (three-input maxima, short chain).
   float mx[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) mx[e] = xv(e);
 #pragma unroll
-  for (int w = E / 2; w >= 1; w >>= 1)
+  for (int n = E; n > 1; n = (n + 2) / 3)
 #pragma unroll
-    for (int e = 0; e < w; ++e) mx[e] = fmaxf(mx[e], mx[e + w]);
+    for (int i = 0; i < (n + 2) / 3; ++i) {
+      float m = mx[3 * i];
+      if (3 * i + 1 < n) m = fmaxf(m, mx[3 * i + 1]);
+      if (3 * i + 2 < n) m = fmaxf(m, mx[3 * i + 2]);
+      mx[i] = m;
+    }
   const float lmax = mx[0];
   const float mw = wave_max_f32(lmax);
   float sl = 0.f;
@@ -154,11 +159,18 @@ __device__ __forceinline__ void scan_chunks(const DraftArgs& a, const char* row,
   const int lim = a.V - lid;
   // (one is opaque to the compiler: written as cond ? 1 << e : 0 the 32
   // masks would be hoisted out of the chunk loop into registers)
+  // Ids past V read -inf, so with a finite Lw no bound check is needed;
+  // Lw = -inf (fewer than k lanes of the wave inside the row) takes it.
   uint32_t one = 1u, bits = 0u;
   asm volatile("" : "+v"(one));
+  if (Lw > -INFINITY) {
 #pragma unroll
-  for (int e = 0; e < E; ++e)
-    bits |= (elem_off<BF16>(e, 0) < lim && xv(e) >= Lw ? one : 0u) << e;
+    for (int e = 0; e < E; ++e) bits |= (xv(e) >= Lw ? one : 0u) << e;
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      bits |= (elem_off<BF16>(e, 0) < lim && xv(e) >= Lw ? one : 0u) << e;
+  }
   // The lane's values are staged in LDS so that each candidate is read by
   // index (a register array cannot be indexed at run time cheaply).
   // Layout: 16-byte group q of every lane in one contiguous row of the
