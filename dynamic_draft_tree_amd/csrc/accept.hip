@@ -57,21 +57,33 @@ __global__ __launch_bounds__(256) void accept_scan_kernel(AcceptArgs a) {
     }
     // phase: chunk loaded
     // (max logit, lowest id) of the wave's elements: the lane maximum as a
-    // pairwise tree, the wave maximum, then the lowest id holding it (a
-    // lane's ids increase with e).
+    // tree of three-input maxima, the wave maximum, then the lowest id
+    // holding it (a lane's ids increase with e).
     float mx[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) mx[e] = x[e];
 #pragma unroll
-    for (int w = E / 2; w >= 1; w >>= 1)
+    for (int n = E; n > 1; n = (n + 2) / 3)
 #pragma unroll
-      for (int e = 0; e < w; ++e) mx[e] = fmaxf(mx[e], mx[e + w]);
+      for (int i = 0; i < (n + 2) / 3; ++i) {
+        float m = mx[3 * i];
+        if (3 * i + 1 < n) m = fmaxf(m, mx[3 * i + 1]);
+        if (3 * i + 2 < n) m = fmaxf(m, mx[3 * i + 2]);
+        mx[i] = m;
+      }
     const float wm = wave_max_f32(mx[0]);
     const int lid = base + tid * per;  // element e's id is lid + elem_off(e, 0)
     uint32_t best = 0xFFFFFFFFu;
+    // ids past V read -inf: with a finite maximum no bound check is needed
+    if (wm > -INFINITY) {
 #pragma unroll
-    for (int e = E - 1; e >= 0; --e)
-      if (x[e] == wm && elem_off<BF16>(e, 0) < a.V - lid) best = (uint32_t)(lid + elem_off<BF16>(e, 0));
+      for (int e = E - 1; e >= 0; --e)
+        if (x[e] == wm) best = (uint32_t)(lid + elem_off<BF16>(e, 0));
+    } else {
+#pragma unroll
+      for (int e = E - 1; e >= 0; --e)
+        if (x[e] == wm && elem_off<BF16>(e, 0) < a.V - lid) best = (uint32_t)(lid + elem_off<BF16>(e, 0));
+    }
     const uint32_t wid = wave_min_u32(best);
     if (lane == 0)
       a.ws.part[(rowid * a.S + c) * kAccWaves + wave] = wid == 0xFFFFFFFFu ? 0 : logit_key(wm, wid);

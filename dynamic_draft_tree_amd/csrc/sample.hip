@@ -31,6 +31,9 @@
 // and in the bonus search.  The final row's segment scales
 // exp2((m_j - max) * c) are fp64; the ratio tests, which need no such
 // resolution, use fp32 scales and masses (one rounding each).
+#include <cfloat>
+#include <cmath>
+
 #include "device.h"
 #include "internal.h"
 
@@ -54,11 +57,12 @@ struct SampleArgs {
 
 constexpr int kSegsPerChunk = kScanThreads / 64;
 
-// fp32 weight of logit x against a segment max m (0 for -inf)
+// fp32 weight of logit x against a segment max m: exp2(d * (c_hi + c_lo)),
+// d = x - m <= 0.  c_lo is a positive normal float, so d = -inf gives
+// -inf + -inf in the exponent and weight 0 with no test.
 __device__ __forceinline__ float seg_weight(float x, float m, float c_hi, float c_lo) {
   const float d = x - m;
-  const float w = exp2f(fmaf(d, c_hi, d * c_lo));
-  return d == -INFINITY ? 0.0f : w;
+  return exp2f(fmaf(d, c_hi, d * c_lo));
 }
 
 // Scan layout: vector i of a lane is at base + (i * 64 + lane) * per (a
@@ -153,9 +157,14 @@ __global__ __launch_bounds__(256) void sample_scan_kernel(SampleArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) t[e] = x[e];
 #pragma unroll
-    for (int w = E / 2; w >= 1; w >>= 1)
+    for (int n = E; n > 1; n = (n + 2) / 3)
 #pragma unroll
-      for (int e = 0; e < w; ++e) t[e] = fmaxf(t[e], t[e + w]);
+      for (int i = 0; i < (n + 2) / 3; ++i) {
+        float m = t[3 * i];
+        if (3 * i + 1 < n) m = fmaxf(m, t[3 * i + 1]);
+        if (3 * i + 2 < n) m = fmaxf(m, t[3 * i + 2]);
+        t[i] = m;
+      }
     const float wm = wave_max_f32(t[0]);
     // mass: fp32 sums of 8 weights, fp64 above
     double ls = 0.0;
@@ -538,8 +547,12 @@ hipError_t launch_accept_sample(const Plan& p, const AcceptWs& w, const void* ta
   a.n_kept = n_kept;
   a.uniforms = uniforms;
   a.c = c;
-  a.c_hi = (float)c;
-  a.c_lo = (float)(c - (double)a.c_hi);
+  // c = c_hi + c_lo with c_hi rounded toward zero, so c_lo >= 0; it is
+  // kept a positive normal float (see seg_weight)
+  float hi = (float)c;
+  if ((double)hi > c) hi = nextafterf(hi, 0.0f);
+  a.c_hi = hi;
+  a.c_lo = fmaxf((float)(c - (double)hi), FLT_MIN);
   a.accept_len = accept_len;
   a.path_slots = path_slots;
   a.out_tokens = out_tokens;
