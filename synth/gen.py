@@ -140,6 +140,54 @@ def attention_inputs(w: Workload, seed: int | None = None) -> dict:
     return out
 
 
+TIED, TIED_TARGET = 13, 14
+
+
+def _tied_rows(g: np.random.Generator, n_rows: int, V: int, s: float) -> np.ndarray:
+    """fp32 rows full of exact ties, by row index r mod 4: 0: every logit
+    0; 1: N(0,1) / 2 rounded to integers (about 16% of a row share the
+    largest common value); 2: N(0,1) with the value 6 at max(300, V/64)
+    random ids; 3: the landscape of draft_logits."""
+    rows = landscape_rows(g, n_rows, V, s, "f32")
+    for r in range(n_rows):
+        kind = r % 4
+        if kind == 0:
+            rows[r] = 0.0
+        elif kind == 1:
+            rows[r] = np.rint(0.5 * g.standard_normal(V))
+        elif kind == 2:
+            x = g.standard_normal(V).astype(np.float32)
+            x[g.choice(V, size=min(V, max(300, V // 64)), replace=False)] = 6.0
+            rows[r] = x
+    return rows
+
+
+def tied_draft_logits(w: Workload, seed: int | None = None) -> np.ndarray:
+    """[B][D][k][V] draft logits of _tied_rows (row index = layer * k +
+    frontier slot).  Values are rounded to the workload's dtype like
+    draft_logits; the integers are exact in both, so the ties survive."""
+    seed = w.seed if seed is None else seed
+    out = np.empty((w.batch, w.depth, w.topk, w.vocab),
+                   dtype=np.float32 if w.logits_dtype == "f32" else np.uint16)
+    for b in range(w.batch):
+        rows = _tied_rows(stream(seed, TIED, b), w.depth * w.topk, w.vocab,
+                          w.sharpness[b])
+        out[b] = _cast(rows, w.logits_dtype).reshape(w.depth, w.topk, w.vocab)
+    return out
+
+
+def tied_target_logits(w: Workload, seed: int | None = None) -> np.ndarray:
+    """[B][T][V] target logits of _tied_rows (row index = slot)."""
+    seed = w.seed if seed is None else seed
+    out = np.empty((w.batch, w.T, w.vocab),
+                   dtype=np.float32 if w.logits_dtype == "f32" else np.uint16)
+    for b in range(w.batch):
+        rows = _tied_rows(stream(seed, TIED_TARGET, b), w.T, w.vocab,
+                          w.sharpness[b])
+        out[b] = _cast(rows, w.logits_dtype)
+    return out
+
+
 LM_HIDDEN, LM_WEIGHT = 11, 12
 
 

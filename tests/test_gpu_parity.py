@@ -86,6 +86,15 @@ VARIANTS = {
 FULL = ["vicuna7b_flat", "vicuna7b_sharp", "llama8b", "llama8b_b64",
         "llama70b_b8"]
 ALL = list(VARIANTS) + FULL
+# Draft rows full of exact ties (synth.gen.tied_draft_logits): whole rows
+# of equal logits put more than 64 candidates in a scan wave (the exact
+# top-k path); ties between ids are broken by the lower id.
+TIED = {
+    "small_bf16": VARIANTS["small_bf16"],
+    "wide_f32": VARIANTS["wide_f32"],
+    "llama8b_d3": WORKLOADS["llama8b"].with_(depth=3),
+    "llama8b_b64_d2": WORKLOADS["llama8b_b64"].with_(depth=2),
+}
 
 
 def _w(name):
@@ -95,15 +104,18 @@ def _w(name):
 _cache = {}
 
 
-def _run(name):
+def _run(name, tied=False):
     """GPU cycle step by step with pool exports, plus the oracle replay.
-    Cached per workload so later tests reuse one run."""
-    if name in _cache:
-        return _cache[name]
+    Cached per workload so later tests reuse one run.  tied: the draft
+    logits of tied_draft_logits instead."""
+    if (name, tied) in _cache:
+        return _cache[(name, tied)]
     d = _lib()
-    w = _w(name)
-    print(f"[parity] {name}: generating inputs", flush=True)
+    w = TIED[name] if tied else _w(name)
+    print(f"[parity] {name}{' tied' if tied else ''}: generating inputs", flush=True)
     inp = make_inputs(w)
+    if tied:
+        inp["draft"] = gen.tied_draft_logits(w)
     dev = dev_inputs(inp)
     plan = d.Plan(w)
     roots = inp["root_tokens"]
@@ -130,7 +142,7 @@ def _run(name):
                   n_kept=plan.n_kept.cpu().numpy())
     res = dict(w=w, inp=inp, dev=dev, plan=plan, gpu_state=before,
                ora_indep=ora_indep, events=events, gpu_rr=gpu_rr)
-    _cache[name] = res
+    _cache[(name, tied)] = res
     print(f"[parity] {name}: draft steps done, near-tie events {events}",
           flush=True)
     return res
@@ -138,8 +150,16 @@ def _run(name):
 
 @pytest.mark.parametrize("name", ALL)
 def test_draft_steps_replay(name):
-    r = _run(name)
-    w = r["w"]
+    _check_replay(_run(name))
+
+
+@pytest.mark.parametrize("name", list(TIED))
+def test_draft_steps_replay_tied(name):
+    _check_replay(_run(name, tied=True))
+
+
+def _check_replay(r):
+    name, w = r["w"].name, r["w"]
     if r["events"] == 0:
         # no near tie anywhere: the independent oracle run must match
         g, o = r["gpu_state"], r["ora_indep"]
@@ -156,7 +176,15 @@ def test_draft_steps_replay(name):
 @pytest.mark.parametrize("name", ALL)
 def test_rerank_and_mask_exact(name):
     """Rerank and mask on the GPU pool equal the oracle's on that pool."""
-    r = _run(name)
+    _check_rerank_mask(_run(name))
+
+
+@pytest.mark.parametrize("name", list(TIED))
+def test_rerank_and_mask_exact_tied(name):
+    _check_rerank_mask(_run(name, tied=True))
+
+
+def _check_rerank_mask(r):
     w, plan = r["w"], r["plan"]
     ora = oracle.rerank(w, r["gpu_state"])
     g = r["gpu_rr"]
@@ -247,6 +275,21 @@ def test_accept_exact(name):
                                       ref["path_slots"])
         np.testing.assert_array_equal(plan.out_tokens.cpu().numpy(),
                                       ref["out_tokens"])
+    print(f"{name}: accept_len {plan.accept_len.cpu().numpy()[:8]}")
+
+
+@pytest.mark.parametrize("name", list(TIED))
+def test_accept_exact_tied(name):
+    """Greedy walk on target rows full of exact ties (lowest id wins)."""
+    r = _run(name, tied=True)
+    w, plan, g = r["w"], r["plan"], r["gpu_rr"]
+    tgt = gen.tied_target_logits(w)
+    plan.accept(to_dev(tgt))
+    torch.cuda.synchronize()
+    ref = oracle.accept(w, tgt, g["tokens"], g["parent_slot"], g["n_kept"])
+    np.testing.assert_array_equal(plan.accept_len.cpu().numpy(), ref["accept_len"])
+    np.testing.assert_array_equal(plan.path_slots.cpu().numpy(), ref["path_slots"])
+    np.testing.assert_array_equal(plan.out_tokens.cpu().numpy(), ref["out_tokens"])
     print(f"{name}: accept_len {plan.accept_len.cpu().numpy()[:8]}")
 
 
