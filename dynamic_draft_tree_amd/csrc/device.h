@@ -48,6 +48,9 @@ __device__ __forceinline__ int pool_index_of(uint64_t key) {
 __device__ __forceinline__ float pool_value_of(uint64_t key) {
   return __uint_as_float((uint32_t)(key >> 34));
 }
+__device__ __forceinline__ int pool_token_of(uint64_t key) {
+  return (1 << 18) - 1 - (int)((key >> 12) & 0x3FFFFu);
+}
 
 // ---- cross-lane exchange without LDS traffic -----------------------------
 // xor_lane<M>(v) returns the value of lane (lane ^ M).  Within a 16-lane

@@ -79,7 +79,6 @@ __device__ __forceinline__ void suffix_pick(const uint32_t* hist, int need,
 
 __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(RerankArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x;
-  __shared__ uint64_t s_key[kMaxBudget + 1];  // rank -> key
   __shared__ uint64_t s_cand[kRerankCand];
   __shared__ int16_t s_slot[kRerankMaxPool];
   __shared__ uint32_t s_hist[256];
@@ -88,14 +87,25 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(RerankArgs a) {
   const int P = a.ws.pool_count[b];
   const int n = P < a.N ? P : a.N;
   constexpr int PER = kRerankMaxPool / kRerankThreads;
+  // Each thread keeps its nodes' fields in registers: the kept ones are
+  // written out by their owner once the ranks are known, with no second
+  // round of pool loads.
   uint64_t key[PER];
+  int par[PER];
+  float cnf[PER];
+  const int root = tid == 0 ? a.ws.root_token[b] : -1;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int idx = tid + kRerankThreads * i;
     key[i] = 0;
-    if (idx < P)
+    par[i] = -1;
+    cnf[i] = 0.f;
+    if (idx < P) {
       key[i] = pool_key(a.ws.pool_value[pb + idx], a.ws.pool_depth[pb + idx],
                         a.ws.pool_token[pb + idx], idx);
+      par[i] = a.ws.pool_parent[pb + idx];
+      cnf[i] = a.ws.pool_conf[pb + idx];
+    }
     s_slot[idx] = -1;
   }
   if (tid == 0) s_count = 0;
@@ -149,32 +159,30 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(RerankArgs a) {
       }
       for (; j < cnt; ++j) r0 += s_cand[j] > me;
       const int rank = (r0 + r1) + (r2 + r3);
-      if (rank < n) {
-        s_key[rank] = me;
-        s_slot[pool_index_of(me)] = (int16_t)(rank + 1);
-      }
+      if (rank < n) s_slot[pool_index_of(me)] = (int16_t)(rank + 1);
     }
   }
   __syncthreads();
-  for (int s = tid; s < a.T; s += kRerankThreads) {
-    int tok = -1, ps = -1;
-    float cf = 0.f, vl = 0.f;
-    if (s == 0) {
-      tok = a.ws.root_token[b];
-      cf = 1.f;
-      vl = 1.f;
-    } else if (s <= n) {
-      const int idx = pool_index_of(s_key[s - 1]);
-      const int par = a.ws.pool_parent[pb + idx];
-      tok = a.ws.pool_token[pb + idx];
-      ps = par < 0 ? 0 : s_slot[par];
-      cf = a.ws.pool_conf[pb + idx];
-      vl = a.ws.pool_value[pb + idx];
+  // kept nodes: slot = rank + 1, written by the thread that holds the node
+  // (token and value come back out of the key, which holds both exactly)
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = tid + kRerankThreads * i;
+    const int s = key[i] != 0 ? s_slot[idx] : -1;
+    if (s > 0) {
+      a.tokens[ob + s] = pool_token_of(key[i]);
+      a.parent_slot[ob + s] = par[i] < 0 ? 0 : s_slot[par[i]];
+      a.conf[ob + s] = cnf[i];
+      a.value[ob + s] = pool_value_of(key[i]);
     }
-    a.tokens[ob + s] = tok;
-    a.parent_slot[ob + s] = ps;
-    a.conf[ob + s] = cf;
-    a.value[ob + s] = vl;
+  }
+  // the root and the pad slots
+  for (int s = tid; s < a.T; s += kRerankThreads) {
+    if (s != 0 && s <= n) continue;
+    a.tokens[ob + s] = s == 0 ? root : -1;
+    a.parent_slot[ob + s] = -1;
+    a.conf[ob + s] = s == 0 ? 1.f : 0.f;
+    a.value[ob + s] = s == 0 ? 1.f : 0.f;
   }
   if (tid == 0) a.n_kept[b] = n;
 }
