@@ -11,8 +11,10 @@ Prints one JSON line: cycles/s, the roofline of the dominant call
 (algorithmic bytes / its average duration, HIP events on the launch
 stream; a call is one or two back-to-back launches) and the CPU oracle
 timed on this host as a reported baseline.  Beside the metric, timed
-after it: KV commit, sampled acceptance, and the fixed-shape tree build
-against the dynamic one with each tree's expected accepted tokens.
+after it: the spread of the cycle time (p10 / median / p90 over groups of
+10 cycles), KV commit, sampled acceptance, the fixed-shape tree build
+against the dynamic one with each tree's expected accepted tokens, and
+the draft step from hidden states (LM head fused) against torch's GEMM.
 """
 from __future__ import annotations
 
@@ -270,6 +272,23 @@ def main():
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
 
+    # ---- spread: per-cycle time of groups of 10 cycles, after the timed
+    # region (events between whole cycles, all groups enqueued at once) ----
+    n_groups, per_group = 20, 10
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_groups + 1)]
+    evs[0].record()
+    for g_ in range(n_groups):
+        for i in range(per_group):
+            run(g_ * per_group + i)
+        evs[g_ + 1].record()
+    torch.cuda.synchronize()
+    grp = np.array([evs[g_].elapsed_time(evs[g_ + 1]) * 1e3 / per_group
+                    for g_ in range(n_groups)])
+    spread = {"groups": n_groups, "cycles_per_group": per_group,
+              "p10_us": round(float(np.percentile(grp, 10)), 2),
+              "median_us": round(float(np.median(grp)), 2),
+              "p90_us": round(float(np.percentile(grp, 90)), 2)}
+
     # ---- per-call durations (instrumented pass, eager, same stream) -------
     # HIP cannot time events recorded inside a graph, so each call is timed
     # in an eager pass bracketed by events on the launch stream.  A spin
@@ -517,6 +536,7 @@ def main():
                    "mode": "eager" if graphs is None else "hip_graph"},
         "roofline": roofline,
         "per_call_us": {n: round(avg_us[n], 3) for n in names},
+        "cycle_us_spread": spread,
         "per_cycle_us": {n: round(per_cycle_us[n], 3) for n in names},
         "next_calls_us": None if args.no_extras else {
             "kv_commit": round(commit_us, 3),
