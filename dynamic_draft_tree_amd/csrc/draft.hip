@@ -669,7 +669,8 @@ hipError_t launch_draft_merge(const Plan& p, const DraftWs& w, int step,
   a.thr = p.cfg.expand_threshold;
   int RW = 1;
   while (kMergeWaves * RW < p.k) RW <<= 1;
-  if (parts > 64 / RW) draft_merge_kernel<false, 4, 4><<<p.B, kMergeWaves * 64, 0, s>>>(a);
+  if (parts > 2 * (64 / RW)) draft_merge_kernel<false, 4, 4><<<p.B, kMergeWaves * 64, 0, s>>>(a);
+  else if (parts > 64 / RW) draft_merge_kernel<false, 2, 4><<<p.B, kMergeWaves * 64, 0, s>>>(a);
   else draft_merge_kernel<false, 1, 8><<<p.B, kMergeWaves * 64, 0, s>>>(a);
   return hipGetLastError();
 }
@@ -714,15 +715,19 @@ hipError_t launch_draft_step(const Plan& p, const DraftWs& w, int step,
   // lanes per row
   int RW = 1;
   while (kMergeWaves * RW < p.k) RW <<= 1;
-  const bool many = a.parts > 64 / RW;
+  // lists per lane: as many as the row's lists need (the bound search
+  // takes one ballot per list slot and bit)
+  const int lpl = (a.parts + 64 / RW - 1) / (64 / RW);
 #define ET_MERGE(BF, L, K)                                                               \
   do {                                                                                   \
     if (fixed) draft_merge_fixed_kernel<BF, L, K><<<p.B, kMergeWaves * 64, 0, s>>>(a, *fixed); \
     else draft_merge_kernel<BF, L, K><<<p.B, kMergeWaves * 64, 0, s>>>(a);               \
   } while (0)
-  if (bf && many) ET_MERGE(true, 4, 4);
+  if (bf && lpl > 2) ET_MERGE(true, 4, 4);
+  else if (bf && lpl == 2) ET_MERGE(true, 2, 4);
   else if (bf) ET_MERGE(true, 1, 8);
-  else if (many) ET_MERGE(false, 4, 4);
+  else if (lpl > 2) ET_MERGE(false, 4, 4);
+  else if (lpl == 2) ET_MERGE(false, 2, 4);
   else ET_MERGE(false, 1, 8);
 #undef ET_MERGE
   return hipGetLastError();
