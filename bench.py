@@ -12,7 +12,8 @@ Prints one JSON line: cycles/s, the roofline of the dominant call
 stream; a call is one or two back-to-back launches) and the CPU oracle
 timed on this host as a reported baseline.  Beside the metric, timed
 after it: the spread of the cycle time (p10 / median / p90 over groups of
-10 cycles), KV commit, sampled acceptance, the fixed-shape tree build
+10 cycles), a streaming-copy bandwidth as the practical HBM ceiling, KV
+commit, sampled acceptance, the fixed-shape tree build
 against the dynamic one with each tree's expected accepted tokens, and
 the draft step from hidden states (LM head fused) against torch's GEMM.
 """
@@ -289,6 +290,22 @@ def main():
               "median_us": round(float(np.median(grp)), 2),
               "p90_us": round(float(np.percentile(grp, 90)), 2)}
 
+    # ---- streaming-copy bandwidth: the practical HBM ceiling beside the
+    # 8 TB/s peak (an elementwise kernel over 512 MiB in, 512 MiB out) ------
+    cn = 512 * (1 << 20) // 4
+    csrc = torch.ones(cn, dtype=torch.float32, device="cuda")
+    cdst = torch.empty_like(csrc)
+    torch.neg(csrc, out=cdst)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        torch.neg(csrc, out=cdst)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * cn * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del csrc, cdst
+
     # ---- per-call durations (instrumented pass, eager, same stream) -------
     # HIP cannot time events recorded inside a graph, so each call is timed
     # in an eager pass bracketed by events on the launch stream.  A spin
@@ -535,6 +552,7 @@ def main():
                    "set_mb": round(set_bytes / 1e6, 1),
                    "mode": "eager" if graphs is None else "hip_graph"},
         "roofline": roofline,
+        "hbm_copy_gbs": round(copy_gbs, 1),
         "per_call_us": {n: round(avg_us[n], 3) for n in names},
         "cycle_us_spread": spread,
         "per_cycle_us": {n: round(per_cycle_us[n], 3) for n in names},
