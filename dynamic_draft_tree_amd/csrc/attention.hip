@@ -546,7 +546,7 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a) {
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int i = 0; i < kAttnMaxSplits; ++i) {
-    const float f = mi[i] == -INFINITY ? 0.f : exp2f(mi[i] - m);
+    const float f = mi[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi[i] - m);
     l += li[i] * f;
     acc.x += oi[i].x * f;
     acc.y += oi[i].y * f;
