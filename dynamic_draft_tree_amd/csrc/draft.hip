@@ -36,7 +36,6 @@ struct DraftArgs {
 
 constexpr int kWaves = kScanThreads / 64;  // waves per scan block
 constexpr int kWaveCap = 64;             // candidate slots per wave
-constexpr int kRowCap = 64;              // merge candidates per row
 
 // The k-th largest of the wave's 64 keys (k <= 64): the largest T whose
 // count of keys >= T is at least k, built bit by bit from the top (bits
@@ -303,176 +302,105 @@ __device__ __forceinline__ void empty_frontier(const DraftArgs& a, int b) {
   }
 }
 
-// The rows of sequence b, every chunk's partials stored by the scan launch:
-// row softmax statistics and top-k, children appended to the pool, next
-// frontier.  One block of kMergeWaves waves (one per SIMD: they start
-// together; a block of more waves per SIMD starts them in groups).
-// LPLM: partial lists per lane, at most; KST: keys staged per list (lists
-// are sorted, so the keys at or above the bound are a prefix of each).
-// With many short lists (64 per row) four keys per list almost always
-// hold every candidate; with 16 lists per row eight are needed.
-constexpr int kMergeWaves = 4;
+// Merge launch: one block of k waves per sequence; wave j merges frontier
+// row j, one partial list per lane (a row has at most 64 lists).  The
+// row's max and sum of exp are wave reductions.  Bound: with at least k
+// lists the k-th largest list head bounds the row's k-th largest key from
+// below, so only keys at or above it (a prefix of every sorted list) are
+// ranked; each lane stages the first KST keys of its list.  A row whose
+// candidates do not fit the staged keys (many equal or clustered logits)
+// takes an exact path: k rounds of wave maximum over all of its keys.
+// The children (conf, value) go to the pool; the next frontier is the k
+// largest children keys, ranked by counting with four threads per child
+// across the whole block.
 // FIXED: the next frontier comes from a fixed shape (fx) instead of the
 // children's values.
-template <bool BF16, int LPLM, int KST, bool FIXED>
-__device__ __forceinline__ void merge_sequence(const DraftArgs& a, const FixedFrontier* fx,
-                                               int b) {
-  constexpr int kLPL = LPLM;
-  constexpr int kStage = KST;
+template <bool BF16, int KST, bool FIXED>
+__device__ __forceinline__ void merge_rows(const DraftArgs& a, const FixedFrontier* fx, int b) {
   constexpr float kLog2e = 1.4426950408889634f;
-  constexpr int NW = kMergeWaves;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int k = a.k, S = a.parts;  // partial lists per row
+  const int tid = threadIdx.x, lane = tid & 63, jr = tid >> 6;  // jr: this wave's row
+  const int k = a.k, S = a.parts;  // partial lists per row (<= 64)
   const int prev = (a.step - 1) & 1, cur = a.step & 1;
-  __shared__ uint64_t s_rc[kMaxTopk * kRowCap];   // row candidates
+  __shared__ uint64_t s_rc[kMaxTopk * 64];        // row candidates
   __shared__ uint64_t s_rk[kMaxTopk * kMaxTopk];  // row top-k keys
-  __shared__ uint64_t s_aux[256];                 // children's pool keys
-  __shared__ uint64_t s_fb[kWaveCap];             // frontier candidates
-  // ---- row merges: a segment of SP lanes per row ------------------------
-  // RW rows per wave (a power of two, NW * RW >= k, so one pass covers
-  // every row), SP = 64 / RW lanes per row; lane q of a segment holds
-  // lists q, q + SP, ... (LPL of them): each list's (max, sum) and its
-  // first kStage keys (lists are sorted).  The row's max and sum of exp
-  // are segment reductions.  Bound: with at least k lists the k-th largest
-  // list head bounds the row's k-th largest key from below, so only keys
-  // at or above it (a prefix of every list) are ranked.
-  // Every load below is issued before the frontier count F arrives: rows
-  // j < k of the workspace are always readable, rows j >= F are dropped.
-  const int64_t e0 = (int64_t)b * k * S;  // first partial of the sequence
-  int RW = 1;
-  while (NW * RW < k) RW <<= 1;
-  const int SP = 64 / RW;
-  const int LPL = (S + SP - 1) / SP;
-  const int seg = lane / SP, q = lane - seg * SP;
-  const uint64_t segmask = SP == 64 ? ~0ull : ((1ull << SP) - 1ull) << (seg * SP);
-  const uint64_t below = segmask & ((1ull << lane) - 1ull);
-  const int64_t pb = (int64_t)b * a.cap;
-  const int jr = wave * RW + seg;  // this lane's row
-  const int jl = min(jr, k - 1);   // row whose memory is loaded
-  const int64_t fs = ((int64_t)prev * a.B + b) * k + jl;
+  __shared__ uint64_t s_aux[kMaxTopk * kMaxTopk]; // children's pool keys
+  __shared__ int s_nf;
+  // Every load is issued before the frontier count F arrives: rows j < k
+  // of the workspace are always readable, rows j >= F are dropped.
+  const int64_t rowid = (int64_t)b * k + jr;
+  const int li = lane < S ? lane : S - 1;
+  const int64_t fs = ((int64_t)prev * a.B + b) * k + jr;
   const int par0 = a.ws.frontier[fs];
   const float vpar0 = a.ws.frontier_val[fs];
-  float pm[kLPL], ps[kLPL];
-  uint64_t pk[kLPL][kStage];
+  float pm = a.ws.part_m[rowid * S + li];
+  float ps = a.ws.part_s[rowid * S + li];
+  uint64_t pk[KST];
 #pragma unroll
-  for (int l = 0; l < kLPL; ++l) {
-    const int li = min(q + l * SP, S - 1);
-    const int64_t e = e0 + (int64_t)jl * S + li;
-    pm[l] = a.ws.part_m[e];
-    ps[l] = a.ws.part_s[e];
-#pragma unroll
-    for (int r = 0; r < kStage; ++r)
-      pk[l][r] = a.ws.part_keys[((int64_t)(b * k + jl) * kMaxTopk + min(r, k - 1)) * S + li];
-  }
+  for (int r = 0; r < KST; ++r)
+    pk[r] = a.ws.part_keys[(rowid * kMaxTopk + min(r, k - 1)) * S + li];
   const int P0 = a.step == 1 ? 0 : a.ws.pool_count[b];
   const int F = a.step == 1 ? 1 : a.ws.frontier_count[prev * a.B + b];
   if (F == 0) {
     empty_frontier(a, b);
     return;
   }
+  if (tid == 0) s_nf = 0;
   // phase: partials read
   const bool on_row = jr < F;
-#pragma unroll
-  for (int l = 0; l < kLPL; ++l) {
-    const bool on = on_row && l < LPL && q + l * SP < S;
-    if (!on) {
-      pm[l] = -INFINITY;
-      ps[l] = 0.f;
-    }
-#pragma unroll
-    for (int r = 0; r < kStage; ++r)
-      if (!on || r >= k) pk[l][r] = 0;
+  if (!on_row || lane >= S) {
+    pm = -INFINITY;
+    ps = 0.f;
   }
+#pragma unroll
+  for (int r = 0; r < KST; ++r)
+    if (!on_row || lane >= S || r >= k) pk[r] = 0;
   const int par = a.step > 1 ? par0 : -1;
   const float vpar = a.step > 1 ? vpar0 : 1.0f;
-  float m = pm[0];
-#pragma unroll
-  for (int l = 1; l < kLPL; ++l) m = fmaxf(m, pm[l]);
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1)
-    if (d < SP) m = fmaxf(m, xor_lane_rt(m, d));
-  float sum = 0.f;
-#pragma unroll
-  for (int l = 0; l < kLPL; ++l)
-    sum += pm[l] > -INFINITY ? ps[l] * __builtin_amdgcn_exp2f((pm[l] - m) * kLog2e) : 0.f;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1)
-    if (d < SP) sum += xor_lane_rt(sum, d);
+  const float m = wave_max_f32(pm);
+  const float sum =
+      wave_sum_f32(pm > -INFINITY ? ps * __builtin_amdgcn_exp2f((pm - m) * kLog2e) : 0.f);
   // phase: row max and sum
-  // k-th largest list head of the segment, bit by bit on the ordered logit
+  // k-th largest list head, bit by bit on the ordered logit
   uint64_t Lk = 0;
   if (S >= k) {
-    uint32_t hk[kLPL];
-#pragma unroll
-    for (int l = 0; l < kLPL; ++l) hk[l] = (uint32_t)(pk[l][0] >> 32);  // 0 for no key
+    const uint32_t hk = (uint32_t)(pk[0] >> 32);  // 0 for no key
     uint32_t t = 0;
 #pragma unroll
     for (int bit = 31; bit >= (BF16 ? 16 : 0); --bit) {
       const uint32_t cand = t | (1u << bit);
-      int c = 0;
-#pragma unroll
-      for (int l = 0; l < kLPL; ++l) c += __popcll(__ballot(hk[l] >= cand) & segmask);
-      if (c >= k) t = cand;
+      if (__popcll(__ballot(hk >= cand)) >= k) t = cand;
     }
     Lk = (uint64_t)t << 32;
   }
   // phase: row bound
   // keys at or above the bound: a prefix of each list; a list whose staged
   // keys all qualify may hold more (then the row takes the exact path)
-  int cq = 0, cl[kLPL];
-  bool more = false;
+  int cl = 0;
 #pragma unroll
-  for (int l = 0; l < kLPL; ++l) {
-    cl[l] = 0;
-#pragma unroll
-    for (int r = 0; r < kStage; ++r) cl[l] += (pk[l][r] != 0 && pk[l][r] >= Lk) ? 1 : 0;
-    cq += cl[l];
-    more |= cl[l] == kStage && k > kStage;
-  }
-  // segment prefix sum and total of cq (<= kLPL * kStage), one ballot per bit
-  int off = 0, n = 0;
-#pragma unroll
-  for (int bit = 0; bit < 6; ++bit) {
-    const uint64_t bm = __ballot((cq >> bit) & 1);
-    off += __popcll(bm & below) << bit;
-    n += __popcll(bm & segmask) << bit;
-  }
-  const bool fits = n <= kRowCap && (__ballot(more) & segmask) == 0ull;
-  // phase: row prefix
+  for (int r = 0; r < KST; ++r) cl += (pk[r] != 0 && pk[r] >= Lk) ? 1 : 0;
+  const bool more = cl == KST && k > KST;
+  int n;
+  const int off = wave_excl_prefix_small(cl, &n);
+  const bool fits = n <= 64 && __ballot(more) == 0ull;
+  uint64_t* lst = &s_rc[jr * 64];
   if (on_row && fits) {
-    uint64_t* lst = &s_rc[jr * kRowCap + off];
-    int o = 0;
 #pragma unroll
-    for (int l = 0; l < kLPL; ++l) {
-#pragma unroll
-      for (int r = 0; r < kStage; ++r)
-        if (r < cl[l]) lst[o + r] = pk[l][r];
-      o += cl[l];
-    }
+    for (int r = 0; r < KST; ++r)
+      if (r < cl) lst[off + r] = pk[r];
   }
   wave_lds_fence();
   // phase: row list written
   if (on_row && fits) {
-    const uint64_t* lst = &s_rc[jr * kRowCap];
-    for (int i = q; i < n; i += SP) {
+    for (int i = lane; i < n; i += 64) {
       const uint64_t me = lst[i];
       int rank = 0;
 #pragma unroll 8
       for (int t = 0; t < n; ++t) rank += lst[t] > me;
       if (rank < k) s_rk[jr * kMaxTopk + rank] = me;
     }
-  }
-  // phase: row ranked
-  // A row whose candidates do not fit the staged keys (many equal or
-  // clustered logits) takes k rounds of maximum over all of its lists'
-  // keys (at most 64 lists x 16 ranks: 16 per lane, loaded once), with
-  // the whole wave.
-  for (int sg = 0; sg < RW; ++sg) {
-    const int jo = wave * RW + sg;
-    if (jo >= F) break;
-    if ((__ballot(!fits) & (SP == 64 ? ~0ull : ((1ull << SP) - 1ull) << (sg * SP))) == 0ull)
-      continue;
-    const uint64_t* rk = &a.ws.part_keys[(int64_t)(b * k + jo) * kMaxTopk * S];  // [rank][list]
+  } else if (on_row) {
+    // every key of the row, at most 64 lists x 16 ranks (16 per lane)
+    const uint64_t* rk = &a.ws.part_keys[rowid * kMaxTopk * S];  // [rank][list]
     uint64_t v[kMaxTopk];
 #pragma unroll
     for (int i = 0; i < kMaxTopk; ++i) {
@@ -486,130 +414,76 @@ __device__ __forceinline__ void merge_sequence(const DraftArgs& a, const FixedFr
       for (int i = 0; i < kMaxTopk; ++i)
         if (v[i] < prevk && v[i] > best) best = v[i];
       const uint64_t w = wave_max_u64(best);
-      if (lane == 0) s_rk[jo * kMaxTopk + r] = w;
+      if (lane == 0) s_rk[jr * kMaxTopk + r] = w;
       prevk = w;
     }
   }
   wave_lds_fence();
-  // phase: row merged
+  // phase: row ranked
   // Children of the row, in rank order (conf decreasing): child r of row
   // jr is pool node P0 + jr * k + r.
-  if (on_row) {
-    for (int r = q; r < k; r += SP) {
-      const uint64_t key = s_rk[jr * kMaxTopk + r];
-      const int tok = (int)id_of(key);
-      const float conf = __builtin_amdgcn_exp2f((logit_of(key) - m) * kLog2e) / sum;
-      const float val = __fmul_rn(vpar, conf);
-      const int ci = jr * k + r, pi = P0 + ci;
-      a.ws.pool_token[pb + pi] = tok;
-      a.ws.pool_parent[pb + pi] = par;
-      a.ws.pool_depth[pb + pi] = a.step;
-      a.ws.pool_conf[pb + pi] = conf;
-      a.ws.pool_value[pb + pi] = val;
-      s_aux[ci] = pool_key(val, a.step, tok, pi);
-    }
+  const int64_t pb = (int64_t)b * a.cap;
+  if (on_row && lane < k) {
+    const uint64_t key = s_rk[jr * kMaxTopk + lane];
+    const int tok = (int)id_of(key);
+    const float conf = __builtin_amdgcn_exp2f((logit_of(key) - m) * kLog2e) / sum;
+    const float val = __fmul_rn(vpar, conf);
+    const int ci = jr * k + lane, pi = P0 + ci;
+    a.ws.pool_token[pb + pi] = tok;
+    a.ws.pool_parent[pb + pi] = par;
+    a.ws.pool_depth[pb + pi] = a.step;
+    a.ws.pool_conf[pb + pi] = conf;
+    a.ws.pool_value[pb + pi] = val;
+    s_aux[ci] = pool_key(val, a.step, tok, pi);
   }
-  const int n_new = F * k;  // <= 256 = NT
-  if (tid == 0) {
-    a.ws.pool_count[b] = P0 + n_new;
-    if (a.step == 1) a.ws.root_token[b] = a.root_tokens[b];
-  }
+  const int n_new = F * k;  // <= k * k: four threads per child fit the k waves
   __syncthreads();
   // phase: children appended
-  if (wave != 0) return;
-  // ---- next frontier (wave 0): the k most valuable children ---------------
-  // Lane l holds children l, l+64, l+128, l+192.  The k-th largest lane
-  // maximum of the keys' top 32 bits bounds the top 32 bits of the k-th
-  // largest key from below; the keys at or above it are ranked by counting
-  // and the top k, in value order, become the frontier (those below the
-  // expansion threshold, a suffix, stay unexpanded).
-  int nf = 0;
+  const int fb = (cur * a.B + b) * k;
   if constexpr (FIXED) {
     // Fixed shape: next-frontier node i is child fx->ci[i] of this step.
-    bool kept = false;
-    if (lane < k) {
+    if (tid < k) {
       int ci = -1;
 #pragma unroll
       for (int i = 0; i < kMaxTopk; ++i)
-        if (lane == i && i < fx->n) ci = fx->ci[i];
-      kept = ci >= 0 && ci < n_new;
+        if (tid == i && i < fx->n) ci = fx->ci[i];
+      const bool kept = ci >= 0 && ci < n_new;
       const uint64_t key = kept ? s_aux[ci] : 0;
-      const int fb = (cur * a.B + b) * k;
-      a.ws.frontier[fb + lane] = kept ? pool_index_of(key) : -1;
-      a.ws.frontier_val[fb + lane] = kept ? pool_value_of(key) : 0.0f;
-      a.next_tokens[(int64_t)b * k + lane] =
-          kept ? (int)((1u << 18) - 1u - (uint32_t)((key >> 12) & 0x3FFFFu)) : -1;
+      a.ws.frontier[fb + tid] = kept ? pool_index_of(key) : -1;
+      a.ws.frontier_val[fb + tid] = kept ? pool_value_of(key) : 0.0f;
+      a.next_tokens[(int64_t)b * k + tid] = kept ? pool_token_of(key) : -1;
+      if (kept) atomicAdd(&s_nf, 1);
     }
-    nf = __popcll(__ballot(kept));
-  } else {
-    if (a.step < a.D) {
-      uint64_t ck[4];
-      uint32_t hmax = 0;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int t = lane + 64 * u;
-        ck[u] = t < n_new ? s_aux[t] : 0;
-        const uint32_t hi = (uint32_t)(ck[u] >> 32);
-        hmax = hi > hmax ? hi : hmax;
-      }
-      const uint32_t T = wave_kth_largest_u32(hmax, k, 0);
-      int cq = 0;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) cq += (ck[u] != 0 && (uint32_t)(ck[u] >> 32) >= T) ? 1 : 0;
-      int n;
-      const int off = wave_excl_prefix_small(cq, &n);
-      uint64_t* wbuf = &s_fb[0];
-      const int fb = (cur * a.B + b) * k;
-      if (n <= kWaveCap) {
-        int o = off;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (ck[u] != 0 && (uint32_t)(ck[u] >> 32) >= T) wbuf[o++] = ck[u];
-        wave_lds_fence();
-        bool kept = false;
-        if (lane < n) {
-          const uint64_t me = wbuf[lane];
-          int rank = 0;
-#pragma unroll 8
-          for (int q = 0; q < n; ++q) rank += wbuf[q] > me;
-          if (rank < k) {
-            kept = !(pool_value_of(me) < a.thr);
-            a.ws.frontier[fb + rank] = kept ? pool_index_of(me) : -1;
-            a.ws.frontier_val[fb + rank] = pool_value_of(me);
-            // token field of the pool key: bits 12..29 hold 2^18 - 1 - token
-            a.next_tokens[(int64_t)b * k + rank] =
-                kept ? (int)((1u << 18) - 1u - (uint32_t)((me >> 12) & 0x3FFFFu)) : -1;
-          }
-        }
-        nf = __popcll(__ballot(kept));
-      } else {
-        // Many equal values: k rounds of wave maximum.
-        uint64_t prevk = ~0ull;
-        for (int r = 0; r < k; ++r) {
-          uint64_t best = 0;
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (ck[u] < prevk && ck[u] > best) best = ck[u];
-          const uint64_t w = wave_max_u64(best);
-          const bool kept = w != 0 && !(pool_value_of(w) < a.thr);
-          if (lane == 0) {
-            a.ws.frontier[fb + r] = kept ? pool_index_of(w) : -1;
-            a.ws.frontier_val[fb + r] = pool_value_of(w);
-            a.next_tokens[(int64_t)b * k + r] =
-                kept ? (int)((1u << 18) - 1u - (uint32_t)((w >> 12) & 0x3FFFFu)) : -1;
-          }
-          nf += kept ? 1 : 0;
-          prevk = w;
-        }
-      }
-    } else if (lane < k) {
-      a.ws.frontier[(cur * a.B + b) * k + lane] = -1;
-      a.next_tokens[(int64_t)b * k + lane] = -1;
+  } else if (a.step < a.D) {
+    // The k largest children keys: child c's rank is the number of larger
+    // keys, counted by its four threads over every fourth child.  Keys are
+    // distinct (the pool index field), so the ranks are too.  Those below
+    // the expansion threshold (a suffix: value leads the key) stay
+    // unexpanded.
+    const int c = tid >> 2, part = tid & 3;
+    const uint64_t me = c < n_new ? s_aux[c] : ~0ull;
+    int cnt = 0;
+#pragma unroll 4
+    for (int j = part; j < n_new; j += 4) cnt += s_aux[j] > me ? 1 : 0;
+    cnt += xor_lane<1>(cnt);
+    cnt += xor_lane<2>(cnt);
+    if (part == 0 && c < n_new && cnt < k) {
+      const bool kept = !(pool_value_of(me) < a.thr);
+      a.ws.frontier[fb + cnt] = kept ? pool_index_of(me) : -1;
+      a.ws.frontier_val[fb + cnt] = pool_value_of(me);
+      a.next_tokens[(int64_t)b * k + cnt] = kept ? pool_token_of(me) : -1;
+      if (kept) atomicAdd(&s_nf, 1);
     }
+  } else if (tid < k) {
+    a.ws.frontier[fb + tid] = -1;
+    a.next_tokens[(int64_t)b * k + tid] = -1;
   }
-  if (lane == 0) {
-    a.ws.frontier_count[cur * a.B + b] = nf;
-    a.next_count[b] = nf;
+  __syncthreads();
+  if (tid == 0) {
+    a.ws.pool_count[b] = P0 + n_new;
+    if (a.step == 1) a.ws.root_token[b] = a.root_tokens[b];
+    a.ws.frontier_count[cur * a.B + b] = s_nf;
+    a.next_count[b] = s_nf;
   }
   // phase: frontier written
 }
@@ -636,16 +510,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? 3 : 1
   scan_chunks<BF16, VEC, E, WAVE>(a, row, j, b, c0, min(a.cpb, a.S - c0), x, raw);
 }
 
-// Merge launch: one block per sequence.
-template <bool BF16, int LPLM, int KST>
-__global__ __launch_bounds__(kMergeWaves * 64) void draft_merge_kernel(DraftArgs a) {
-  merge_sequence<BF16, LPLM, KST, false>(a, nullptr, blockIdx.x);
+// Merge launch: one block of k waves per sequence.
+template <bool BF16, int KST>
+__global__ __launch_bounds__(1024) void draft_merge_kernel(DraftArgs a) {
+  merge_rows<BF16, KST, false>(a, nullptr, blockIdx.x);
 }
-template <bool BF16, int LPLM, int KST>
-__global__ __launch_bounds__(kMergeWaves * 64) void draft_merge_fixed_kernel(DraftArgs a,
-                                                                            FixedFrontier fx) {
-  merge_sequence<BF16, LPLM, KST, true>(a, &fx, blockIdx.x);
+template <bool BF16, int KST>
+__global__ __launch_bounds__(1024) void draft_merge_fixed_kernel(DraftArgs a, FixedFrontier fx) {
+  merge_rows<BF16, KST, true>(a, &fx, blockIdx.x);
 }
+
+// Keys staged per list: four when a row has many lists (its top k then
+// almost always lie within the first four of each), eight with few.
+constexpr int merge_stage(int parts) { return parts > 16 ? 4 : 8; }
 
 hipError_t launch_draft_merge(const Plan& p, const DraftWs& w, int step,
                               const int32_t* root_tokens, int parts,
@@ -667,11 +544,8 @@ hipError_t launch_draft_merge(const Plan& p, const DraftWs& w, int step,
   a.step = step;
   a.cap = p.cap;
   a.thr = p.cfg.expand_threshold;
-  int RW = 1;
-  while (kMergeWaves * RW < p.k) RW <<= 1;
-  if (parts > 2 * (64 / RW)) draft_merge_kernel<false, 4, 4><<<p.B, kMergeWaves * 64, 0, s>>>(a);
-  else if (parts > 64 / RW) draft_merge_kernel<false, 2, 4><<<p.B, kMergeWaves * 64, 0, s>>>(a);
-  else draft_merge_kernel<false, 1, 8><<<p.B, kMergeWaves * 64, 0, s>>>(a);
+  if (merge_stage(parts) == 4) draft_merge_kernel<false, 4><<<p.B, 64 * p.k, 0, s>>>(a);
+  else draft_merge_kernel<false, 8><<<p.B, 64 * p.k, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -711,24 +585,16 @@ hipError_t launch_draft_step(const Plan& p, const DraftWs& w, int step,
   if (wv) ET_SCAN(true);
   else ET_SCAN(false);
 #undef ET_SCAN
-  // lists per lane of the merge: rows per wave RW (NW * RW >= k), 64 / RW
-  // lanes per row
-  int RW = 1;
-  while (kMergeWaves * RW < p.k) RW <<= 1;
-  // lists per lane: as many as the row's lists need (the bound search
-  // takes one ballot per list slot and bit)
-  const int lpl = (a.parts + 64 / RW - 1) / (64 / RW);
-#define ET_MERGE(BF, L, K)                                                               \
+#define ET_MERGE(BF, K)                                                                  \
   do {                                                                                   \
-    if (fixed) draft_merge_fixed_kernel<BF, L, K><<<p.B, kMergeWaves * 64, 0, s>>>(a, *fixed); \
-    else draft_merge_kernel<BF, L, K><<<p.B, kMergeWaves * 64, 0, s>>>(a);               \
+    if (fixed) draft_merge_fixed_kernel<BF, K><<<p.B, 64 * p.k, 0, s>>>(a, *fixed);      \
+    else draft_merge_kernel<BF, K><<<p.B, 64 * p.k, 0, s>>>(a);                          \
   } while (0)
-  if (bf && lpl > 2) ET_MERGE(true, 4, 4);
-  else if (bf && lpl == 2) ET_MERGE(true, 2, 4);
-  else if (bf) ET_MERGE(true, 1, 8);
-  else if (lpl > 2) ET_MERGE(false, 4, 4);
-  else if (lpl == 2) ET_MERGE(false, 2, 4);
-  else ET_MERGE(false, 1, 8);
+  const int kst = merge_stage(a.parts);
+  if (bf && kst == 4) ET_MERGE(true, 4);
+  else if (bf) ET_MERGE(true, 8);
+  else if (kst == 4) ET_MERGE(false, 4);
+  else ET_MERGE(false, 8);
 #undef ET_MERGE
   return hipGetLastError();
 }
