@@ -283,6 +283,42 @@ def test_frontier_and_threshold_rule(seed):
         assert (par == p).sum() == w.topk
 
 
+def _boundary_draft(w, ids=(5, 40)):
+    """Every draft row: logit 0 at two ids, -inf elsewhere, so each row's
+    softmax gives exactly 1/2 to both ids (a closed form)."""
+    row = np.full(w.vocab, -np.inf, np.float32)
+    row[list(ids)] = 0.0
+    draft = np.ascontiguousarray(
+        np.broadcast_to(row, (w.batch, w.depth, w.topk, w.vocab)))
+    return gen.f32_to_bf16_bits(draft) if w.logits_dtype == "bf16" else draft
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_value_equal_to_threshold_is_expanded(dtype):
+    """[P3] Expand stage: a node stays unexpanded only when its value is
+    below the threshold.  With conf = 1/2 exactly (two equal finite
+    logits), threshold 0.5 puts both children of the root exactly on it:
+    they are expanded; their children (value 1/4) are not.  A '<=' slip
+    in the stop rule leaves the root's children unexpanded."""
+    w = _small(vocab=64, topk=2, depth=3, budget_n=8, threshold=0.5,
+               logits_dtype=dtype)
+    st = oracle.TreeState(w)
+    roots = np.array([7], np.int32)
+    draft = _boundary_draft(w)
+    nt, nc = oracle.draft_step(w, st, 1, roots, draft[:, 0])
+    assert st.conf[0, 0] == 0.5 and st.value[0, 0] == 0.5
+    assert int(nc[0]) == 2 and sorted(nt[0].tolist()) == [5, 40]
+    nt, nc = oracle.draft_step(w, st, 2, roots, draft[:, 1])
+    assert (st.value[0, 2:6] == 0.25).all()
+    assert int(nc[0]) == 0 and (nt[0] == -1).all()
+    assert int(st.count[0]) == 6
+    # just above the threshold: the root's children stop as well
+    w2 = w.with_(threshold=float(np.nextafter(np.float32(0.5), np.float32(1))))
+    st2 = oracle.TreeState(w2)
+    _, nc2 = oracle.draft_step(w2, st2, 1, roots, draft[:, 0])
+    assert int(nc2[0]) == 0
+
+
 def test_stop_when_frontier_empty():
     """All values below the threshold after layer 1: nothing is expanded
     again and the pool keeps only the root's children."""
