@@ -51,13 +51,18 @@ __device__ __forceinline__ uint32_t wave_kth_largest_u32(uint32_t key, int k, in
   }
   return t;
 }
-// The same over float values through their order-preserving image; values
-// from bf16 have 16 significant bits.  (For negative bf16 values the image
-// has ones in its low bits, so the result can sit slightly below the exact
-// k-th largest: still a lower bound.)
+// The same over float values through their order-preserving image.  Values
+// from bf16 have 16 significant bits: the search fixes the image's top 16
+// bits, and the low 16 are those every bf16 image has (zeros for a
+// non-negative value, ones for a negative one), so the result is the exact
+// k-th largest.  (Left at zero for a negative value, they would make an
+// image below that of -inf, i.e. a NaN, against which every comparison
+// fails: a wave with fewer than k finite values would lose its top ones.)
 template <bool BF16>
 __device__ __forceinline__ float wave_kth_largest(float v, int k) {
-  return unordered_f32(wave_kth_largest_u32(ordered_f32(v), k, BF16 ? 16 : 0));
+  uint32_t t = wave_kth_largest_u32(ordered_f32(v), k, BF16 ? 16 : 0);
+  if (BF16 && !(t & 0x80000000u)) t |= 0xFFFFu;
+  return unordered_f32(t);
 }
 
 // Smallest logit key whose logit is >= x.

@@ -15,6 +15,7 @@ import torch
 import oracle
 from synth import WORKLOADS, gen
 
+import gpu_util
 from gpu_util import (ATTN_TOL_BF16, ATTN_TOL_F32, bf16_dev_to_f64,
                       check_draft_step, dev_inputs, make_inputs,
                       random_path_targets, state_from_export, to_dev)
@@ -78,6 +79,14 @@ VARIANTS = {
                                   sharpness=tuple([2.5, 0.8] * 8),
                                   n_q_heads=2, n_kv_heads=1, head_dim=64,
                                   prefix_cap=64, prefix_range=(1, 64), seed=14),
+    # 128-row attention blocks (G * T rows = 488 per kv head, no key
+    # split): the three-buffer path, compared in full
+    "rows128_bf16": TINY.with_(batch=8, vocab=5000, topk=10, depth=8,
+                               budget_n=60, threshold=0.0, logits_dtype="bf16",
+                               sharpness=(2.5, 0.8) * 4, n_q_heads=64,
+                               n_kv_heads=8, head_dim=128, prefix_cap=256,
+                               prefix_range=(256, 256), qkv_dtype="bf16",
+                               seed=15),
     "f32_gqa": TINY.with_(batch=2, vocab=1500, topk=3, depth=4, budget_n=10,
                           threshold=0.0, sharpness=(2.0, 1.0), n_q_heads=4,
                           n_kv_heads=2, head_dim=128, prefix_cap=100,
@@ -121,6 +130,7 @@ def _run(name, tied=False):
     roots = inp["root_tokens"]
     before = oracle.TreeState(w)
     events = 0
+    first_event = np.full(w.batch, w.depth + 1, np.int64)  # step of b's first event
     ora_indep = oracle.TreeState(w)
     for step in range(1, w.depth + 1):
         plan.draft_step(step, dev["root_tokens"], dev["draft"][:, step - 1])
@@ -130,8 +140,11 @@ def _run(name, tied=False):
         ora_after = before.copy()
         ora_next = oracle.draft_step(w, ora_after, step, roots,
                                      inp["draft"][:, step - 1])
-        events += check_draft_step(w, before, gpu_after, ora_after, gpu_next,
-                                   ora_next)
+        ev = check_draft_step(w, before, gpu_after, ora_after, gpu_next,
+                              ora_next)
+        events += len(ev)
+        for b in ev:
+            first_event[b] = min(first_event[b], step)
         oracle.draft_step(w, ora_indep, step, roots, inp["draft"][:, step - 1])
         before = gpu_after
     plan.rerank()
@@ -141,8 +154,10 @@ def _run(name, tied=False):
                   conf=plan.conf.cpu().numpy(), value=plan.value.cpu().numpy(),
                   n_kept=plan.n_kept.cpu().numpy())
     res = dict(w=w, inp=inp, dev=dev, plan=plan, gpu_state=before,
-               ora_indep=ora_indep, events=events, gpu_rr=gpu_rr)
+               ora_indep=ora_indep, events=events, first_event=first_event,
+               gpu_rr=gpu_rr)
     _cache[(name, tied)] = res
+    gpu_util.NEAR_TIES[f"{name}{' tied' if tied else ''}"] = (events, w.batch * w.depth)
     print(f"[parity] {name}: draft steps done, near-tie events {events}",
           flush=True)
     return res
@@ -158,19 +173,35 @@ def test_draft_steps_replay_tied(name):
     _check_replay(_run(name, tied=True))
 
 
+# Near-tie events accepted per replay, at most: one sequence-step in 20
+# (they need two candidates of one layer within 1e-5 relative of each
+# other, rare on these landscapes), and at least 2 for the smallest runs.
+def _near_tie_bound(w):
+    return max(2, (w.batch * w.depth) // 20)
+
+
 def _check_replay(r):
-    name, w = r["w"].name, r["w"]
-    if r["events"] == 0:
-        # no near tie anywhere: the independent oracle run must match
-        g, o = r["gpu_state"], r["ora_indep"]
-        np.testing.assert_array_equal(g.count, o.count)
-        for b in range(w.batch):
-            n = int(o.count[b])
-            for f in ("token", "parent", "depth"):
-                np.testing.assert_array_equal(getattr(g, f)[b, :n],
-                                              getattr(o, f)[b, :n])
-    else:
-        print(f"{name}: {r['events']} near-tie event(s) accepted")
+    """Against the independent oracle run (its own frontiers throughout):
+    a sequence's pool must match it node for node up to and including the
+    first step at which a near tie let the two frontiers differ (all of it
+    when there was none); the number of near-tie events is bounded."""
+    w = r["w"]
+    g, o = r["gpu_state"], r["ora_indep"]
+    for b in range(w.batch):
+        upto = int(r["first_event"][b])  # layers built from equal frontiers
+        if upto > w.depth:
+            assert int(g.count[b]) == int(o.count[b]), f"b={b} pool count"
+        n = int(min(g.count[b], o.count[b]))
+        keep = o.depth[b, :n] <= upto
+        n_cmp = int(np.argmin(keep)) if not keep.all() else n  # depth-ordered prefix
+        for f in ("token", "parent", "depth"):
+            np.testing.assert_array_equal(getattr(g, f)[b, :n_cmp],
+                                          getattr(o, f)[b, :n_cmp],
+                                          err_msg=f"b={b} {f}")
+    bound = _near_tie_bound(w)
+    assert r["events"] <= bound, (
+        f"{r['events']} near-tie events in {w.batch * w.depth} sequence-steps "
+        f"(bound {bound})")
 
 
 @pytest.mark.parametrize("name", ALL)
@@ -192,11 +223,12 @@ def _check_rerank_mask(r):
         np.testing.assert_array_equal(g[f], ora[f], err_msg=f)
     np.testing.assert_array_equal(g["conf"], ora["conf"])
     np.testing.assert_array_equal(g["value"], ora["value"])
-    # independent oracle run: equal when no near-tie event happened
-    if r["events"] == 0:
-        ind = oracle.rerank(w, r["ora_indep"])
-        np.testing.assert_array_equal(g["tokens"], ind["tokens"])
-        np.testing.assert_array_equal(g["parent_slot"], ind["parent_slot"])
+    # independent oracle run: equal for every sequence without a near tie
+    ind = oracle.rerank(w, r["ora_indep"])
+    for b in np.nonzero(r["first_event"] > w.depth)[0]:
+        np.testing.assert_array_equal(g["tokens"][b], ind["tokens"][b])
+        np.testing.assert_array_equal(g["parent_slot"][b], ind["parent_slot"][b])
+        assert gpu_util.rel_close(g["value"][b], ind["value"][b]).all(), f"b={b} value"
     plan.tree_mask(r["dev"]["prefix_len"])
     torch.cuda.synchronize()
     om = oracle.tree_mask(w, g["parent_slot"], g["n_kept"],
@@ -205,6 +237,13 @@ def _check_rerank_mask(r):
                                   om["mask"])
     np.testing.assert_array_equal(plan.depth.cpu().numpy(), om["depth"])
     np.testing.assert_array_equal(plan.pos_ids.cpu().numpy(), om["pos_ids"])
+
+
+# Attention outputs compared in full against the oracle (OpenMP over
+# sequences and heads) up to this many (query row, key) pairs, which covers
+# every workload here (the 70B shape has 5.1e8, about 15 s on 8 threads);
+# above it, sampled rows.
+ATTN_FULL_KEYS = 6e8
 
 
 def _attn_rows(w, n_kept, rng, limit):
@@ -235,7 +274,7 @@ def test_tree_attention_parity(name):
     n_kept = plan.n_kept.cpu().numpy()
     tol = ATTN_TOL_F32 if w.qkv_dtype == "f32" else ATTN_TOL_BF16
     total_keys = w.batch * w.T * w.n_q_heads * (w.prefix_cap + w.T)
-    if total_keys <= 3e7:
+    if total_keys <= ATTN_FULL_KEYS:
         ref = oracle.tree_attention(w, inp["attn"], inp["prefix_len"], mask,
                                     n_kept)
         err = np.abs(out - ref).max()
@@ -595,11 +634,18 @@ def test_accept_sample_distribution(dtype):
 def test_target_rows_past_n_kept_are_ignored(name):
     """Target rows s > n_kept are loaded before n_kept is known but never
     used: NaN there changes no output bit (greedy and sampled walks)."""
-    r = _run(name)
-    w, plan, inp = r["w"], r["plan"], r["inp"]
-    n_kept = r["gpu_rr"]["n_kept"]
-    if not (n_kept < w.budget_n).any():
-        pytest.skip("every sequence kept N nodes")
+    # A budget above the pool's capacity: every sequence keeps fewer than
+    # N nodes, so rows n_kept + 1 .. N exist and are poisoned below.
+    w0 = _w(name)
+    w = w0.with_(budget_n=min(255, w0.pool_cap + 7))
+    inp = make_inputs(w)
+    dev = dev_inputs(inp)
+    plan = _lib().Plan(w)
+    plan.cycle(dev["root_tokens"], dev["draft"], dev["prefix_len"], dev["attn"],
+               dev["target"])
+    torch.cuda.synchronize()
+    n_kept = plan.n_kept.cpu().numpy()
+    assert (n_kept < w.budget_n).all()
     td = to_dev(inp["target"])
     plan.accept(td)
     torch.cuda.synchronize()
@@ -783,6 +829,41 @@ def test_rows_past_frontier_are_ignored(name):
         assert torch.equal(getattr(plan_a, t), getattr(plan_b, t)), t
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_value_equal_to_threshold_is_expanded(dtype):
+    """EAGLE notes, Expand stage: only values below the threshold stop.
+    Every draft row has logit 0 at two ids and -inf elsewhere, so the
+    root's children have conf and value exactly 1/2; with threshold 0.5
+    both are expanded (their children, value 1/4, are not).  Each step
+    is compared with the oracle from the same state."""
+    d = _lib()
+    w = TINY.with_(threshold=0.5, topk=2, depth=3, budget_n=8,
+                   logits_dtype=dtype, seed=4)
+    row = np.full(w.vocab, -np.inf, np.float32)
+    row[[5, 700]] = 0.0
+    draft = np.ascontiguousarray(np.broadcast_to(row, (w.batch, w.depth, w.topk, w.vocab)))
+    if dtype == "bf16":
+        draft = gen.f32_to_bf16_bits(draft)
+    roots = gen.root_tokens(w)
+    ddraft, droots = to_dev(draft), to_dev(roots)
+    plan = d.Plan(w)
+    before = oracle.TreeState(w)
+    counts = []
+    for step in range(1, w.depth + 1):
+        plan.draft_step(step, droots, ddraft[:, step - 1])
+        torch.cuda.synchronize()
+        gpu_after = state_from_export(w, plan.export_pool(), roots)
+        gpu_next = (plan.next_tokens.cpu().numpy(), plan.next_count.cpu().numpy())
+        ora_after = before.copy()
+        ora_next = oracle.draft_step(w, ora_after, step, roots, draft[:, step - 1])
+        assert check_draft_step(w, before, gpu_after, ora_after, gpu_next, ora_next) == []
+        np.testing.assert_array_equal(gpu_next[0], ora_next[0])
+        counts.append(int(gpu_next[1][0]))
+        before = gpu_after
+    assert counts == [2, 0, 0]
+    assert (before.value[0, :2] == 0.5).all() and (before.value[0, 2:6] == 0.25).all()
+
+
 def test_tree_stops_when_all_below_threshold():
     """Threshold 0.9 with flat rows: step 1 expands nothing further; later
     steps leave the pool unchanged and report an empty frontier."""
@@ -827,9 +908,10 @@ def test_attention_empty_prefix():
 @pytest.mark.parametrize("name,reps", [("llama8b", 40), ("llama8b_b64", 8),
                                        ("small_bf16", 100)])
 def test_repeated_cycles_bit_identical(name, reps):
-    """Blocks of one launch hand partial results to the last-arriving block
-    through agent-coherent accesses; repeated cycles over alternating input
-    sets must reproduce the first cycle's outputs bit for bit."""
+    """Scan blocks publish partial results that a second launch merges, and
+    attention splits publish (O, m, l) partials combined by a merge
+    launch; repeated cycles over alternating input sets must reproduce the
+    first cycle's outputs bit for bit."""
     d = _lib()
     w = _w(name)
     sets = [dev_inputs(make_inputs(w, seed=w.seed + i)) for i in range(2)]
