@@ -5,6 +5,7 @@ this package holds its HIP sources (csrc/), the build step and a thin
 ctypes binding that passes torch device pointers and streams through.
 """
 from .binding import (EXPORTS, EtError, Plan, et_accept,  # noqa: F401
+                      et_accept_noalloc,
                       et_accept_sample, et_config, et_draft_step_hidden,
                       et_draft_step_static,
                       et_set_static_shape, et_static_tree,

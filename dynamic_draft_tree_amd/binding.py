@@ -25,7 +25,7 @@ EXPORTS = ("et_plan_create", "et_plan_destroy", "et_workspace_bytes",
            "et_rerank", "et_tree_mask", "et_tree_attention", "et_accept",
            "et_accept_sample", "et_kv_commit", "et_pool_export",
            "et_set_static_shape", "et_draft_step_static", "et_static_tree",
-           "et_draft_step_hidden", "et_last_error")
+           "et_draft_step_hidden", "et_accept_noalloc", "et_last_error")
 
 
 class et_config(ctypes.Structure):
@@ -73,6 +73,8 @@ def lib():
             "et_accept": ([vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "et_accept_sample": ([vp, vp, vp, i64, i64, vp, vp, vp, f32, vp, vp, vp, vp,
                                   vp], ctypes.c_int),
+            "et_accept_noalloc": ([vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp],
+                                  ctypes.c_int),
             "et_kv_commit": ([vp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "et_set_static_shape": ([vp, vp, vp, i32], ctypes.c_int),
             "et_draft_step_hidden": ([vp, vp, i32, vp, vp, i64, i64, vp, i32, vp, vp, vp],
@@ -235,6 +237,15 @@ def et_accept(plan, ws, target_logits, tokens, parent_slot, n_kept,
                            _ptr(out_tokens), _stream(stream)))
 
 
+def et_accept_noalloc(plan, target_logits, tokens, parent_slot, n_kept,
+                      accept_len, path_slots, out_tokens, stream=None):
+    bs, rs = _rows(target_logits)
+    _check(lib().et_accept_noalloc(plan, _ptr(target_logits), bs, rs,
+                                   _ptr(tokens), _ptr(parent_slot), _ptr(n_kept),
+                                   _ptr(accept_len), _ptr(path_slots),
+                                   _ptr(out_tokens), _stream(stream)))
+
+
 def et_accept_sample(plan, ws, target_logits, tokens, parent_slot, n_kept,
                      temperature, uniforms, accept_len, path_slots, out_tokens,
                      stream=None):
@@ -349,6 +360,12 @@ class Plan:
         et_accept(self.handle, self.ws, target_logits, self.tokens,
                   self.parent_slot, self.n_kept, self.accept_len,
                   self.path_slots, self.out_tokens, stream)
+
+    def accept_noalloc(self, target_logits, stream=None):
+        """et_accept on the library's fixed scratch (no workspace)."""
+        et_accept_noalloc(self.handle, target_logits, self.tokens,
+                          self.parent_slot, self.n_kept, self.accept_len,
+                          self.path_slots, self.out_tokens, stream)
 
     def accept_sample(self, target_logits, temperature, uniforms, stream=None):
         """Ratio-test acceptance at temperature > 0; uniforms [B][T] f32."""

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "internal.h"
@@ -566,6 +567,85 @@ int et_accept(et_plan_t plan, void* ws, const void* target_logits,
       et::launch_accept(p, et::accept_ws(p, ws), target_logits, batch_stride,
                         row_stride, vec, tokens, parent_slot, n_kept,
                         accept_len, path_slots, out_tokens,
+                        (hipStream_t)stream),
+      fn);
+}
+
+}  // extern "C"
+
+// Scratch of et_accept_noalloc: the accept partial keys of one call.  Each
+// device the library runs on holds its own copy, at its own address.
+static __device__ __align__(256) unsigned char scratch[ET_ACCEPT_NOALLOC_SCRATCH];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, resolved with
+// hipGetSymbolAddress on the first call there and kept per device.  (In
+// host code the array's name stands for no device address.)
+int scratch_on_device(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ET_EHIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ET_EUNSUPPORTED, "%s: device %d outside 0..%d", fn, dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(ET_EHIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ET_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int et_accept_noalloc(et_plan_t plan, const void* target_logits,
+                      int64_t batch_stride, int64_t row_stride,
+                      const int32_t* tokens, const int32_t* parent_slot,
+                      const int32_t* n_kept, int32_t* accept_len,
+                      int32_t* path_slots, int32_t* out_tokens,
+                      et_stream_t stream) {
+  const char* fn = "et_accept_noalloc";
+  CHECK_PTR(plan);
+  CHECK_PTR(target_logits);
+  CHECK_PTR(tokens);
+  CHECK_PTR(parent_slot);
+  CHECK_PTR(n_kept);
+  CHECK_PTR(accept_len);
+  CHECK_PTR(path_slots);
+  CHECK_PTR(out_tokens);
+  et::Plan& p = *as_plan(plan);
+  if (row_stride < p.V)
+    return fail(ET_EINVAL, "%s: row_stride %lld < vocab %d", fn,
+                (long long)row_stride, p.V);
+  if (batch_stride < 0)
+    return fail(ET_EINVAL, "%s: negative batch_stride", fn);
+  // one 8-byte key per (target row, chunk, wave)
+  const size_t need = (size_t)p.B * p.T * p.s_accept * (et::kScanThreads / 64) * 8;
+  if (need > ET_ACCEPT_NOALLOC_SCRATCH)
+    return fail(ET_EINVAL, "%s: this plan needs %zu bytes of scratch, the maximum is %u "
+                "(use et_accept with a workspace)", fn, need, ET_ACCEPT_NOALLOC_SCRATCH);
+  void* sp = nullptr;
+  int rc = scratch_on_device(fn, &sp);
+  if (rc != ET_OK) return rc;
+  et::AcceptWs w;
+  w.part = static_cast<uint64_t*>(sp);
+  const int per = p.ldt == ET_BF16 ? 8 : 4;
+  const bool vec = aligned16(target_logits) && batch_stride % per == 0 &&
+                   row_stride % per == 0 && p.V >= per;
+  return hip_status(
+      et::launch_accept(p, w, target_logits, batch_stride, row_stride, vec, tokens,
+                        parent_slot, n_kept, accept_len, path_slots, out_tokens,
                         (hipStream_t)stream),
       fn);
 }

@@ -217,6 +217,29 @@ int et_accept(et_plan_t plan, void* ws, const void* target_logits,
               const int32_t* n_kept, int32_t* accept_len,
               int32_t* path_slots, int32_t* out_tokens, et_stream_t stream);
 
+/* et_accept without a workspace, for callers that cannot allocate (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the per-(row, chunk, wave) argmax keys that et_accept keeps
+ * in the workspace go to a fixed device array of the library instead,
+ * ET_ACCEPT_NOALLOC_SCRATCH bytes per device, held from the first call on
+ * that device until the process ends.  A call needs
+ *     batch * T * ceil(vocab / chunk) * 4 * 8 bytes
+ * (chunk = 16384 ids for bf16 logits, 8192 for fp32); a plan needing more
+ * is rejected with ET_EINVAL before anything is launched.  The call uses
+ * the array of the current device (the stream must belong to it).  Every
+ * call on one device shares that array: calls that overlap on one device
+ * (several streams or threads) race and must not be issued; calls on one
+ * stream are ordered.  No other state is kept between calls.  Arguments,
+ * outputs and other errors as et_accept; it allocates nothing (no
+ * hipMalloc, no hipFree). */
+#define ET_ACCEPT_NOALLOC_SCRATCH (4u << 20)
+int et_accept_noalloc(et_plan_t plan, const void* target_logits,
+                      int64_t batch_stride, int64_t row_stride,
+                      const int32_t* tokens, const int32_t* parent_slot,
+                      const int32_t* n_kept, int32_t* accept_len,
+                      int32_t* path_slots, int32_t* out_tokens,
+                      et_stream_t stream);
+
 /* Stochastic acceptance at temperature > 0 ([P1] s2.1: draft tokens are
  * accepted one after another by the ratio of target to draft probability;
  * [P1] s2.2: the tree lets the siblings of a rejected token be tried;

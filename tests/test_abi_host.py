@@ -145,3 +145,17 @@ def test_calls_validate_before_launch():
                                   nul) == binding.ET_EINVAL, bad
         assert b"temperature" in L.et_last_error()
     d.et_plan_destroy(h)
+
+
+def test_accept_noalloc_rejects_plans_beyond_its_scratch():
+    """The fixed scratch holds batch * T * chunks * 4 keys of 8 bytes: 300
+    sequences of 61 slots over 128256 bf16 ids need 4.7 MB, more than its
+    4 MiB, and the call fails before touching any pointer."""
+    w = WORKLOADS["llama8b"]
+    h = d.et_plan_create(d.make_config(w.with_(batch=300)))
+    dummy = ctypes.c_void_p(16)  # never dereferenced: rejected on the host
+    rc = binding.lib().et_accept_noalloc(h, dummy, 0, w.vocab, dummy, dummy,
+                                         dummy, dummy, dummy, dummy, None)
+    assert rc == binding.ET_EINVAL
+    assert "scratch" in binding.lib().et_last_error().decode()
+    d.et_plan_destroy(h)
