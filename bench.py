@@ -9,13 +9,17 @@ exceeds the 256 MB MALL and every cycle reads HBM.
 
 Prints one JSON line: cycles/s, the roofline of the dominant call
 (algorithmic bytes / its average duration, HIP events on the launch
-stream; a call is one or two back-to-back launches) and the CPU oracle
-timed on this host as a reported baseline.  Beside the metric, timed
-after it: the spread of the cycle time (p10 / median / p90 over groups of
-10 cycles), a streaming-copy bandwidth as the practical HBM ceiling, KV
-commit, sampled acceptance, the fixed-shape tree build
-against the dynamic one with each tree's expected accepted tokens, and
-the draft step from hidden states (LM head fused) against torch's GEMM.
+stream; a call is one or two back-to-back launches), the whole cycle's
+roofline fraction (sum over calls of max(bytes / 8 TB/s, flops / 2.5
+PFLOP/s) over the measured cycle time), per-call GB/s against the peak and
+against a measured streaming copy, and the CPU oracle timed on this host
+(one thread and all threads) as a reported baseline, with the near-tie
+events of input set 0.  Beside the metric, timed after it: the spread of
+the cycle time (p10 / median / p90 over groups of 10 cycles), KV commit,
+sampled acceptance, the fixed-shape tree build against the dynamic one
+with each tree's expected accepted tokens, the draft step from hidden
+states (LM head fused) against torch's GEMM, and the batch-64 and 70B
+workloads' cycles/s and rooflines.
 """
 from __future__ import annotations
 
@@ -184,6 +188,367 @@ def algorithmic(w, n_kept, frontier_rows, prefix_len):
                 attention_flops=flops)
 
 
+def cycle_roof_us(w, alg):
+    """Roofline time of one cycle: each call at max(bytes / HBM peak,
+    flops / bf16 MFMA peak) from its algorithmic bytes and flops (rerank
+    and mask move negligible bytes)."""
+    bw = HBM_PEAK_GBS * 1e3      # bytes per us
+    mf = MFMA_BF16_PEAK_TFLOPS * 1e6  # flops per us
+    t = sum(b / bw for b in alg["draft"])
+    t += max(alg["attention"] / bw, alg["attention_flops"] / mf)
+    t += alg["accept"] / bw
+    return t
+
+
+def call_rooflines(w, alg, avg_us, copy_gbs):
+    """Per call: algorithmic GB/s (TFLOP/s for attention too) against the
+    8 TB/s peak and against the measured streaming copy."""
+    out = {}
+    for name, byts, flops in (("draft", float(np.mean(alg["draft"])), 0.0),
+                              ("attention", alg["attention"], alg["attention_flops"]),
+                              ("accept", alg["accept"], 0.0)):
+        us = avg_us[name]
+        gbs = byts / (us * 1e-6) / 1e9
+        e = {"us": round(us, 3), "bytes": byts, "gbs": round(gbs, 1),
+             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+             "frac_copy": round(gbs / copy_gbs, 4) if copy_gbs else None}
+        if flops and w.qkv_dtype == "bf16":
+            tf = flops / (us * 1e-6) / 1e12
+            e.update({"tflops": round(tf, 1),
+                      "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
+        out[name] = e
+    return out
+
+
+def dominant_roofline(w, alg, avg_us, per_cycle_us):
+    """The roofline entry of the call with the largest time per cycle:
+    algorithmic bytes (or flops, above the ridge) per call over its
+    average duration."""
+    names = list(per_cycle_us)
+    dominant = max(names, key=lambda n: per_cycle_us[n])
+    call = {"draft": "draft_step", "accept": "accept",
+            "attention": "tree_attention"}.get(dominant)
+    bytes_per_call = {"draft": float(np.mean(alg["draft"])),
+                      "accept": alg["accept"],
+                      "attention": alg["attention"]}.get(dominant, 0.0)
+    achieved = bytes_per_call / (avg_us[dominant] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(call, w.name) if call else None,
+                "call": call or dominant,
+                "kernels": CALLS[call][0] if call else [],
+                "avg_us": round(avg_us[dominant], 3),
+                "bytes_per_call": bytes_per_call}
+    if dominant == "attention" and w.qkv_dtype == "bf16":
+        # above the ridge (flops per byte > peak flops / peak bytes) the
+        # matrix cores, not HBM, bound the call
+        flops = alg["attention_flops"]
+        if flops / bytes_per_call > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+            tf = flops / (avg_us[dominant] * 1e-6) / 1e12
+            roofline.update({"bound": "mfma", "achieved": round(tf, 1),
+                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "flops_per_call": flops})
+    return roofline
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+class Bench:
+    """One workload on one GPU: resident input sets, one HIP graph per set,
+    the timed replays, and the per-call timing pass."""
+
+    def __init__(self, w, n_sets, torch, d, gen):
+        self.w, self.torch, self.d, self.gen = w, torch, d, gen
+        t0 = time.time()
+        self.sets = []
+        seed = w.seed
+        while True:
+            s = dict(draft=gen.draft_logits(w, seed), target=gen.target_logits(w, seed),
+                     roots=gen.root_tokens(w, seed), prefix=gen.prefix_lens(w, seed),
+                     attn=gen.attention_inputs(w, seed))
+            ds = dict(draft=self.dev(s["draft"]), target=self.dev(s["target"]),
+                      roots=self.dev(s["roots"]), prefix=self.dev(s["prefix"]),
+                      attn={k: self.dev(v) for k, v in s["attn"].items()})
+            if not self.sets:
+                self.host0 = s
+                self.set_bytes = sum(t.numel() * t.element_size() for t in
+                                     [ds["draft"], ds["target"], *ds["attn"].values()])
+            else:
+                del s
+            self.sets.append(ds)
+            seed += 1000
+            want = n_sets or max(2, -(-2 * MALL_BYTES // self.set_bytes))
+            if len(self.sets) >= min(want, 64):
+                break
+        self.gen_s = time.time() - t0
+        self.plan = d.Plan(w)
+        self.stream = torch.cuda.current_stream()
+        self.graphs = None
+
+    def dev(self, a):
+        if a.dtype == np.uint16:
+            return self.torch.from_numpy(a.view(np.int16)).view(self.torch.bfloat16).cuda()
+        return self.torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    def cycle(self, ds, stream=None):
+        self.plan.cycle(ds["roots"], ds["draft"], ds["prefix"], ds["attn"],
+                        ds["target"], stream or self.stream)
+
+    def capture(self):
+        torch = self.torch
+        self.cycle(self.sets[0])  # warm the code objects before capture
+        torch.cuda.synchronize()
+        self.graphs = []
+        for ds in self.sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.cycle(ds, torch.cuda.current_stream())
+            self.graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(self, i):
+        if self.graphs is not None:
+            self.graphs[i % len(self.sets)].replay()
+        else:
+            self.cycle(self.sets[i % len(self.sets)])
+
+    def timed(self, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            self.run(i)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(steps):
+            self.run(i)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+    def spread(self, n_groups=20, per_group=10):
+        """Per-cycle time of groups of cycles (events between whole cycles,
+        all groups enqueued at once)."""
+        torch = self.torch
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_groups + 1)]
+        evs[0].record()
+        for g_ in range(n_groups):
+            for i in range(per_group):
+                self.run(g_ * per_group + i)
+            evs[g_ + 1].record()
+        torch.cuda.synchronize()
+        grp = np.array([evs[g_].elapsed_time(evs[g_ + 1]) * 1e3 / per_group
+                        for g_ in range(n_groups)])
+        return {"groups": n_groups, "cycles_per_group": per_group,
+                "p10_us": round(float(np.percentile(grp, 10)), 2),
+                "median_us": round(float(np.median(grp)), 2),
+                "p90_us": round(float(np.percentile(grp, 90)), 2)}
+
+    def per_call(self, K, spin_per_ms, hold_ms=20.0):
+        """Average duration of each call, in an eager pass bracketed by HIP
+        events on the launch stream (events recorded inside a graph cannot
+        be timed).  A spin kernel at the head of every batch holds the GPU
+        until the host has enqueued the whole batch, so the calls run back
+        to back as in the graph and the events time the GPU work, not the
+        host's launch rate.  The D draft steps of a cycle sit between one
+        pair of events."""
+        torch, w, plan, stream = self.torch, self.w, self.plan, self.stream
+        names = ["draft", "rerank", "mask", "attention", "accept"]
+        acc = {n: 0.0 for n in names}
+        cnt = {n: 0 for n in names}
+
+        def enqueue_cycle(ds, row):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for step in range(1, w.depth + 1):
+                plan.draft_step(step, ds["roots"], ds["draft"][:, step - 1], stream)
+            e1.record(stream)
+            row.append(("draft", e0, e1))
+            for n, fn in (("rerank", lambda: plan.rerank(stream)),
+                          ("mask", lambda: plan.tree_mask(ds["prefix"], stream)),
+                          ("attention", lambda: plan.tree_attention(
+                              ds["attn"]["q"], ds["attn"]["k_cache"],
+                              ds["attn"]["v_cache"], ds["attn"]["k_tree"],
+                              ds["attn"]["v_tree"], ds["prefix"], stream=stream)),
+                          ("accept", lambda: plan.accept(ds["target"], stream))):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                row.append((n, e0, e1))
+
+        per_batch = 10
+        done = starved = 0
+        while done < K:
+            nb = min(per_batch, K - done)
+            rows = []
+            torch.cuda._sleep(int(hold_ms * spin_per_ms))
+            gate = torch.cuda.Event()
+            gate.record(stream)
+            t_host = time.time()
+            for i in range(nb):
+                row = []
+                enqueue_cycle(self.sets[(done + i) % len(self.sets)], row)
+                rows.append(row)
+            host_ms = (time.time() - t_host) * 1e3
+            if gate.query():  # the GPU caught up with the host: hold longer
+                torch.cuda.synchronize()
+                starved += 1
+                if starved > 6:
+                    raise RuntimeError("bench: could not hold the GPU while enqueueing")
+                hold_ms = max(2 * hold_ms, 3 * host_ms)
+                continue
+            torch.cuda.synchronize()
+            for row in rows:
+                for n, e0, e1 in row:
+                    acc[n] += e0.elapsed_time(e1) * 1e3  # us
+                    cnt[n] += w.depth if n == "draft" else 1
+            done += nb
+        avg_us = {n: acc[n] / cnt[n] for n in names}
+        per_cycle_us = {n: acc[n] / K for n in names}
+        return avg_us, per_cycle_us, hold_ms
+
+    def algorithmic(self):
+        w = self.w
+        n_kept = self.plan.n_kept.cpu().numpy()
+        # frontier rows per step: 1 at step 1; with the threshold off every
+        # later step reads k rows per sequence
+        fr = [w.batch] + [w.batch * w.topk] * (w.depth - 1)
+        return algorithmic(w, n_kept, fr, self.host0["prefix"])
+
+    def release(self):
+        self.graphs = None
+        self.sets = None
+        self.plan = None
+        self.torch.cuda.synchronize()
+        self.torch.cuda.empty_cache()
+
+
+def spin_rate(torch):
+    """Cycles per ms of torch's spin kernel (its argument counts clock
+    cycles), to size the hold of the per-call pass."""
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    torch.cuda._sleep(2_000_000)
+    s1.record()
+    torch.cuda.synchronize()
+    return 2_000_000 / max(s0.elapsed_time(s1), 1e-3)
+
+
+def near_ties(b, oracle):
+    """The GPU tree of input set 0 against the oracle: each draft step is
+    compared with the oracle run from the GPU's own state; a frontier that
+    differs only where two oracle values lie within 1e-5 relative is a
+    near-tie event, any other difference a mismatch.  Also whether the
+    final GPU tree equals an independent oracle run (with no event, it
+    must).  Outside the timed region."""
+    torch, w, plan, ds = b.torch, b.w, b.plan, b.sets[0]
+    h = b.host0
+    roots = np.asarray(h["roots"], np.int32)
+    before = oracle.TreeState(w)
+    indep = oracle.TreeState(w)
+    events = mismatches = 0
+    for step in range(1, w.depth + 1):
+        plan.draft_step(step, ds["roots"], ds["draft"][:, step - 1])
+        torch.cuda.synchronize()
+        ex = plan.export_pool()
+        after = oracle.TreeState(w)
+        for f in ("token", "parent", "depth", "conf", "value"):
+            setattr(after, f, ex[f].cpu().numpy().copy())
+        after.count = ex["pool_count"].cpu().numpy().copy()
+        after.frontier = ex["frontier"].cpu().numpy().copy()
+        after.frontier_count = ex["frontier_count"].cpu().numpy().copy()
+        after.root = roots.copy()
+        ref = before.copy()
+        oracle.draft_step(w, ref, step, roots, h["draft"][:, step - 1])
+        oracle.draft_step(w, indep, step, roots, h["draft"][:, step - 1])
+        for q in range(w.batch):
+            fg = list(after.frontier[q, :after.frontier_count[q]])
+            fo = list(ref.frontier[q, :ref.frontier_count[q]])
+            if fg == fo:
+                continue
+            vo = ref.value[q]
+            vg = sorted((float(vo[i]) for i in fg), reverse=True)
+            vr = sorted((float(vo[i]) for i in fo), reverse=True)
+            near = len(vg) == len(vr) and all(
+                abs(x - y) <= 1e-5 * max(abs(x), abs(y)) for x, y in zip(vg, vr))
+            events += near
+            mismatches += not near
+        before = after
+    plan.rerank()
+    torch.cuda.synchronize()
+    ind = oracle.rerank(w, indep)
+    same = bool(np.array_equal(plan.tokens.cpu().numpy(), ind["tokens"]) and
+                np.array_equal(plan.parent_slot.cpu().numpy(), ind["parent_slot"]))
+    return {"events": int(events), "mismatches": int(mismatches),
+            "sequence_steps": w.batch * w.depth, "tree_equals_oracle": same}
+
+
+def cpu_baseline(w, host0, seconds, oracle):
+    """The oracle (as is: OpenMP over (sequence, head) in attention only)
+    on this host's cores: single-threaded, then on all its threads, each
+    for up to half the budget (at least one cycle)."""
+    inputs = dict(root_tokens=host0["roots"], draft=host0["draft"],
+                  prefix_len=host0["prefix"], attn=host0["attn"],
+                  target=host0["target"])
+    n_all = oracle.num_threads()
+    res = {}
+    for label, nt in (("single", 1), ("all", n_all)):
+        oracle.set_num_threads(nt)
+        t1 = time.time()
+        n = 0
+        while True:
+            oracle.cycle(w, inputs)
+            n += 1
+            if time.time() - t1 >= seconds / 2 or n >= 50:
+                break
+        res[label] = (n, time.time() - t1, nt)
+    oracle.set_num_threads(n_all)
+    n, el, nt = res["all"]
+    n1, el1, _ = res["single"]
+    return {"value": round(n / el, 4), "unit": "cycles/s", "cores": nt,
+            "kind": "oracle",
+            "sample": f"{n} full oracle cycle(s) of the {w.name} workload "
+                      f"(input set 0) in {el:.1f} s on {nt} threads; "
+                      f"{n1} in {el1:.1f} s on 1 thread",
+            "single_thread": round(n1 / el1, 4), "threads_all": nt,
+            "cpu_model": cpu_model(), "nproc": os.cpu_count()}
+
+
+def extra_workload(name, args, torch, d, gen, WORKLOADS, copy_gbs, spin_per_ms):
+    """cycles/s and rooflines of another workload, measured in the same
+    run: one input set (each is larger than twice the MALL), graph
+    replay, then the per-call pass."""
+    w = WORKLOADS[name]
+    b = Bench(w, 1, torch, d, gen)
+    b.capture()
+    ms = b.timed(min(args.steps, 50), 5)
+    avg_us, per_cycle_us, _ = b.per_call(10, spin_per_ms)
+    alg = b.algorithmic()
+    out = {"cycles_per_s": round(1e3 / ms, 2), "ms_per_cycle": round(ms, 5),
+           "per_call_us": {n: round(v, 3) for n, v in avg_us.items()},
+           "cycle_roofline_frac": round(cycle_roof_us(w, alg) / (ms * 1e3), 4),
+           "calls": call_rooflines(w, alg, avg_us, copy_gbs),
+           "roofline": dominant_roofline(w, alg, avg_us, per_cycle_us),
+           "set_mb": round(b.set_bytes / 1e6, 1)}
+    b.release()
+    del b
+    return out
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -207,88 +572,11 @@ def main():
     w = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
 
-    def dev(a):
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
-
-    # ---- resident input sets ---------------------------------------------
-    t0 = time.time()
-    sets = []
-    set_bytes = 0
-    n_sets = args.sets
-    seed = w.seed
-    while True:
-        s = dict(draft=gen.draft_logits(w, seed), target=gen.target_logits(w, seed),
-                 roots=gen.root_tokens(w, seed), prefix=gen.prefix_lens(w, seed),
-                 attn=gen.attention_inputs(w, seed))
-        ds = dict(draft=dev(s["draft"]), target=dev(s["target"]),
-                  roots=dev(s["roots"]), prefix=dev(s["prefix"]),
-                  attn={k: dev(v) for k, v in s["attn"].items()})
-        if not sets:
-            host0 = s
-            set_bytes = sum(t.numel() * t.element_size() for t in
-                            [ds["draft"], ds["target"], *ds["attn"].values()])
-        sets.append(ds)
-        seed += 1000
-        want = n_sets or max(2, -(-2 * MALL_BYTES // set_bytes))
-        if len(sets) >= min(want, 64):
-            break
-    gen_s = time.time() - t0
-    plan = d.Plan(w)
-    stream = torch.cuda.current_stream()
-
-    def cycle(ds):
-        plan.cycle(ds["roots"], ds["draft"], ds["prefix"], ds["attn"],
-                   ds["target"], stream)
-
-    # ---- graphs: one per input set ---------------------------------------
-    graphs = None
+    b = Bench(w, args.sets, torch, d, gen)
     if not args.no_graph:
-        cycle(sets[0])  # warm the code objects before capture
-        torch.cuda.synchronize()
-        graphs = []
-        for ds in sets:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                plan.cycle(ds["roots"], ds["draft"], ds["prefix"], ds["attn"],
-                           ds["target"], torch.cuda.current_stream())
-            graphs.append(g)
-        torch.cuda.synchronize()
-
-    def run(i):
-        if graphs is not None:
-            graphs[i % len(sets)].replay()
-        else:
-            cycle(sets[i % len(sets)])
-
-    for i in range(args.warmup):
-        run(i)
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(args.steps):
-        run(i)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-
-    # ---- spread: per-cycle time of groups of 10 cycles, after the timed
-    # region (events between whole cycles, all groups enqueued at once) ----
-    n_groups, per_group = 20, 10
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_groups + 1)]
-    evs[0].record()
-    for g_ in range(n_groups):
-        for i in range(per_group):
-            run(g_ * per_group + i)
-        evs[g_ + 1].record()
-    torch.cuda.synchronize()
-    grp = np.array([evs[g_].elapsed_time(evs[g_ + 1]) * 1e3 / per_group
-                    for g_ in range(n_groups)])
-    spread = {"groups": n_groups, "cycles_per_group": per_group,
-              "p10_us": round(float(np.percentile(grp, 10)), 2),
-              "median_us": round(float(np.median(grp)), 2),
-              "p90_us": round(float(np.percentile(grp, 90)), 2)}
+        b.capture()
+    ms = b.timed(args.steps, args.warmup)
+    spread = b.spread()
 
     # ---- streaming-copy bandwidth: the practical HBM ceiling beside the
     # 8 TB/s peak (an elementwise kernel over 512 MiB in, 512 MiB out) ------
@@ -306,79 +594,10 @@ def main():
     copy_gbs = 2 * cn * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del csrc, cdst
 
-    # ---- per-call durations (instrumented pass, eager, same stream) -------
-    # HIP cannot time events recorded inside a graph, so each call is timed
-    # in an eager pass bracketed by events on the launch stream.  A spin
-    # kernel at the head of every batch holds the GPU until the host has
-    # enqueued the whole batch, so the calls run back to back as in the
-    # graph and the events time the GPU work, not the host's launch rate.
-    names = ["draft", "rerank", "mask", "attention", "accept"]
-    acc = {n: 0.0 for n in names}
-    cnt = {n: 0 for n in names}
+    spin_per_ms = spin_rate(torch)
     K = max(10, min(args.steps, 200))
-    per_batch = 10
-
-    def enqueue_cycle(ds, row):
-        # the D draft steps run back to back between one pair of events;
-        # their average carries no per-launch event overhead
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for step in range(1, w.depth + 1):
-            plan.draft_step(step, ds["roots"], ds["draft"][:, step - 1], stream)
-        e1.record(stream)
-        row.append(("draft", e0, e1))
-        for n, fn in (("rerank", lambda: plan.rerank(stream)),
-                      ("mask", lambda: plan.tree_mask(ds["prefix"], stream)),
-                      ("attention", lambda: plan.tree_attention(
-                          ds["attn"]["q"], ds["attn"]["k_cache"],
-                          ds["attn"]["v_cache"], ds["attn"]["k_tree"],
-                          ds["attn"]["v_tree"], ds["prefix"], stream=stream)),
-                      ("accept", lambda: plan.accept(ds["target"], stream))):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            row.append((n, e0, e1))
-
-    # spin-kernel rate (its argument counts GPU clock cycles)
-    torch.cuda.synchronize()
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record(stream)
-    torch.cuda._sleep(1_000_000)
-    s1.record(stream)
-    torch.cuda.synchronize()
-    spin_per_ms = 1_000_000 / max(s0.elapsed_time(s1), 1e-3)
-    hold_ms = 20.0
-    done = 0
-    starved = 0
-    while done < K:
-        nb = min(per_batch, K - done)
-        rows = []
-        torch.cuda._sleep(int(hold_ms * spin_per_ms))
-        gate = torch.cuda.Event()
-        gate.record(stream)
-        t_host = time.time()
-        for i in range(nb):
-            row = []
-            enqueue_cycle(sets[(done + i) % len(sets)], row)
-            rows.append(row)
-        host_ms = (time.time() - t_host) * 1e3
-        if gate.query():  # the GPU caught up with the host: hold longer
-            torch.cuda.synchronize()
-            starved += 1
-            if starved > 4:
-                raise RuntimeError("bench: could not hold the GPU while enqueueing")
-            hold_ms = max(2 * hold_ms, 3 * host_ms)
-            continue
-        torch.cuda.synchronize()
-        for row in rows:
-            for n, e0, e1 in row:
-                acc[n] += e0.elapsed_time(e1) * 1e3  # us
-                cnt[n] += w.depth if n == "draft" else 1
-        done += nb
-    avg_us = {n: acc[n] / cnt[n] for n in names}
+    avg_us, per_cycle_us, hold_ms = b.per_call(K, spin_per_ms)
+    plan, stream, sets = b.plan, b.stream, b.sets
 
     # ---- calls beside the cycle (not part of the metric) ----
     # KV commit: the last cycle's accepted paths are appended to copies of
@@ -404,7 +623,7 @@ def main():
                 e1.record(stream)
                 ev.append((e0, e1))
             torch.cuda.synchronize()
-            return float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+            return float(np.median([a.elapsed_time(b_) * 1e3 for a, b_ in ev]))
 
         ds0 = sets[0]
         kc = ds0["attn"]["k_cache"].clone()
@@ -438,8 +657,6 @@ def main():
             else:
                 splan.rerank(stream)
 
-        readout = {}
-        build_us = {}
         for static in (True, False):
             name = "static" if static else "dynamic"
             build_us[name] = time_next(lambda: build(static))
@@ -451,8 +668,8 @@ def main():
         # et_draft_step; D steps timed as one call, reported per step.
         H = 4096
         lm = gen.lm_head_inputs(w, H)
-        hid = dev(lm["hidden"])
-        wlm = dev(lm["lm_head"])
+        hid = b.dev(lm["hidden"])
+        wlm = b.dev(lm["lm_head"])
         del lm
         lplan = d.Plan(w)
 
@@ -474,62 +691,29 @@ def main():
                    "fused_gbs": round(w_bytes / fused_us / 1e3, 1),
                    "fused_frac_hbm": round(w_bytes / fused_us / 1e3 / HBM_PEAK_GBS, 4)}
         del hid, wlm, lplan
-    per_cycle_us = {n: acc[n] / K for n in names}
 
-    # algorithmic bytes of the last cycle's shapes
-    n_kept = plan.n_kept.cpu().numpy()
-    # frontier rows per step: 1 at step 1; with the threshold off every
-    # later step reads k rows per sequence
-    fr = [w.batch] + [w.batch * w.topk] * (w.depth - 1)
-    alg = algorithmic(w, n_kept, fr, host0["prefix"])
-    # The dominant call (the draft step at the default workload) is the
-    # unit of the roofline: its launches (a vocab scan and a small merge)
-    # run back to back and the events time them together.
-    dominant = max(names, key=lambda n: per_cycle_us[n])
-    call = {"draft": "draft_step", "accept": "accept",
-            "attention": "tree_attention"}.get(dominant)
-    bytes_per_call = {"draft": float(np.mean(alg["draft"])),
-                      "accept": alg["accept"],
-                      "attention": alg["attention"]}.get(dominant, 0.0)
-    achieved = bytes_per_call / (avg_us[dominant] * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(call, w.name) if call else None,
-                "call": call or dominant,
-                "kernels": CALLS[call][0] if call else [],
-                "avg_us": round(avg_us[dominant], 3),
-                "bytes_per_call": bytes_per_call}
-    if dominant == "attention" and w.qkv_dtype == "bf16":
-        # above the ridge (flops per byte > peak flops / peak bytes) the
-        # matrix cores, not HBM, bound the call
-        flops = alg["attention_flops"]
-        if flops / bytes_per_call > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
-            tf = flops / (avg_us[dominant] * 1e-6) / 1e12
-            roofline.update({"bound": "mfma", "achieved": round(tf, 1),
-                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                             "flops_per_call": flops})
+    alg = b.algorithmic()
+    roofline = dominant_roofline(w, alg, avg_us, per_cycle_us)
+    calls = call_rooflines(w, alg, avg_us, copy_gbs)
+    t_roof = cycle_roof_us(w, alg)
 
-    # ---- CPU oracle baseline ---------------------------------------------
-    cpu = None
+    # ---- CPU oracle baseline and near-tie events on input set 0 ----------
+    cpu = ties = None
     if args.cpu_seconds > 0:
         import oracle
-        inputs = dict(root_tokens=host0["roots"], draft=host0["draft"],
-                      prefix_len=host0["prefix"], attn=host0["attn"],
-                      target=host0["target"])
-        t1 = time.time()
-        n = 0
-        while True:
-            oracle.cycle(w, inputs)
-            n += 1
-            if time.time() - t1 >= args.cpu_seconds or n >= 50:
-                break
-        el = time.time() - t1
-        cpu = {"value": round(n / el, 4), "unit": "cycles/s",
-               "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": f"{n} full oracle cycle(s) of the {w.name} workload "
-                         f"(input set 0) in {el:.1f} s"}
+        ties = near_ties(b, oracle)
+        cpu = cpu_baseline(w, b.host0, args.cpu_seconds, oracle)
+    set_mb = round(b.set_bytes / 1e6, 1)
+    n_sets, gen_s, mode = len(sets), b.gen_s, "eager" if b.graphs is None else "hip_graph"
+    b.release()
+    del plan, sets, stream
+
+    # ---- the other large workloads in the same run ------------------------
+    others = {}
+    if not args.no_extras and args.workload == "llama8b":
+        for name in ("llama8b_b64", "llama70b_b8"):
+            others[name] = extra_workload(name, args, torch, d, gen, WORKLOADS,
+                                          copy_gbs, spin_per_ms)
 
     line = {
         "metric": "draft-tree build+verify cycles/sec at Llama-3.1-8B shape, "
@@ -548,14 +732,17 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "vocab": w.vocab,
                    "topk": w.topk, "depth": w.depth, "budget_n": w.budget_n,
                    "heads": f"{w.n_q_heads}/{w.n_kv_heads}x{w.head_dim}",
-                   "prefix": list(w.prefix_range), "input_sets": len(sets),
-                   "set_mb": round(set_bytes / 1e6, 1),
-                   "mode": "eager" if graphs is None else "hip_graph"},
+                   "prefix": list(w.prefix_range), "input_sets": n_sets,
+                   "set_mb": set_mb, "mode": mode},
         "roofline": roofline,
+        "cycle_roofline_frac": round(t_roof / (ms * 1e3), 4),
+        "cycle_roof_us": round(t_roof, 3),
+        "calls": calls,
         "hbm_copy_gbs": round(copy_gbs, 1),
-        "per_call_us": {n: round(avg_us[n], 3) for n in names},
+        "per_call_us": {n: round(avg_us[n], 3) for n in avg_us},
         "cycle_us_spread": spread,
-        "per_cycle_us": {n: round(per_cycle_us[n], 3) for n in names},
+        "per_cycle_us": {n: round(per_cycle_us[n], 3) for n in per_cycle_us},
+        "near_ties": ties,
         "next_calls_us": None if args.no_extras else {
             "kv_commit": round(commit_us, 3),
             "accept_sample": round(sample_us, 3),
@@ -566,6 +753,7 @@ def main():
             "expected_accepted_dynamic": readout["dynamic"],
             "expected_accepted_static": readout["static"],
             "static_nodes": int(len(shape_p) - 1)},
+        "workloads": others or None,
         "cpu_baseline": cpu,
         "gen_seconds": round(gen_s, 1),
     }

@@ -43,6 +43,7 @@ def lib():
         _lib.etref_attention_row.restype = None
         _lib.etref_tree_attention.restype = None
         _lib.etref_kv_commit.restype = None
+        _lib.etref_set_num_threads.restype = None
     return _lib
 
 
@@ -286,6 +287,11 @@ def kv_commit(w, attn, prefix_len, path_slots, accept_len):
 
 def num_threads() -> int:
     return int(lib().etref_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Cap the threads of the attention loop (OpenMP)."""
+    lib().etref_set_num_threads(int(n))
 
 
 def cycle(w, inputs: dict):

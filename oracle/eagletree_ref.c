@@ -715,6 +715,16 @@ int etref_static_tree(int B, int V, int k, int D, int T, int dtype,
   return rc;
 }
 
+/* Cap the threads of the OpenMP loop above (no effect without OpenMP);
+ * the single-threaded baseline of the benchmark uses 1. */
+void etref_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* Threads the OpenMP loop above may use (1 without OpenMP). */
 int etref_num_threads(void) {
 #ifdef _OPENMP
