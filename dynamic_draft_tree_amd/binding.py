@@ -25,7 +25,8 @@ EXPORTS = ("et_plan_create", "et_plan_destroy", "et_workspace_bytes",
            "et_rerank", "et_tree_mask", "et_tree_attention", "et_accept",
            "et_accept_sample", "et_kv_commit", "et_pool_export",
            "et_set_static_shape", "et_draft_step_static", "et_static_tree",
-           "et_draft_step_hidden", "et_accept_noalloc", "et_last_error")
+           "et_draft_step_hidden", "et_accept_noalloc", "et_check_tree",
+           "et_check_prefix", "et_plan_debug", "et_last_error")
 
 
 class et_config(ctypes.Structure):
@@ -82,6 +83,9 @@ def lib():
             "et_draft_step_static": ([vp, vp, i32, vp, vp, i64, i64, vp, vp, vp], ctypes.c_int),
             "et_static_tree": ([vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "et_pool_export": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+            "et_check_tree": ([vp, vp, vp, vp], ctypes.c_int),
+            "et_check_prefix": ([vp, vp], ctypes.c_int),
+            "et_plan_debug": ([vp], ctypes.c_int),
             "et_last_error": ([], ctypes.c_char_p),
         }
         for name, (args, res) in sig.items():
@@ -235,6 +239,31 @@ def et_accept(plan, ws, target_logits, tokens, parent_slot, n_kept,
                            _ptr(tokens), _ptr(parent_slot), _ptr(n_kept),
                            _ptr(accept_len), _ptr(path_slots),
                            _ptr(out_tokens), _stream(stream)))
+
+
+def _host_i32(a):
+    import numpy as np
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, ctypes.c_void_p(a.ctypes.data)
+
+
+def et_check_tree(plan, tokens, parent_slot, n_kept):
+    """Host check of a tree in et_rerank's layout (numpy arrays)."""
+    keep = []
+    ptrs = []
+    for a in (tokens, parent_slot, n_kept):
+        if a is None:
+            ptrs.append(None)
+        else:
+            h, p = _host_i32(a)
+            keep.append(h)
+            ptrs.append(p)
+    _check(lib().et_check_tree(plan, *ptrs))
+
+
+def et_check_prefix(plan, prefix_len):
+    h, p = _host_i32(prefix_len)
+    _check(lib().et_check_prefix(plan, p))
 
 
 def et_accept_noalloc(plan, target_logits, tokens, parent_slot, n_kept,

@@ -4,9 +4,11 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
+#include <vector>
 
 #include "internal.h"
 
@@ -93,6 +95,117 @@ T* at(void* ws, const et::Plan& p, int r) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + p.off[r]);
 }
 
+// ---- checks of documented device preconditions (ET_DEBUG) ---------------
+// The calls document what they expect of device data (n_kept, parent_slot,
+// tokens as et_rerank writes them; prefix lengths within the cache) rather
+// than checking it on every launch.  With ET_DEBUG set when a plan is
+// created, every call of that plan copies those inputs to the host and
+// checks them before launching, synchronises after launching (a kernel
+// fault is reported by the call that caused it) and checks the tree and
+// frontier outputs it wrote.  The same checks are exported for host
+// arrays (et_check_tree, et_check_prefix).
+
+bool env_debug() {
+  const char* e = std::getenv("ET_DEBUG");
+  return e && *e && std::strcmp(e, "0") != 0;
+}
+
+// The tree layout of et_rerank: 0 <= n_kept <= N; slot 0 the root (parent
+// -1, a token); slots 1..n a token in [0, V) and a parent slot in [0, s);
+// pad slots token -1 and parent -1.  tokens may be NULL (not checked).
+int check_tree_host(const et::Plan& p, const char* fn, const int32_t* tokens,
+                    const int32_t* parent, const int32_t* n_kept) {
+  for (int b = 0; b < p.B; ++b) {
+    const int n = n_kept[b];
+    if (n < 0 || n > p.N)
+      return fail(ET_EINVAL, "%s: n_kept[%d] = %d outside 0..%d", fn, b, n, p.N);
+    for (int s = 0; s < p.T; ++s) {
+      const int64_t o = (int64_t)b * p.T + s;
+      const int par = parent[o];
+      const int tok = tokens ? tokens[o] : 0;
+      const bool kept = s <= n;
+      const bool par_ok = s == 0 || !kept ? par == -1 : (par >= 0 && par < s);
+      if (!par_ok)
+        return fail(ET_EINVAL, "%s: parent_slot[%d][%d] = %d (n_kept %d)", fn, b, s, par, n);
+      if (tokens && (kept ? (tok < 0 || tok >= p.V) : tok != -1))
+        return fail(ET_EINVAL, "%s: tokens[%d][%d] = %d (n_kept %d, vocab %d)", fn, b, s,
+                    tok, n, p.V);
+    }
+  }
+  return ET_OK;
+}
+
+int check_prefix_host(const et::Plan& p, const char* fn, const int32_t* prefix_len) {
+  for (int b = 0; b < p.B; ++b)
+    if (prefix_len[b] < 0 || prefix_len[b] > p.Pcap)
+      return fail(ET_EINVAL, "%s: prefix_len[%d] = %d outside 0..%d", fn, b, prefix_len[b],
+                  p.Pcap);
+  return ET_OK;
+}
+
+// Copy n int32 values from the device (stream-ordered) and wait.
+int d2h(const char* fn, std::vector<int32_t>& h, const int32_t* d, size_t n, hipStream_t s) {
+  h.resize(n);
+  hipError_t e = hipMemcpyAsync(h.data(), d, n * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(ET_EHIP, "%s (ET_DEBUG): device read: %s", fn, hipGetErrorString(e));
+  return ET_OK;
+}
+
+// tokens may be NULL; n_kept only (parent == NULL) checks n_kept's range.
+int debug_tree(const et::Plan& p, const char* fn, const int32_t* tokens, const int32_t* parent,
+               const int32_t* n_kept, hipStream_t s) {
+  std::vector<int32_t> tk, ps, nk;
+  int rc = d2h(fn, nk, n_kept, p.B, s);
+  if (rc == ET_OK && tokens) rc = d2h(fn, tk, tokens, (size_t)p.B * p.T, s);
+  if (rc == ET_OK && parent) rc = d2h(fn, ps, parent, (size_t)p.B * p.T, s);
+  if (rc != ET_OK) return rc;
+  if (!parent) {
+    for (int b = 0; b < p.B; ++b)
+      if (nk[b] < 0 || nk[b] > p.N)
+        return fail(ET_EINVAL, "%s: n_kept[%d] = %d outside 0..%d", fn, b, nk[b], p.N);
+    return ET_OK;
+  }
+  return check_tree_host(p, fn, tokens ? tk.data() : nullptr, ps.data(), nk.data());
+}
+
+int debug_prefix(const et::Plan& p, const char* fn, const int32_t* prefix_len, hipStream_t s) {
+  std::vector<int32_t> pl;
+  const int rc = d2h(fn, pl, prefix_len, p.B, s);
+  return rc != ET_OK ? rc : check_prefix_host(p, fn, pl.data());
+}
+
+// After a launch: wait for it and report a failure on the device.
+int debug_sync(const char* fn, hipStream_t s) {
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail(ET_EHIP, "%s (ET_DEBUG): failed on the device: %s", fn,
+                                   hipGetErrorString(e));
+  return ET_OK;
+}
+
+// After a draft step: 0 <= next_count <= k, next_tokens in [0, V) for the
+// first next_count entries and -1 after.
+int debug_frontier(const et::Plan& p, const char* fn, const int32_t* next_tokens,
+                   const int32_t* next_count, hipStream_t s) {
+  std::vector<int32_t> nt, nc;
+  int rc = debug_sync(fn, s);
+  if (rc == ET_OK) rc = d2h(fn, nc, next_count, p.B, s);
+  if (rc == ET_OK) rc = d2h(fn, nt, next_tokens, (size_t)p.B * p.k, s);
+  if (rc != ET_OK) return rc;
+  for (int b = 0; b < p.B; ++b) {
+    if (nc[b] < 0 || nc[b] > p.k)
+      return fail(ET_EINVAL, "%s: next_count[%d] = %d outside 0..%d", fn, b, nc[b], p.k);
+    for (int j = 0; j < p.k; ++j) {
+      const int t = nt[(size_t)b * p.k + j];
+      if (j < nc[b] ? (t < 0 || t >= p.V) : t != -1)
+        return fail(ET_EINVAL, "%s: next_tokens[%d][%d] = %d (next_count %d)", fn, b, j, t,
+                    nc[b]);
+    }
+  }
+  return ET_OK;
+}
+
 }  // namespace
 
 namespace et {
@@ -142,6 +255,24 @@ AttnWs attn_ws(const Plan& p, void* ws) {
 extern "C" {
 
 const char* et_last_error(void) { return g_err; }
+
+int et_check_tree(et_plan_t plan, const int32_t* tokens, const int32_t* parent_slot,
+                  const int32_t* n_kept) {
+  const char* fn = "et_check_tree";
+  CHECK_PTR(plan);
+  CHECK_PTR(parent_slot);
+  CHECK_PTR(n_kept);
+  return check_tree_host(*as_plan(plan), fn, tokens, parent_slot, n_kept);
+}
+
+int et_check_prefix(et_plan_t plan, const int32_t* prefix_len) {
+  const char* fn = "et_check_prefix";
+  CHECK_PTR(plan);
+  CHECK_PTR(prefix_len);
+  return check_prefix_host(*as_plan(plan), fn, prefix_len);
+}
+
+int et_plan_debug(et_plan_t plan) { return plan && as_plan(plan)->debug ? 1 : 0; }
 
 int et_plan_create(const et_config* cfg, et_plan_t* out) {
   const char* fn = "et_plan_create";
@@ -233,6 +364,7 @@ int et_plan_create(const et_config* cfg, et_plan_t* out) {
   p->attn_splits = p->qdt == ET_F32 ? 1 : (int)splits;
   p->last_ws = nullptr;
   p->last_step = 0;
+  p->debug = env_debug();
   layout(*p);
   *out = reinterpret_cast<et_plan_t>(p);
   g_err[0] = 0;
@@ -305,6 +437,8 @@ int draft_step(const char* fn, et_plan_t plan, void* ws, int32_t step,
                             batch_stride, row_stride, vec, fixed ? &ff : nullptr,
                             next_tokens, next_count, (hipStream_t)stream),
       fn);
+  if (rc == ET_OK && p.debug)
+    rc = debug_frontier(p, fn, next_tokens, next_count, (hipStream_t)stream);
   if (rc == ET_OK) {
     p.last_ws = ws;
     p.last_step = step;
@@ -373,6 +507,8 @@ int et_draft_step_hidden(et_plan_t plan, void* ws, int32_t step,
                                    lm_head, hidden_dim, next_tokens, next_count,
                                    (hipStream_t)stream),
       fn);
+  if (rc == ET_OK && p.debug)
+    rc = debug_frontier(p, fn, next_tokens, next_count, (hipStream_t)stream);
   if (rc == ET_OK) {
     p.last_ws = ws;
     p.last_step = step;
@@ -457,10 +593,14 @@ int et_static_tree(et_plan_t plan, void* ws, int32_t* tokens,
   et::FixedSlots fs;
   fs.m = p.static_m;
   for (int s = 0; s <= et::kMaxBudget; ++s) fs.slot[s] = s <= p.static_m ? p.static_slot[s] : 0;
-  return hip_status(et::launch_static_tree(p, et::draft_ws(p, ws), fs, tokens,
-                                           parent_slot, conf, value, n_kept,
-                                           (hipStream_t)stream),
-                    fn);
+  int rc = hip_status(et::launch_static_tree(p, et::draft_ws(p, ws), fs, tokens,
+                                             parent_slot, conf, value, n_kept,
+                                             (hipStream_t)stream),
+                      fn);
+  if (rc == ET_OK && p.debug) rc = debug_sync(fn, (hipStream_t)stream);
+  if (rc == ET_OK && p.debug)
+    rc = debug_tree(p, fn, tokens, parent_slot, n_kept, (hipStream_t)stream);
+  return rc;
 }
 
 int et_rerank(et_plan_t plan, void* ws, int32_t* tokens, int32_t* parent_slot,
@@ -478,10 +618,14 @@ int et_rerank(et_plan_t plan, void* ws, int32_t* tokens, int32_t* parent_slot,
   if (p.last_ws != ws || p.last_step != p.D)
     return fail(ET_ESTATE, "%s: the tree is not complete (last step %d of "
                 "%d on this workspace)", fn, p.last_step, p.D);
-  return hip_status(et::launch_rerank(p, et::draft_ws(p, ws), tokens,
-                                      parent_slot, conf, value, n_kept,
-                                      (hipStream_t)stream),
-                    fn);
+  int rc = hip_status(et::launch_rerank(p, et::draft_ws(p, ws), tokens,
+                                        parent_slot, conf, value, n_kept,
+                                        (hipStream_t)stream),
+                      fn);
+  if (rc == ET_OK && p.debug) rc = debug_sync(fn, (hipStream_t)stream);
+  if (rc == ET_OK && p.debug)
+    rc = debug_tree(p, fn, tokens, parent_slot, n_kept, (hipStream_t)stream);
+  return rc;
 }
 
 int et_tree_mask(et_plan_t plan, const int32_t* parent_slot,
@@ -497,10 +641,17 @@ int et_tree_mask(et_plan_t plan, const int32_t* parent_slot,
   CHECK_PTR(depth);
   CHECK_PTR(pos_ids);
   et::Plan& p = *as_plan(plan);
-  return hip_status(et::launch_tree_mask(p, parent_slot, n_kept, prefix_len,
-                                         mask, depth, pos_ids,
-                                         (hipStream_t)stream),
-                    fn);
+  const hipStream_t st = (hipStream_t)stream;
+  if (p.debug) {
+    int rc = debug_tree(p, fn, nullptr, parent_slot, n_kept, st);
+    if (rc == ET_OK) rc = debug_prefix(p, fn, prefix_len, st);
+    if (rc != ET_OK) return rc;
+  }
+  int rc = hip_status(et::launch_tree_mask(p, parent_slot, n_kept, prefix_len,
+                                           mask, depth, pos_ids, st),
+                      fn);
+  if (rc == ET_OK && p.debug) rc = debug_sync(fn, st);
+  return rc;
 }
 
 int et_tree_attention(et_plan_t plan, void* ws, const void* q,
@@ -530,11 +681,18 @@ int et_tree_attention(et_plan_t plan, void* ws, const void* q,
       !(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) &&
         aligned16(k_tree) && aligned16(v_tree) && aligned16(out)))
     return fail(ET_EINVAL, "%s: bf16 q/k/v/out must be 16-byte aligned", fn);
-  return hip_status(et::launch_tree_attention(
-                        p, et::attn_ws(p, ws), q, k_cache, v_cache, k_tree,
-                        v_tree, prefix_len, mask, n_kept, scale, out,
-                        (hipStream_t)stream),
-                    fn);
+  const hipStream_t st = (hipStream_t)stream;
+  if (p.debug) {
+    int rc = debug_tree(p, fn, nullptr, nullptr, n_kept, st);
+    if (rc == ET_OK) rc = debug_prefix(p, fn, prefix_len, st);
+    if (rc != ET_OK) return rc;
+  }
+  int rc = hip_status(et::launch_tree_attention(
+                          p, et::attn_ws(p, ws), q, k_cache, v_cache, k_tree,
+                          v_tree, prefix_len, mask, n_kept, scale, out, st),
+                      fn);
+  if (rc == ET_OK && p.debug) rc = debug_sync(fn, st);
+  return rc;
 }
 
 int et_accept(et_plan_t plan, void* ws, const void* target_logits,
@@ -563,12 +721,18 @@ int et_accept(et_plan_t plan, void* ws, const void* target_logits,
   const int per = p.ldt == ET_BF16 ? 8 : 4;
   const bool vec = aligned16(target_logits) && batch_stride % per == 0 &&
                    row_stride % per == 0 && p.V >= per;
-  return hip_status(
+  const hipStream_t st = (hipStream_t)stream;
+  if (p.debug) {
+    const int rc = debug_tree(p, fn, tokens, parent_slot, n_kept, st);
+    if (rc != ET_OK) return rc;
+  }
+  int rc = hip_status(
       et::launch_accept(p, et::accept_ws(p, ws), target_logits, batch_stride,
                         row_stride, vec, tokens, parent_slot, n_kept,
-                        accept_len, path_slots, out_tokens,
-                        (hipStream_t)stream),
+                        accept_len, path_slots, out_tokens, st),
       fn);
+  if (rc == ET_OK && p.debug) rc = debug_sync(fn, st);
+  return rc;
 }
 
 }  // extern "C"
@@ -638,16 +802,22 @@ int et_accept_noalloc(et_plan_t plan, const void* target_logits,
   void* sp = nullptr;
   int rc = scratch_on_device(fn, &sp);
   if (rc != ET_OK) return rc;
+  const hipStream_t st = (hipStream_t)stream;
+  if (p.debug) {
+    rc = debug_tree(p, fn, tokens, parent_slot, n_kept, st);
+    if (rc != ET_OK) return rc;
+  }
   et::AcceptWs w;
   w.part = static_cast<uint64_t*>(sp);
   const int per = p.ldt == ET_BF16 ? 8 : 4;
   const bool vec = aligned16(target_logits) && batch_stride % per == 0 &&
                    row_stride % per == 0 && p.V >= per;
-  return hip_status(
+  rc = hip_status(
       et::launch_accept(p, w, target_logits, batch_stride, row_stride, vec, tokens,
-                        parent_slot, n_kept, accept_len, path_slots, out_tokens,
-                        (hipStream_t)stream),
+                        parent_slot, n_kept, accept_len, path_slots, out_tokens, st),
       fn);
+  if (rc == ET_OK && p.debug) rc = debug_sync(fn, st);
+  return rc;
 }
 
 int et_accept_sample(et_plan_t plan, void* ws, const void* target_logits,
@@ -683,12 +853,19 @@ int et_accept_sample(et_plan_t plan, void* ws, const void* target_logits,
   const int per = p.ldt == ET_BF16 ? 8 : 4;
   const bool vec = aligned16(target_logits) && batch_stride % per == 0 &&
                    row_stride % per == 0 && p.V >= per;
-  return hip_status(
+  const hipStream_t st = (hipStream_t)stream;
+  if (p.debug) {
+    const int rc = debug_tree(p, fn, tokens, parent_slot, n_kept, st);
+    if (rc != ET_OK) return rc;
+  }
+  int rc = hip_status(
       et::launch_accept_sample(p, et::accept_ws(p, ws), target_logits,
                                batch_stride, row_stride, vec, tokens,
                                parent_slot, n_kept, c, uniforms, accept_len,
-                               path_slots, out_tokens, (hipStream_t)stream),
+                               path_slots, out_tokens, st),
       fn);
+  if (rc == ET_OK && p.debug) rc = debug_sync(fn, st);
+  return rc;
 }
 
 int et_kv_commit(et_plan_t plan, void* k_cache, void* v_cache,
@@ -708,10 +885,22 @@ int et_kv_commit(et_plan_t plan, void* k_cache, void* v_cache,
       !aligned16(v_tree))
     return fail(ET_EINVAL, "%s: K/V buffers must be 16-byte aligned", fn);
   et::Plan& p = *as_plan(plan);
-  return hip_status(
+  const hipStream_t st = (hipStream_t)stream;
+  if (p.debug) {
+    std::vector<int32_t> al;
+    int rc = debug_prefix(p, fn, prefix_len, st);
+    if (rc == ET_OK) rc = d2h(fn, al, accept_len, p.B, st);
+    if (rc != ET_OK) return rc;
+    for (int b = 0; b < p.B; ++b)
+      if (al[b] < 0 || al[b] > p.D)
+        return fail(ET_EINVAL, "%s: accept_len[%d] = %d outside 0..%d", fn, b, al[b], p.D);
+  }
+  int rc = hip_status(
       et::launch_kv_commit(p, k_cache, v_cache, k_tree, v_tree, prefix_len,
-                           path_slots, accept_len, (hipStream_t)stream),
+                           path_slots, accept_len, st),
       fn);
+  if (rc == ET_OK && p.debug) rc = debug_sync(fn, st);
+  return rc;
 }
 
 int et_pool_export(et_plan_t plan, const void* ws, int32_t* token,

@@ -112,6 +112,7 @@ struct Plan {
   // workspace layout
   size_t off[32];
   size_t ws_bytes;
+  bool debug;             // ET_DEBUG set at plan creation: sync and check
   // call-order check
   const void* last_ws;
   int last_step;

@@ -43,6 +43,14 @@
  *   - Device-side preconditions (not checked, documented instead): logits
  *     are finite or -inf with at least one finite entry per row; no NaN;
  *     n_kept / parent_slot / tokens are the values written by et_rerank.
+ *   - Debug mode: with the environment variable ET_DEBUG set (not "0")
+ *     when a plan is created, every call of that plan copies the tree and
+ *     prefix-length inputs it reads to the host and checks them (as
+ *     et_check_tree / et_check_prefix) before launching, returning
+ *     ET_EINVAL with a message and launching nothing on a violation; then
+ *     it synchronises the stream, so a failure on the device is reported
+ *     (ET_EHIP) by the call that caused it, and checks the tree or
+ *     frontier it wrote.  Slow: for debugging only.
  *   - T = N + 1 tree slots per sequence: slot 0 is the root (the last
  *     committed token), slots 1..n hold the kept draft tokens, slots
  *     n+1..N are padding.  W = ceil(T / 64) mask words per slot.
@@ -74,7 +82,7 @@ typedef void* et_stream_t;              /* a hipStream_t                    */
 typedef struct et_plan_s* et_plan_t;    /* opaque, host-side metadata only  */
 
 /* Shapes of one cycle.  Limits (ET_EUNSUPPORTED / ET_EINVAL otherwise):
- *   1 <= batch <= 65535; 2 <= vocab <= 2^24; 1 <= topk <= 16;
+ *   1 <= batch <= 65535; 2 <= vocab <= 2^18; 1 <= topk <= 16;
  *   1 <= depth <= 15; 1 <= budget_n <= 255 (so T <= 256, W <= 4);
  *   expand_threshold >= 0 (0 disables the stop rule);
  *   head_dim in {64, 128}; n_q_heads % n_kv_heads == 0;
@@ -366,6 +374,22 @@ int et_pool_export(et_plan_t plan, const void* ws, int32_t* token,
                    int32_t* parent, int32_t* depth, float* conf, float* value,
                    int32_t* pool_count, int32_t* frontier,
                    int32_t* frontier_count, et_stream_t stream);
+
+/* Host-side checks of the device data the calls expect (what ET_DEBUG
+ * runs on copies of device buffers), on HOST arrays:
+ *   et_check_tree    tokens (may be NULL: not checked), parent_slot
+ *                    [B][T] and n_kept [B] in the layout of et_rerank:
+ *                    0 <= n_kept[b] <= N; slot 0 has parent -1; a kept slot
+ *                    s <= n_kept[b] has a token in [0, vocab) and a parent
+ *                    slot in [0, s) (the flattened order is topological);
+ *                    pad slots have token -1 and parent -1
+ *   et_check_prefix  0 <= prefix_len[b] <= prefix_cap
+ * ET_OK, or ET_EINVAL with the first violation in et_last_error().
+ * et_plan_debug returns 1 if the plan was created in debug mode. */
+int et_check_tree(et_plan_t plan, const int32_t* tokens,
+                  const int32_t* parent_slot, const int32_t* n_kept);
+int et_check_prefix(et_plan_t plan, const int32_t* prefix_len);
+int et_plan_debug(et_plan_t plan);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* et_last_error(void);

@@ -159,3 +159,28 @@ def test_accept_noalloc_rejects_plans_beyond_its_scratch():
     assert rc == binding.ET_EINVAL
     assert "scratch" in binding.lib().et_last_error().decode()
     d.et_plan_destroy(h)
+
+
+def test_static_shape_validation_on_the_host():
+    """et_set_static_shape (host only): the generated shape of every
+    workload is accepted; shapes breaking a rule are rejected."""
+    from synth import gen
+    for name, w in WORKLOADS.items():
+        h = d.et_plan_create(d.make_config(w))
+        p, r = gen.static_shape(w)
+        binding.et_set_static_shape(h, p[1:], r[1:])
+        d.et_plan_destroy(h)
+    w = WORKLOADS["tiny"]  # k = 2, D = 3, N = 8
+    h = d.et_plan_create(d.make_config(w))
+    bad = [([0], [2]),                 # rank >= k
+           ([1], [0]),                 # parent not an earlier slot
+           ([0, 0], [1, 1]),           # repeated sibling rank
+           ([0, 1, 2, 3], [0] * 4),    # depth 4 > D
+           # three depth-2 slots with children, more than k
+           ([0, 0, 1, 1, 2, 3, 4, 5], [0, 1, 0, 1, 0, 0, 0, 0]),
+           ([0] * 9, list(range(9)))]  # more nodes than N (and ranks >= k)
+    for parent, rank in bad:
+        with pytest.raises(binding.EtError) as e:
+            binding.et_set_static_shape(h, parent, rank)
+        assert e.value.code == binding.ET_EINVAL
+    d.et_plan_destroy(h)
