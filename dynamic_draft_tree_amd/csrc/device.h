@@ -148,12 +148,15 @@ __device__ __forceinline__ int ballot_rank(bool pred, int* count) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Exclusive prefix sum over the wave of small non-negative values (< 128),
-// from one ballot per bit plane; *total receives the wave sum.
+// Exclusive prefix sum over the wave of small non-negative values (below
+// 2^BITS), from one ballot per bit plane (each a round trip through the
+// scalar unit, so BITS is kept to what the values need); *total receives
+// the wave sum.
+template <int BITS>
 __device__ __forceinline__ int wave_excl_prefix_small(int v, int* total) {
   int pre = 0, tot = 0;
 #pragma unroll
-  for (int bit = 0; bit < 7; ++bit) {
+  for (int bit = 0; bit < BITS; ++bit) {
     int cnt;
     const int r = ballot_rank((v >> bit) & 1, &cnt);
     pre += r << bit;
@@ -161,6 +164,16 @@ __device__ __forceinline__ int wave_excl_prefix_small(int v, int* total) {
   }
   *total = tot;
   return pre;
+}
+
+// Block barrier for LDS data only: each wave waits for its own LDS
+// operations, then all waves meet.  Unlike __syncthreads it does not wait
+// for outstanding global memory operations (__syncthreads waits for every
+// global store of the block to be acknowledged, about a microsecond).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // LDS writes of this wave visible to its later LDS reads, without waiting

@@ -70,6 +70,26 @@ __device__ __forceinline__ uint64_t key_floor(float x) {
   return (uint64_t)ordered_f32(x) << 32;
 }
 
+typedef uint64_t u64x2_t __attribute__((ext_vector_type(2)));
+// Number of keys in base[lo, hi) (LDS) greater than me, read 16 keys at a
+// time with 16-byte loads issued together (one wait per 16 keys, not one
+// per key).  base must be 16-byte aligned and lo even; reads reach below
+// lo + 16 * ceil((hi - lo) / 16), which the caller's array must hold.
+__device__ __forceinline__ int count_greater(const uint64_t* base, int lo, int hi, uint64_t me) {
+  int cnt = 0;
+  for (int j0 = lo; j0 < hi; j0 += 16) {
+    u64x2_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *(const u64x2_t*)&base[j0 + 2 * u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      cnt += (j0 + 2 * u < hi && v[u].x > me) ? 1 : 0;
+      cnt += (j0 + 2 * u + 1 < hi && v[u].y > me) ? 1 : 0;
+    }
+  }
+  return cnt;
+}
+
 // Chunks [c0, c0 + nch) of row j of sequence b: per chunk, the block's
 // (max, sum of exp) and its top-k logit keys, stored for the merge launch;
 // with WAVE, each wave publishes its own 1/4 of the chunk instead
@@ -88,9 +108,10 @@ __device__ __forceinline__ void scan_chunks(const DraftArgs& a, const char* row,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k = a.k, S = a.S;
   constexpr int NV = chunk_vectors<BF16, E>();
+  constexpr int kE2Bits = E < 32 ? 5 : E < 64 ? 6 : 7;  // bit planes of a count <= E
   // lane values as loaded (vector path) or as fp32 (element-wise path)
   __shared__ u32x4_t s_x[kScanThreads * (VEC ? NV : E / 4)];
-  __shared__ uint64_t s_wl[kWaves * kWaveCap];  // wave candidate lists
+  __shared__ __attribute__((aligned(16))) uint64_t s_wl[kWaves * kWaveCap];  // wave candidate lists
   __shared__ uint64_t s_bc[kWaves * kWaveCap];  // block candidates
   __shared__ float s_wf[3][kWaves];             // wave bound, max, sum
   __shared__ int s_wcnt[kWaves];
@@ -193,7 +214,7 @@ __device__ __forceinline__ void scan_chunks(const DraftArgs& a, const char* row,
   if constexpr (VEC)
     if (ci + 1 < nch) issue_chunk<BF16, E>(row, base + kChunkE, a.V, tid, raw);
   int wtot;
-  int o = wave_excl_prefix_small(__popc(bits), &wtot);
+  int o = wave_excl_prefix_small<kE2Bits>(__popc(bits), &wtot);  // popc(bits) <= E
   uint64_t* wl = &s_wl[wave * kWaveCap];
   if (wtot <= kWaveCap) {
     while (bits) {
@@ -231,9 +252,7 @@ __device__ __forceinline__ void scan_chunks(const DraftArgs& a, const char* row,
     uint64_t* dst = &a.ws.part_keys[rowid * kMaxTopk * a.parts + li];  // rank r at r * parts
     if (lane < wtot) {
       const uint64_t me = wl[lane];
-      int rank = 0;
-#pragma unroll 8
-      for (int q = 0; q < wtot; ++q) rank += wl[q] > me;
+      const int rank = count_greater(wl, 0, wtot, me);  // wtot <= 64: reads within the list
       if (rank < k) dst[(int64_t)rank * a.parts] = me;
     }
     if (lane >= wtot && lane < k) dst[(int64_t)lane * a.parts] = 0;
@@ -326,9 +345,10 @@ __device__ __forceinline__ void merge_rows(const DraftArgs& a, const FixedFronti
   const int tid = threadIdx.x, lane = tid & 63, jr = tid >> 6;  // jr: this wave's row
   const int k = a.k, S = a.parts;  // partial lists per row (<= 64)
   const int prev = (a.step - 1) & 1, cur = a.step & 1;
-  __shared__ uint64_t s_rc[kMaxTopk * 64];        // row candidates
+  __shared__ __attribute__((aligned(16))) uint64_t s_rc[kMaxTopk * 64];  // row candidates
   __shared__ uint64_t s_rk[kMaxTopk * kMaxTopk];  // row top-k keys
-  __shared__ uint64_t s_aux[kMaxTopk * kMaxTopk]; // children's pool keys
+  // children's pool keys; the padding covers count_greater's last reads
+  __shared__ __attribute__((aligned(16))) uint64_t s_aux[kMaxTopk * kMaxTopk + 32];
   __shared__ int s_nf;
   // Every load is issued before the frontier count F arrives: rows j < k
   // of the workspace are always readable, rows j >= F are dropped.
@@ -385,7 +405,7 @@ __device__ __forceinline__ void merge_rows(const DraftArgs& a, const FixedFronti
   for (int r = 0; r < KST; ++r) cl += (pk[r] != 0 && pk[r] >= Lk) ? 1 : 0;
   const bool more = cl == KST && k > KST;
   int n;
-  const int off = wave_excl_prefix_small(cl, &n);
+  const int off = wave_excl_prefix_small<KST == 4 ? 3 : 4>(cl, &n);  // cl <= KST
   const bool fits = n <= 64 && __ballot(more) == 0ull;
   uint64_t* lst = &s_rc[jr * 64];
   if (on_row && fits) {
@@ -395,13 +415,16 @@ __device__ __forceinline__ void merge_rows(const DraftArgs& a, const FixedFronti
   }
   wave_lds_fence();
   // phase: row list written
+  // The row's top-k keys: the candidate of rank r (r < k) becomes child r,
+  // formed by the lane that ranked it (fast path), or by lane r from the
+  // exact path's list.
+  uint64_t ckey = 0;
+  int crank = -1;
   if (on_row && fits) {
-    for (int i = lane; i < n; i += 64) {
-      const uint64_t me = lst[i];
-      int rank = 0;
-#pragma unroll 8
-      for (int t = 0; t < n; ++t) rank += lst[t] > me;
-      if (rank < k) s_rk[jr * kMaxTopk + rank] = me;
+    if (lane < n) {  // n <= 64: reads stay within the row's 64 entries
+      ckey = lst[lane];
+      crank = count_greater(lst, 0, n, ckey);
+      if (crank >= k) crank = -1;
     }
   } else if (on_row) {
     // every key of the row, at most 64 lists x 16 ranks (16 per lane)
@@ -422,29 +445,38 @@ __device__ __forceinline__ void merge_rows(const DraftArgs& a, const FixedFronti
       if (lane == 0) s_rk[jr * kMaxTopk + r] = w;
       prevk = w;
     }
+    wave_lds_fence();
+    if (lane < k) {
+      ckey = s_rk[jr * kMaxTopk + lane];
+      crank = lane;
+    }
   }
-  wave_lds_fence();
   // phase: row ranked
   // Children of the row, in rank order (conf decreasing): child r of row
   // jr is pool node P0 + jr * k + r.
+  // The child's pool fields stay in registers: every global store of the
+  // merge is issued at its end, so no later step waits for a store to land
+  // (the compiler waits for pending stores before reusing their registers).
   const int64_t pb = (int64_t)b * a.cap;
-  if (on_row && lane < k) {
-    const uint64_t key = s_rk[jr * kMaxTopk + lane];
-    const int tok = (int)id_of(key);
-    const float conf = __builtin_amdgcn_exp2f((logit_of(key) - m) * kLog2e) / sum;
-    const float val = __fmul_rn(vpar, conf);
-    const int ci = jr * k + lane, pi = P0 + ci;
-    a.ws.pool_token[pb + pi] = tok;
-    a.ws.pool_parent[pb + pi] = par;
-    a.ws.pool_depth[pb + pi] = a.step;
-    a.ws.pool_conf[pb + pi] = conf;
-    a.ws.pool_value[pb + pi] = val;
-    s_aux[ci] = pool_key(val, a.step, tok, pi);
+  const bool mine = crank >= 0;  // on_row is implied
+  const float rsum = __builtin_amdgcn_rcpf(sum);
+  int c_tok = 0, c_pi = 0;
+  float c_conf = 0.f, c_val = 0.f;
+  if (mine) {
+    c_tok = (int)id_of(ckey);
+    c_conf = __builtin_amdgcn_exp2f((logit_of(ckey) - m) * kLog2e) * rsum;
+    c_val = __fmul_rn(vpar, c_conf);
+    const int ci = jr * k + crank;
+    c_pi = P0 + ci;
+    s_aux[ci] = pool_key(c_val, a.step, c_tok, c_pi);
   }
   const int n_new = F * k;  // <= k * k: four threads per child fit the k waves
-  __syncthreads();
+  lds_barrier();
   // phase: children appended
   const int fb = (cur * a.B + b) * k;
+  // the frontier entry this thread writes at the end (slot f_at, or none)
+  int f_at = -1, f_idx = -1, f_tok = -1;
+  float f_val = 0.f;
   if constexpr (FIXED) {
     // Fixed shape: next-frontier node i is child fx->ci[i] of this step.
     if (tid < k) {
@@ -454,43 +486,65 @@ __device__ __forceinline__ void merge_rows(const DraftArgs& a, const FixedFronti
         if (tid == i && i < fx->n) ci = fx->ci[i];
       const bool kept = ci >= 0 && ci < n_new;
       const uint64_t key = kept ? s_aux[ci] : 0;
-      a.ws.frontier[fb + tid] = kept ? pool_index_of(key) : -1;
-      a.ws.frontier_val[fb + tid] = kept ? pool_value_of(key) : 0.0f;
-      a.next_tokens[(int64_t)b * k + tid] = kept ? pool_token_of(key) : -1;
+      f_at = tid;
+      f_idx = kept ? pool_index_of(key) : -1;
+      f_val = kept ? pool_value_of(key) : 0.0f;
+      f_tok = kept ? pool_token_of(key) : -1;
       if (kept) atomicAdd(&s_nf, 1);
     }
   } else if (a.step < a.D) {
     // The k largest children keys: child c's rank is the number of larger
-    // keys, counted by its four threads over every fourth child.  Keys are
-    // distinct (the pool index field), so the ranks are too.  Those below
-    // the expansion threshold (a suffix: value leads the key) stay
+    // keys, counted by its four threads over a quarter of the children each
+    // (q of them, q even so every quarter starts 16-byte aligned).  Keys
+    // are distinct (the pool index field), so the ranks are too.  Those
+    // below the expansion threshold (a suffix: value leads the key) stay
     // unexpanded.
     const int c = tid >> 2, part = tid & 3;
     const uint64_t me = c < n_new ? s_aux[c] : ~0ull;
-    int cnt = 0;
-#pragma unroll 4
-    for (int j = part; j < n_new; j += 4) cnt += s_aux[j] > me ? 1 : 0;
+    const int q = ((n_new + 3) / 4 + 1) & ~1;
+    int cnt = count_greater(s_aux, part * q, min(n_new, part * q + q), me);
     cnt += xor_lane<1>(cnt);
     cnt += xor_lane<2>(cnt);
     if (part == 0 && c < n_new && cnt < k) {
       const bool kept = !(pool_value_of(me) < a.thr);
-      a.ws.frontier[fb + cnt] = kept ? pool_index_of(me) : -1;
-      a.ws.frontier_val[fb + cnt] = pool_value_of(me);
-      a.next_tokens[(int64_t)b * k + cnt] = kept ? pool_token_of(me) : -1;
-      if (kept) atomicAdd(&s_nf, 1);
+      f_at = cnt;
+      f_idx = kept ? pool_index_of(me) : -1;
+      f_val = pool_value_of(me);
+      f_tok = kept ? pool_token_of(me) : -1;
+      if (kept && a.thr > 0.f) atomicAdd(&s_nf, 1);
     }
   } else if (tid < k) {
-    a.ws.frontier[fb + tid] = -1;
-    a.next_tokens[(int64_t)b * k + tid] = -1;
+    f_at = tid;  // the last step: no frontier
   }
-  __syncthreads();
+  // With the stop rule off every one of the k (<= n_new) frontier nodes is
+  // kept: the count is known without a reduction.
+  int nf = 0;
+  if (FIXED || a.step >= a.D || a.thr > 0.f) {
+    lds_barrier();  // s_nf complete
+    nf = s_nf;
+  } else {
+    nf = k;
+  }
+  // phase: frontier written
+  // every global store of the merge
+  if (mine) {
+    a.ws.pool_token[pb + c_pi] = c_tok;
+    a.ws.pool_parent[pb + c_pi] = par;
+    a.ws.pool_depth[pb + c_pi] = a.step;
+    a.ws.pool_conf[pb + c_pi] = c_conf;
+    a.ws.pool_value[pb + c_pi] = c_val;
+  }
+  if (f_at >= 0) {
+    a.ws.frontier[fb + f_at] = f_idx;
+    if (FIXED || a.step < a.D) a.ws.frontier_val[fb + f_at] = f_val;
+    a.next_tokens[(int64_t)b * k + f_at] = f_tok;
+  }
   if (tid == 0) {
     a.ws.pool_count[b] = P0 + n_new;
     if (a.step == 1) a.ws.root_token[b] = a.root_tokens[b];
-    a.ws.frontier_count[cur * a.B + b] = s_nf;
-    a.next_count[b] = s_nf;
+    a.ws.frontier_count[cur * a.B + b] = nf;
+    a.next_count[b] = nf;
   }
-  // phase: frontier written
 }
 
 // Scan launch: block (x, j, b) streams chunks [x * cpb, x * cpb + cpb) of
