@@ -156,18 +156,20 @@ __device__ __forceinline__ void scan_chunks(const DraftArgs& a, const char* row,
       mx[i] = m;
     }
   const float lmax = mx[0];
-  const float mw = wave_max_f32(lmax);
-  float sl = 0.f;
-  if (mw > -INFINITY) {
-    // exp(x - m) = 2^(x log2 e - m log2 e): one FMA and v_exp_f32; four
-    // accumulators keep the add chain short.
-    const float off = mw * kLog2e;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  // exp(x - m) = 2^(x log2 e - m log2 e): one FMA and v_exp_f32; four
+  // accumulators keep the add chain short.  The lane sums against its own
+  // maximum (offset a), so the exps need not wait for the wave's maximum
+  // (offset b): the lane's share of the wave sum is that sum times
+  // 2^(a - b), and with x log2 e - a exact inside the FMA the product
+  // differs from the direct 2^(x log2 e - b) by the rounding of a - b.
+  const float offa = lmax > -INFINITY ? lmax * kLog2e : 0.f;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      acc[e & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(xv(e), kLog2e, -off));
-    sl = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  }
+  for (int e = 0; e < E; ++e)
+    acc[e & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(xv(e), kLog2e, -offa));
+  const float ls = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  const float mw = wave_max_f32(lmax);
+  const float sl = lmax > -INFINITY ? ls * __builtin_amdgcn_exp2f(offa - mw * kLog2e) : 0.f;
   const float sw = wave_sum_f32(sl);
   // phase: max and sum of exp
   // The wave's k-th largest lane maximum Lw bounds its k-th largest
@@ -182,16 +184,28 @@ __device__ __forceinline__ void scan_chunks(const DraftArgs& a, const char* row,
   constexpr int per = BF16 ? 8 : 4;
   const int lid = base + tid * per;
   const int lim = a.V - lid;
-  // (one is opaque to the compiler: written as cond ? 1 << e : 0 the 32
-  // masks would be hoisted out of the chunk loop into registers)
   // Ids past V read -inf, so with a finite Lw no bound check is needed;
   // Lw = -inf (fewer than k lanes of the wave inside the row) takes it.
-  uint32_t one = 1u, bits = 0u;
-  asm volatile("" : "+v"(one));
+  static_assert(E <= 32, "one mask bit per element");
+  uint32_t bits = 0u;
   if (Lw > -INFINITY) {
+    // x >= Lw exactly when x - Lw has a clear sign bit: x - Lw is +0 for
+    // x == Lw and -inf for x = -inf (inputs hold no NaN or +inf), and a
+    // zero bound is taken as -0 so that an element -0, equal to it, gives
+    // +0.  Each sign bit is shifted into a register with one alignbit
+    // ((neg << 1) | (d >> 31)), element e ending at bit E - 1 - e; one bit
+    // reversal then puts element e at bit e.
+    const float Lz = Lw == 0.f ? -0.f : Lw;
+    uint32_t neg = 0u;
 #pragma unroll
-    for (int e = 0; e < E; ++e) bits |= (xv(e) >= Lw ? one : 0u) << e;
+    for (int e = 0; e < E; ++e)
+      neg = __builtin_amdgcn_alignbit(neg, __float_as_uint(xv(e) - Lz), 31);
+    bits = __brev(~neg) >> (32 - E);
   } else {
+    // (one is opaque to the compiler: written as cond ? 1 << e : 0 the
+    // masks would be hoisted out of the chunk loop into registers)
+    uint32_t one = 1u;
+    asm volatile("" : "+v"(one));
 #pragma unroll
     for (int e = 0; e < E; ++e)
       bits |= (elem_off<BF16>(e, 0) < lim && xv(e) >= Lw ? one : 0u) << e;
