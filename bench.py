@@ -1,7 +1,8 @@
 """Throughput of one EAGLE-2 draft-tree build + verify cycle on one MI355X.
 
-A step is one whole cycle over one batch: D x et_draft_step, et_rerank,
-et_tree_mask, et_tree_attention (one attention layer) and et_accept, on
+A step is one whole cycle over one batch: D x et_draft_step, et_rerank_mask
+(rerank and tree mask in one launch), et_tree_attention (one attention
+layer) and et_accept, on
 synthetic inputs already resident in HBM.  The default workload is the
 Llama-3.1-8B shape at batch 1 (vocab 128256, top-k 10, depth 8, N 60,
 GQA 32/8 x 128, prefix 4096, bf16).  Input sets rotate so the working set
@@ -190,8 +191,8 @@ def algorithmic(w, n_kept, frontier_rows, prefix_len):
 
 def cycle_roof_us(w, alg):
     """Roofline time of one cycle: each call at max(bytes / HBM peak,
-    flops / bf16 MFMA peak) from its algorithmic bytes and flops (rerank
-    and mask move negligible bytes)."""
+    flops / bf16 MFMA peak) from its algorithmic bytes and flops (the
+    rerank and mask call moves negligible bytes)."""
     bw = HBM_PEAK_GBS * 1e3      # bytes per us
     mf = MFMA_BF16_PEAK_TFLOPS * 1e6  # flops per us
     t = sum(b / bw for b in alg["draft"])
@@ -363,7 +364,7 @@ class Bench:
         host's launch rate.  The D draft steps of a cycle sit between one
         pair of events."""
         torch, w, plan, stream = self.torch, self.w, self.plan, self.stream
-        names = ["draft", "rerank", "mask", "attention", "accept"]
+        names = ["draft", "rerank_mask", "attention", "accept"]
         acc = {n: 0.0 for n in names}
         cnt = {n: 0 for n in names}
 
@@ -375,8 +376,7 @@ class Bench:
                 plan.draft_step(step, ds["roots"], ds["draft"][:, step - 1], stream)
             e1.record(stream)
             row.append(("draft", e0, e1))
-            for n, fn in (("rerank", lambda: plan.rerank(stream)),
-                          ("mask", lambda: plan.tree_mask(ds["prefix"], stream)),
+            for n, fn in (("rerank_mask", lambda: plan.rerank_mask(ds["prefix"], stream)),
                           ("attention", lambda: plan.tree_attention(
                               ds["attn"]["q"], ds["attn"]["k_cache"],
                               ds["attn"]["v_cache"], ds["attn"]["k_tree"],

@@ -628,6 +628,40 @@ int et_rerank(et_plan_t plan, void* ws, int32_t* tokens, int32_t* parent_slot,
   return rc;
 }
 
+int et_rerank_mask(et_plan_t plan, void* ws, int32_t* tokens, int32_t* parent_slot,
+                   float* conf, float* value, int32_t* n_kept,
+                   const int32_t* prefix_len, uint64_t* mask, int32_t* depth,
+                   int32_t* pos_ids, et_stream_t stream) {
+  const char* fn = "et_rerank_mask";
+  CHECK_PTR(plan);
+  CHECK_PTR(ws);
+  CHECK_PTR(tokens);
+  CHECK_PTR(parent_slot);
+  CHECK_PTR(conf);
+  CHECK_PTR(value);
+  CHECK_PTR(n_kept);
+  CHECK_PTR(prefix_len);
+  CHECK_PTR(mask);
+  CHECK_PTR(depth);
+  CHECK_PTR(pos_ids);
+  et::Plan& p = *as_plan(plan);
+  const hipStream_t st = (hipStream_t)stream;
+  if (p.last_ws != ws || p.last_step != p.D)
+    return fail(ET_ESTATE, "%s: the tree is not complete (last step %d of "
+                "%d on this workspace)", fn, p.last_step, p.D);
+  if (p.debug) {
+    const int rc = debug_prefix(p, fn, prefix_len, st);
+    if (rc != ET_OK) return rc;
+  }
+  int rc = hip_status(et::launch_rerank_mask(p, et::draft_ws(p, ws), tokens, parent_slot,
+                                             conf, value, n_kept, prefix_len, mask,
+                                             depth, pos_ids, st),
+                      fn);
+  if (rc == ET_OK && p.debug) rc = debug_sync(fn, st);
+  if (rc == ET_OK && p.debug) rc = debug_tree(p, fn, tokens, parent_slot, n_kept, st);
+  return rc;
+}
+
 int et_tree_mask(et_plan_t plan, const int32_t* parent_slot,
                  const int32_t* n_kept, const int32_t* prefix_len,
                  uint64_t* mask, int32_t* depth, int32_t* pos_ids,

@@ -161,6 +161,11 @@ hipError_t launch_draft_step_hidden(const Plan& p, const DraftWs& w, const LmWs&
 hipError_t launch_rerank(const Plan& p, const DraftWs& w, int32_t* tokens,
                          int32_t* parent_slot, float* conf, float* value,
                          int32_t* n_kept, hipStream_t s);
+hipError_t launch_rerank_mask(const Plan& p, const DraftWs& w, int32_t* tokens,
+                              int32_t* parent_slot, float* conf, float* value,
+                              int32_t* n_kept, const int32_t* prefix_len,
+                              uint64_t* mask, int32_t* depth, int32_t* pos,
+                              hipStream_t s);
 hipError_t launch_static_tree(const Plan& p, const DraftWs& w, const FixedSlots& fs,
                               int32_t* tokens, int32_t* parent_slot, float* conf,
                               float* value, int32_t* n_kept, hipStream_t s);

@@ -25,7 +25,12 @@ struct RerankArgs {
   float* conf;
   float* value;
   int32_t* n_kept;
-  int B, N, T, cap;
+  // flatten outputs (the fused form only)
+  const int32_t* prefix_len;
+  uint64_t* mask;
+  int32_t* depth;
+  int32_t* pos;
+  int B, N, T, W, cap;
 };
 
 // One block per sequence.  Pool keys (value, -depth, -token, -index) order
@@ -36,12 +41,12 @@ struct RerankArgs {
 // Selection of the n = min(N, pool) largest keys is a radix select from
 // the top: a 256-bucket histogram of the next 8 key bits, restricted to
 // the keys that share the prefix chosen so far, picks the bucket where the
-// count from the top first reaches n.  Usually two levels (value exponent
-// and leading mantissa bits) leave at most kRerankCand keys at or above
-// the prefix; further levels run only while more remain.  Keys are
-// distinct (the index field), so the eighth level leaves exactly n.  The
-// survivors are ranked by counting in LDS.
-constexpr int kRerankCand = 1024;
+// count from the top first reaches n.  Levels continue until at most
+// max(128, n + 64) keys lie at or above the prefix (usually two: value
+// exponent, then leading mantissa bits).  Keys are distinct (the index
+// field), so the eighth level leaves exactly n.  The survivors are ranked
+// by counting in LDS, each by a group of lanes that split the list.
+constexpr int kRerankCand = 512;  // >= max(128, n + 64) for n <= 255
 
 // Wave 0: find the largest bucket c of hist[0..255] whose suffix count
 // (sum of hist[c..255]) reaches `need`; returns c and the count above c.
@@ -77,15 +82,20 @@ __device__ __forceinline__ void suffix_pick(const uint32_t* hist, int need,
   *above = __shfl(ab, src);
 }
 
+// MASK: also flatten the kept tree (the tree-mask outputs), from the
+// parent slots held in LDS, in the same launch.
+template <bool MASK>
 __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(RerankArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x;
   __shared__ uint64_t s_cand[kRerankCand];
   __shared__ int16_t s_slot[kRerankMaxPool];
+  __shared__ int16_t s_ps[MASK ? 256 : 1];  // parent slot of each slot
   __shared__ uint32_t s_hist[256];
   __shared__ int s_pick, s_above, s_count;
   const int64_t pb = (int64_t)b * a.cap;
   const int P = a.ws.pool_count[b];
   const int n = P < a.N ? P : a.N;
+  const int pre = MASK ? a.prefix_len[b] : 0;
   constexpr int PER = kRerankMaxPool / kRerankThreads;
   // Each thread keeps its nodes' fields in registers: the kept ones are
   // written out by their owner once the ranks are known, with no second
@@ -138,7 +148,7 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(RerankArgs a) {
     cnt = above + (int)s_hist[c];
     shift = sh;
     __syncthreads();  // s_hist and s_pick are rewritten by the next level
-    if (cnt <= kRerankCand) break;
+    if (cnt <= max(128, n + 64)) break;
   }
   const uint64_t T = prefix << shift;
   const int64_t ob = (int64_t)b * a.T;
@@ -147,19 +157,17 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(RerankArgs a) {
     for (int i = 0; i < PER; ++i)
       if (key[i] != 0 && key[i] >= T) s_cand[atomicAdd(&s_count, 1)] = key[i];
     __syncthreads();
-    for (int t = tid; t < cnt; t += kRerankThreads) {
+    // g consecutive lanes rank one candidate, each counting every g-th key
+    // of the list; a butterfly over the group adds the counts.  The group
+    // shares its loop trip count, so all its lanes take part in the sums.
+    const int g = cnt <= 64 ? 16 : cnt <= 128 ? 8 : cnt <= 256 ? 4 : 2;
+    const int part = tid & (g - 1);
+    for (int t = tid / g; t < cnt; t += kRerankThreads / g) {
       const uint64_t me = s_cand[t];
-      int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
-      int j = 0;
-      for (; j + 4 <= cnt; j += 4) {
-        r0 += s_cand[j] > me;
-        r1 += s_cand[j + 1] > me;
-        r2 += s_cand[j + 2] > me;
-        r3 += s_cand[j + 3] > me;
-      }
-      for (; j < cnt; ++j) r0 += s_cand[j] > me;
-      const int rank = (r0 + r1) + (r2 + r3);
-      if (rank < n) s_slot[pool_index_of(me)] = (int16_t)(rank + 1);
+      int rank = 0;
+      for (int j = part; j < cnt; j += g) rank += s_cand[j] > me ? 1 : 0;
+      for (int o = 1; o < g; o <<= 1) rank += __shfl_xor(rank, o);
+      if (part == 0 && rank < n) s_slot[pool_index_of(me)] = (int16_t)(rank + 1);
     }
   }
   __syncthreads();
@@ -170,10 +178,12 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(RerankArgs a) {
     const int idx = tid + kRerankThreads * i;
     const int s = key[i] != 0 ? s_slot[idx] : -1;
     if (s > 0) {
+      const int ps = par[i] < 0 ? 0 : s_slot[par[i]];
       a.tokens[ob + s] = pool_token_of(key[i]);
-      a.parent_slot[ob + s] = par[i] < 0 ? 0 : s_slot[par[i]];
+      a.parent_slot[ob + s] = ps;
       a.conf[ob + s] = cnf[i];
       a.value[ob + s] = pool_value_of(key[i]);
+      if (MASK) s_ps[s] = (int16_t)ps;
     }
   }
   // the root and the pad slots
@@ -185,6 +195,37 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(RerankArgs a) {
     a.value[ob + s] = s == 0 ? 1.f : 0.f;
   }
   if (tid == 0) a.n_kept[b] = n;
+  if constexpr (MASK) {
+    // Flatten: slot s <= n walks its parent slots (each smaller than its
+    // own, so the walk ends at the root within s steps), setting one mask
+    // bit per slot on its path.
+    if (tid == 0) s_ps[0] = -1;
+    __syncthreads();
+    const int s = tid;
+    if (s < a.T) {
+      const int64_t o = ob + s;
+      uint64_t bits[4] = {0, 0, 0, 0};
+      int d = -1, p = -1;
+      if (s <= n) {
+        int cur = s;
+        d = 0;
+        for (int guard = 0; guard < a.T; ++guard) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            if ((cur >> 6) == w) bits[w] |= 1ull << (cur & 63);
+          if (cur <= 0) break;
+          cur = s_ps[cur];
+          ++d;
+        }
+        p = pre + d;
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        if (w < a.W) a.mask[o * a.W + w] = bits[w];
+      a.depth[o] = d;
+      a.pos[o] = p;
+    }
+  }
 }
 
 hipError_t launch_rerank(const Plan& p, const DraftWs& w, int32_t* tokens,
@@ -197,11 +238,40 @@ hipError_t launch_rerank(const Plan& p, const DraftWs& w, int32_t* tokens,
   a.conf = conf;
   a.value = value;
   a.n_kept = n_kept;
+  a.prefix_len = nullptr;
+  a.mask = nullptr;
+  a.depth = a.pos = nullptr;
   a.B = p.B;
   a.N = p.N;
   a.T = p.T;
+  a.W = p.W;
   a.cap = p.cap;
-  rerank_kernel<<<p.B, kRerankThreads, 0, s>>>(a);
+  rerank_kernel<false><<<p.B, kRerankThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rerank_mask(const Plan& p, const DraftWs& w, int32_t* tokens,
+                              int32_t* parent_slot, float* conf, float* value,
+                              int32_t* n_kept, const int32_t* prefix_len,
+                              uint64_t* mask, int32_t* depth, int32_t* pos,
+                              hipStream_t s) {
+  RerankArgs a;
+  a.ws = w;
+  a.tokens = tokens;
+  a.parent_slot = parent_slot;
+  a.conf = conf;
+  a.value = value;
+  a.n_kept = n_kept;
+  a.prefix_len = prefix_len;
+  a.mask = mask;
+  a.depth = depth;
+  a.pos = pos;
+  a.B = p.B;
+  a.N = p.N;
+  a.T = p.T;
+  a.W = p.W;
+  a.cap = p.cap;
+  rerank_kernel<true><<<p.B, kRerankThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -187,6 +187,19 @@ int et_tree_mask(et_plan_t plan, const int32_t* parent_slot,
                  uint64_t* mask, int32_t* depth, int32_t* pos_ids,
                  et_stream_t stream);
 
+/* Rerank and flatten in one launch ([P1] s4.2: rerank, then the flattened
+ * sequence and its mask): writes every output of et_rerank and of
+ * et_tree_mask, with the same values and layouts as that pair of calls
+ * (et_tree_mask applied to the rerank's parent_slot and n_kept).  The
+ * parent walk reads the parent slots from on-chip memory, so neither the
+ * second launch nor a reread of parent_slot is needed.  Requirements and
+ * errors are those of et_rerank, plus the prefix_len range of
+ * et_tree_mask (checked in debug mode). */
+int et_rerank_mask(et_plan_t plan, void* ws, int32_t* tokens, int32_t* parent_slot,
+                   float* conf, float* value, int32_t* n_kept,
+                   const int32_t* prefix_len, uint64_t* mask, int32_t* depth,
+                   int32_t* pos_ids, et_stream_t stream);
+
 /* Tree attention, the verify pass ([P1] s4.2; [P2]: the tree is checked
  * in one tree-attention pass; [P3]: Medusa-style tree attention).
  * For sequence b, query head h (kv head h / G) and slot s <= n_kept[b]:

@@ -237,6 +237,20 @@ def _check_rerank_mask(r):
                                   om["mask"])
     np.testing.assert_array_equal(plan.depth.cpu().numpy(), om["depth"])
     np.testing.assert_array_equal(plan.pos_ids.cpu().numpy(), om["pos_ids"])
+    # rerank and flatten in one launch: every output element written, each
+    # equal bit for bit to what the pair of calls wrote
+    fields = ("tokens", "parent_slot", "conf", "value", "n_kept", "mask", "depth",
+              "pos_ids")
+    pair = {f: getattr(plan, f).clone() for f in fields}
+    for f in fields:
+        getattr(plan, f).fill_(-7)
+    plan.rerank_mask(r["dev"]["prefix_len"])
+    torch.cuda.synchronize()
+    for f in fields:
+        a, b = getattr(plan, f), pair[f]
+        if a.dtype == torch.float32:
+            a, b = a.view(torch.int32), b.view(torch.int32)
+        assert torch.equal(a, b), f"et_rerank_mask {f} differs from the pair of calls"
 
 
 # Attention outputs compared in full against the oracle (OpenMP over
