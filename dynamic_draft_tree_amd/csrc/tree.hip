@@ -99,24 +99,39 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(RerankArgs a) {
   constexpr int PER = kRerankMaxPool / kRerankThreads;
   // Each thread keeps its nodes' fields in registers: the kept ones are
   // written out by their owner once the ranks are known, with no second
-  // round of pool loads.
+  // round of pool loads.  The loads cover the whole capacity (cap <=
+  // kRerankMaxPool, all of it readable) and go out together with the pool
+  // size's; entries at or past the size are dropped once it arrives.
+  // (Loads in rounds of the block size, as many as the capacity needs; the
+  // index is clamped rather than guarded so that no branch splits them,
+  // and the values pass through an empty asm after the last load is
+  // issued, so that nothing computed from them is scheduled between the
+  // loads, each such use being a wait for the memory round trip.)
   uint64_t key[PER];
-  int par[PER];
-  float cnf[PER];
-  const int root = tid == 0 ? a.ws.root_token[b] : -1;
+  int par[PER], dep[PER], tok[PER];
+  float cnf[PER], val[PER];
+  const int root = a.ws.root_token[b];
+  const int rounds = (a.cap + kRerankThreads - 1) / kRerankThreads;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int idx = tid + kRerankThreads * i;
-    key[i] = 0;
-    par[i] = -1;
-    cnf[i] = 0.f;
-    if (idx < P) {
-      key[i] = pool_key(a.ws.pool_value[pb + idx], a.ws.pool_depth[pb + idx],
-                        a.ws.pool_token[pb + idx], idx);
-      par[i] = a.ws.pool_parent[pb + idx];
-      cnf[i] = a.ws.pool_conf[pb + idx];
+    val[i] = cnf[i] = 0.f;
+    par[i] = dep[i] = tok[i] = -1;
+    if (i < rounds) {  // uniform
+      const int64_t g = pb + min(idx, a.cap - 1);
+      val[i] = a.ws.pool_value[g];
+      dep[i] = a.ws.pool_depth[g];
+      tok[i] = a.ws.pool_token[g];
+      par[i] = a.ws.pool_parent[g];
+      cnf[i] = a.ws.pool_conf[g];
     }
     s_slot[idx] = -1;
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    asm volatile("" : "+v"(val[i]), "+v"(dep[i]), "+v"(tok[i]), "+v"(par[i]), "+v"(cnf[i]));
+    const int idx = tid + kRerankThreads * i;
+    key[i] = idx < P ? pool_key(val[i], dep[i], tok[i], idx) : 0;
   }
   if (tid == 0) s_count = 0;
   uint64_t prefix = 0;  // chosen high key bits, right-aligned
