@@ -337,7 +337,12 @@ int et_plan_create(const et_config* cfg, et_plan_t* out) {
   p->Pcap = c.prefix_cap;
   p->ldt = c.logits_dtype;
   p->qdt = c.qkv_dtype;
-  p->s_draft = (p->V + et::chunk_elems(p->ldt) - 1) / et::chunk_elems(p->ldt);
+  {
+    const int narrow = (p->V + et::chunk_elems(p->ldt, false) - 1) / et::chunk_elems(p->ldt, false);
+    p->draft_wide = (long long)p->B * p->k * narrow > et::kScanWideBlocks;
+    const int ce = et::chunk_elems(p->ldt, p->draft_wide);
+    p->s_draft = (p->V + ce - 1) / ce;
+  }
   p->s_accept = (p->V + et::accept_chunk_elems(p->ldt) - 1) / et::accept_chunk_elems(p->ldt);
   p->draft_cpb = chunks_per_block((long long)p->B * p->k, p->s_draft);
   p->accept_cpb = chunks_per_block((long long)p->B * p->T, p->s_accept);

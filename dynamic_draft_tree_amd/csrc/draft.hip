@@ -18,6 +18,8 @@
 // value), appends them to the pool and selects the next frontier.  (A
 // single launch in which the last scan block to arrive does the merge was
 // slower: every block then waits for its stores and an arrival ticket.)
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
@@ -186,25 +188,28 @@ __device__ __forceinline__ void scan_chunks(const DraftArgs& a, const char* row,
   const int lim = a.V - lid;
   // Ids past V read -inf, so with a finite Lw no bound check is needed;
   // Lw = -inf (fewer than k lanes of the wave inside the row) takes it.
-  static_assert(E <= 32, "one mask bit per element");
-  uint32_t bits = 0u;
+  static_assert(E <= 64, "one mask bit per element");
+  using mask_t = typename std::conditional<(E > 32), uint64_t, uint32_t>::type;
+  mask_t bits = 0u;
   if (Lw > -INFINITY) {
     // x >= Lw exactly when x - Lw has a clear sign bit: x - Lw is +0 for
     // x == Lw and -inf for x = -inf (inputs hold no NaN or +inf), and a
     // zero bound is taken as -0 so that an element -0, equal to it, gives
     // +0.  Each sign bit is shifted into a register with one alignbit
-    // ((neg << 1) | (d >> 31)), element e ending at bit E - 1 - e; one bit
-    // reversal then puts element e at bit e.
+    // ((neg << 1) | (d >> 31)), elements 32 h .. 32 h + 31 into word h,
+    // element e ending at bit n_h - 1 - (e - 32 h) of it (n_h elements);
+    // one bit reversal per word then puts element e at bit e - 32 h.
     const float Lz = Lw == 0.f ? -0.f : Lw;
-    uint32_t neg = 0u;
+    uint32_t neg[2] = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      neg = __builtin_amdgcn_alignbit(neg, __float_as_uint(xv(e) - Lz), 31);
-    bits = __brev(~neg) >> (32 - E);
+      neg[e >> 5] = __builtin_amdgcn_alignbit(neg[e >> 5], __float_as_uint(xv(e) - Lz), 31);
+    bits = (mask_t)(__brev(~neg[0]) >> (32 - (E < 32 ? E : 32)));
+    if constexpr (E > 32) bits |= (mask_t)(__brev(~neg[1]) >> (64 - E)) << 32;
   } else {
     // (one is opaque to the compiler: written as cond ? 1 << e : 0 the
     // masks would be hoisted out of the chunk loop into registers)
-    uint32_t one = 1u;
+    mask_t one = 1u;
     asm volatile("" : "+v"(one));
 #pragma unroll
     for (int e = 0; e < E; ++e)
@@ -228,11 +233,11 @@ __device__ __forceinline__ void scan_chunks(const DraftArgs& a, const char* row,
   if constexpr (VEC)
     if (ci + 1 < nch) issue_chunk<BF16, E>(row, base + kChunkE, a.V, tid, raw);
   int wtot;
-  int o = wave_excl_prefix_small<kE2Bits>(__popc(bits), &wtot);  // popc(bits) <= E
+  int o = wave_excl_prefix_small<kE2Bits>(__popcll((uint64_t)bits), &wtot);  // <= E
   uint64_t* wl = &s_wl[wave * kWaveCap];
   if (wtot <= kWaveCap) {
     while (bits) {
-      const int e = __ffs(bits) - 1;
+      const int e = __ffsll((unsigned long long)bits) - 1;
       bits &= bits - 1;
       wl[o++] = logit_key(xs(e), (uint32_t)(lid + elem_off<BF16>(e, 0)));
     }
@@ -568,7 +573,7 @@ __device__ __forceinline__ void merge_rows(const DraftArgs& a, const FixedFronti
 // behind the logits'.  WAVE: per-wave partials (when a row's S * 4 lists
 // fit one merge wave), else per-block partials.
 template <bool BF16, bool VEC, int E, bool WAVE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? 3 : 1))) void draft_scan_kernel(DraftArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? (E > 32 ? 4 : 3) : 1))) void draft_scan_kernel(DraftArgs a) {
   constexpr int kChunkE = kScanThreads * E;
   const int j = blockIdx.y, b = blockIdx.z;
   if (a.step == 1 && j > 0) return;  // the root is the only row of step 1
@@ -648,15 +653,21 @@ hipError_t launch_draft_step(const Plan& p, const DraftWs& w, int step,
   const dim3 grid((p.s_draft + p.draft_cpb - 1) / p.draft_cpb, p.k, p.B);
   const bool wv = p.s_draft * kWaves <= 64;
   a.parts = wv ? p.s_draft * kWaves : p.s_draft;
-#define ET_SCAN(W)                                                                               \
-  do {                                                                                           \
-    if (bf && vec) draft_scan_kernel<true, true, kElemsBf16, W><<<grid, kScanThreads, 0, s>>>(a);  \
-    else if (bf) draft_scan_kernel<true, false, kElemsBf16, W><<<grid, kScanThreads, 0, s>>>(a);   \
-    else if (vec) draft_scan_kernel<false, true, kElemsF32, W><<<grid, kScanThreads, 0, s>>>(a);   \
-    else draft_scan_kernel<false, false, kElemsF32, W><<<grid, kScanThreads, 0, s>>>(a);          \
+#define ET_SCAN(W, X)                                                                                   \
+  do {                                                                                                  \
+    if (bf && vec) draft_scan_kernel<true, true, X * kElemsBf16, W><<<grid, kScanThreads, 0, s>>>(a);  \
+    else if (bf) draft_scan_kernel<true, false, X * kElemsBf16, W><<<grid, kScanThreads, 0, s>>>(a);   \
+    else if (vec) draft_scan_kernel<false, true, X * kElemsF32, W><<<grid, kScanThreads, 0, s>>>(a);   \
+    else draft_scan_kernel<false, false, X * kElemsF32, W><<<grid, kScanThreads, 0, s>>>(a);          \
   } while (0)
-  if (wv) ET_SCAN(true);
-  else ET_SCAN(false);
+  // wide chunks (twice the elements per thread) for grids of many rows
+  if (p.draft_wide) {
+    if (wv) ET_SCAN(true, 2);
+    else ET_SCAN(false, 2);
+  } else {
+    if (wv) ET_SCAN(true, 1);
+    else ET_SCAN(false, 1);
+  }
 #undef ET_SCAN
 #define ET_MERGE(BF, K)                                                                  \
   do {                                                                                   \

@@ -39,9 +39,10 @@ constexpr int kAccElemsF32 = 32;
 constexpr int accept_chunk_elems(int dtype) {
   return kScanThreads * (dtype == ET_BF16 ? kAccElemsBf16 : kAccElemsF32);
 }
-// vocab elements per row-scan block for a logits dtype
-constexpr int chunk_elems(int dtype) {
-  return kScanThreads * (dtype == ET_BF16 ? kElemsBf16 : kElemsF32);
+// vocab elements per row-scan block for a logits dtype; wide chunks hold
+// twice as many (eight 16-byte loads per thread)
+constexpr int chunk_elems(int dtype, bool wide) {
+  return kScanThreads * (dtype == ET_BF16 ? kElemsBf16 : kElemsF32) * (wide ? 2 : 1);
 }
 // Scan grids (draft and accept) above this many one-chunk blocks give
 // each block several chunks of its row (the chip holds a few thousand
@@ -50,6 +51,14 @@ constexpr int chunk_elems(int dtype) {
 #define ET_SCAN_TARGET_BLOCKS 6000
 #endif
 constexpr int kScanTargetBlocks = ET_SCAN_TARGET_BLOCKS;
+// Draft scan grids above this many (narrow) blocks use wide chunks: a
+// thread's fixed work per chunk (wave bound, candidate list, partial
+// record) is then paid once per twice the elements, where the many waves
+// per SIMD make the scan bound by instruction issue.
+#ifndef ET_SCAN_WIDE_BLOCKS
+#define ET_SCAN_WIDE_BLOCKS 2048
+#endif
+constexpr int kScanWideBlocks = ET_SCAN_WIDE_BLOCKS;
 constexpr int kAttnTile = 64;            // keys per staged K/V tile
 constexpr int kAttnMaxSplits = 32;       // key splits per (kv head, row block)
 #ifndef ET_ATTN_TARGET_BLOCKS
@@ -105,6 +114,7 @@ struct Plan {
   int ldt, qdt;           // et_dtype of logits and q/k/v
   int s_draft;            // vocab chunks per row
   int draft_cpb;          // chunks streamed by one draft scan block
+  int draft_wide;         // draft scan chunks of twice the elements per thread
   int s_accept;           // target-row chunks per row
   int accept_cpb;         // chunks streamed by one accept scan block
   int attn_wr;            // 16-row groups per wave (rows per block 64*wr)

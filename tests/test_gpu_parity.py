@@ -72,13 +72,20 @@ VARIANTS = {
                             sharpness=(2.5, 0.8), n_q_heads=4, n_kv_heads=1,
                             head_dim=128, prefix_cap=128,
                             prefix_range=(64, 128), qkv_dtype="bf16", seed=13),
-    # more than 6000 one-chunk scan blocks: two chunks per block, fp32
-    # logits with per-block partials (the scan loop's barrier path)
-    "f32_multi_chunk": TINY.with_(batch=16, vocab=100000, topk=16, depth=2,
+    # more than 6000 (wide) scan blocks: wide chunks, two per block, fp32
+    # logits (the scan loop's chunk-to-chunk path)
+    "f32_multi_chunk": TINY.with_(batch=32, vocab=100000, topk=16, depth=2,
                                   budget_n=16, threshold=0.0,
-                                  sharpness=tuple([2.5, 0.8] * 8),
+                                  sharpness=tuple([2.5, 0.8] * 16),
                                   n_q_heads=2, n_kv_heads=1, head_dim=64,
                                   prefix_cap=64, prefix_range=(1, 64), seed=14),
+    # wide chunks on the element-wise path: an odd vocab leaves bf16 rows
+    # unaligned, and 64 x 8 rows of 5 narrow chunks exceed the wide limit
+    "wide_bf16_rows": TINY.with_(batch=64, vocab=40099, topk=8, depth=3,
+                                 budget_n=24, threshold=0.0, logits_dtype="bf16",
+                                 sharpness=tuple([2.5, 0.8] * 32), n_q_heads=2,
+                                 n_kv_heads=1, head_dim=64, prefix_cap=64,
+                                 prefix_range=(1, 64), qkv_dtype="bf16", seed=16),
     # 128-row attention blocks (G * T rows = 488 per kv head, no key
     # split): the three-buffer path, compared in full
     "rows128_bf16": TINY.with_(batch=8, vocab=5000, topk=10, depth=8,
