@@ -132,6 +132,93 @@ def summarize_pmc(args):
     print(json.dumps(out))
 
 
+def trace_durations_us(db):
+    """Mean duration (us) per kernel name in a rocprofv3 kernel-trace
+    database (rocpd SQLite, table kernels)."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    out = {}
+    for name, dur in con.execute("select name, duration from kernels"):
+        out.setdefault(name, []).append(float(dur))
+    con.close()
+    return {k: float(np.mean(v)) / 1e3 for k, v in out.items()}
+
+
+# Engine clock for converting busy cycles to time: 2.4 GHz, the clock an
+# s_memtime / s_memrealtime comparison reads inside a kernel on this part.
+SCLK_GHZ = 2.4
+N_SIMD = 1024  # 256 compute units x 4
+
+
+def summarize_counters(args):
+    """Write profiles/<call>_<workload>_counters.json: per kernel of the
+    call, the mean per dispatch of every counter in the given --pmc runs
+    of the bench, HBM bytes (FETCH_SIZE, WRITE_SIZE scaled by the copy
+    calibration runs), instructions per wave, the matrix-core busy fraction
+    and achieved bf16 rate over the kernel's mean duration in a
+    kernel-trace run of the same command."""
+    call = args.summarize_call
+    cfetch, cwrite = args.copy_dirs
+    copy_bytes = args.copy_mb * (1 << 20)
+
+    def means(dirs, name_part):
+        acc = {}
+        for d in dirs:
+            for k, c, x in pmc_rows(d):
+                if name_part in k:
+                    acc.setdefault(c, []).append(x)
+        return {c: float(np.mean(v)) for c, v in acc.items()}, \
+            max((len(v) for v in acc.values()), default=0)
+
+    cf = means([cfetch], "neg_kernel")[0]["FETCH_SIZE"]
+    cw = means([cwrite], "neg_kernel")[0]["WRITE_SIZE"]
+    f_fetch, f_write = copy_bytes / cf, copy_bytes / cw
+    durs = trace_durations_us(args.trace_db)
+    kernels = {}
+    for kn in CALLS[call][0]:
+        c, n = means(args.summarize_counters, kn)
+        if not c:  # not launched at this workload (e.g. no key split)
+            kernels[kn] = {"dispatches": 0}
+            continue
+        dur = [v for k, v in durs.items() if kn in k]
+        us = float(np.mean(dur)) if dur else None
+        waves = c.get("SQ_WAVES", 0.0)
+        e = {"dispatches": n, "avg_us": round(us, 3) if us else None,
+             "counters": {k: round(v, 1) for k, v in sorted(c.items())}}
+        if "FETCH_SIZE" in c and "WRITE_SIZE" in c:
+            e["fetch_bytes"] = round(c["FETCH_SIZE"] * f_fetch)
+            e["write_bytes"] = round(c["WRITE_SIZE"] * f_write)
+            if us:
+                gbs = (e["fetch_bytes"] + e["write_bytes"]) / (us * 1e3)
+                e["hbm_gbs"] = round(gbs, 1)
+                e["frac_hbm_peak"] = round(gbs / HBM_PEAK_GBS, 4)
+        if "TCC_HIT_sum" in c and "TCC_MISS_sum" in c:
+            tot = c["TCC_HIT_sum"] + c["TCC_MISS_sum"]
+            e["l2_hit_rate"] = round(c["TCC_HIT_sum"] / tot, 4) if tot else None
+        if waves:
+            e["per_wave"] = {k[len("SQ_INSTS_"):].lower(): round(v / waves, 1)
+                             for k, v in c.items()
+                             if k.startswith("SQ_INSTS_") and "MOPS" not in k}
+        if us and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            busy_us = c["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMD / (SCLK_GHZ * 1e3)
+            e["mfma_busy_us_per_simd"] = round(busy_us, 3)
+            e["mfma_busy_frac"] = round(busy_us / us, 4)
+        if us and c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16"):
+            tf = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / (us * 1e-6) / 1e12
+            e["bf16_tflops"] = round(tf, 1)
+            e["frac_mfma_peak"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+        kernels[kn] = e
+    out = {"call": call, "workload": args.workload, "kernels": kernels,
+           "copy_calibration": {"bytes": copy_bytes, "fetch_kib": cf, "write_kib": cw,
+                                "fetch_bytes_per_unit": f_fetch,
+                                "write_bytes_per_unit": f_write},
+           "sclk_ghz": SCLK_GHZ, "source_digest": source_digest(call)}
+    path = os.path.join(ROOT, "profiles", f"{call}_{args.workload}_counters.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
 def copy_calibration(args):
     """A plain device copy of --copy-mb MiB, the reference for scaling the
     FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -168,6 +255,14 @@ def parse():
                     help="write the traffic summary from the FETCH_SIZE and "
                          "WRITE_SIZE runs of the bench and of the copy")
     ap.add_argument("--summarize-call", default="draft_step", choices=sorted(CALLS))
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="write the counter summary of --summarize-call from "
+                         "these --pmc runs of the bench (with --copy-dirs and "
+                         "--trace-db)")
+    ap.add_argument("--copy-dirs", nargs=2, metavar="DIR",
+                    help="FETCH_SIZE and WRITE_SIZE runs of the copy")
+    ap.add_argument("--trace-db", help="rocprofv3 kernel-trace database of the "
+                                       "same bench command")
     return ap.parse_args()
 
 
@@ -553,6 +648,9 @@ def main():
     args = parse()
     if args.summarize_pmc:
         summarize_pmc(args)
+        return
+    if args.summarize_counters:
+        summarize_counters(args)
         return
     if args.copy_mb:
         copy_calibration(args)

@@ -297,11 +297,17 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   __syncthreads();
 
   const int sw = r16 & (CPR - 1);  // swizzle of the K rows this lane reads
+  // A row group whose rows all lie past the kept slots' rows (the last
+  // block of a unit whose row count is not a multiple of the block's) only
+  // helps stage the tiles: its accumulators stay zero, which writes the
+  // zero output (or empty partial) such rows get.
+  const bool active = row0 + rg * 16 * WR < R;  // wave-uniform
   for (int it = 0; it < cnt; ++it) {
     const int cur = it % NB;
     // buffer (it+PD) % NB was last read in iteration it-1, before its barrier
     if (it + PD < cnt) ET_ISSUE_TILE(t_begin + it + PD, (it + PD) % NB);
 
+    if (active) {
     const int t = t_begin + it;
     const bool tree = t >= tp;
     const int key0 = (tree ? t - tp : t) * kAttnTile;
@@ -423,6 +429,7 @@ void tree_attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int w = 0; w < WR; ++w)
       lacc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[w], lacc[w], 0, 0, 0);
+    }  // active
     // tile it+1 must have landed before the barrier; tile it+2 may fly on
     if (PD > 1 && it + 2 < cnt) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * CH));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
