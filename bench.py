@@ -1,8 +1,9 @@
 """Throughput of one EAGLE-2 draft-tree build + verify cycle on one MI355X.
 
-A step is one whole cycle over one batch: D x et_draft_step, et_rerank_mask
-(rerank and tree mask in one launch), et_tree_attention (one attention
-layer) and et_accept, on
+A step is one whole cycle over one batch: D - 1 x et_draft_step, then
+et_draft_step_last (the last draft step, whose merge also reranks the pool
+and flattens the tree), et_tree_attention (one attention layer) and
+et_accept, on
 synthetic inputs already resident in HBM.  The default workload is the
 Llama-3.1-8B shape at batch 1 (vocab 128256, top-k 10, depth 8, N 60,
 GQA 32/8 x 128, prefix 4096, bf16).  Input sets rotate so the working set
@@ -45,6 +46,8 @@ MALL_BYTES = 256 << 20
 CALLS = {
     "draft_step": (["draft_scan_kernel", "draft_merge_kernel"],
                    ["draft.hip", "device.h", "internal.h"]),
+    "draft_step_last": (["draft_scan_kernel", "draft_merge_last_kernel"],
+                        ["draft.hip", "rerank.h", "device.h", "internal.h"]),
     "accept": (["accept_scan_kernel", "accept_walk_kernel"],
                ["accept.hip", "device.h", "internal.h"]),
     "tree_attention": (["tree_attn_bf16_kernel", "tree_attn_merge_kernel"],
@@ -296,13 +299,23 @@ def cycle_roof_us(w, alg):
     return t
 
 
+def draft_step_bytes(alg):
+    """Mean logits bytes of the ordinary draft steps (all but the last,
+    which the cycle takes as et_draft_step_last)."""
+    d = alg["draft"]
+    return float(np.mean(d[:-1])) if len(d) > 1 else float(d[0])
+
+
 def call_rooflines(w, alg, avg_us, copy_gbs):
     """Per call: algorithmic GB/s (TFLOP/s for attention too) against the
     8 TB/s peak and against the measured streaming copy."""
     out = {}
-    for name, byts, flops in (("draft", float(np.mean(alg["draft"])), 0.0),
+    for name, byts, flops in (("draft", draft_step_bytes(alg), 0.0),
+                              ("draft_last", alg["draft"][-1], 0.0),
                               ("attention", alg["attention"], alg["attention_flops"]),
                               ("accept", alg["accept"], 0.0)):
+        if name not in avg_us:
+            continue
         us = avg_us[name]
         gbs = byts / (us * 1e-6) / 1e9
         e = {"us": round(us, 3), "bytes": byts, "gbs": round(gbs, 1),
@@ -322,9 +335,9 @@ def dominant_roofline(w, alg, avg_us, per_cycle_us):
     average duration."""
     names = list(per_cycle_us)
     dominant = max(names, key=lambda n: per_cycle_us[n])
-    call = {"draft": "draft_step", "accept": "accept",
+    call = {"draft": "draft_step", "draft_last": "draft_step_last", "accept": "accept",
             "attention": "tree_attention"}.get(dominant)
-    bytes_per_call = {"draft": float(np.mean(alg["draft"])),
+    bytes_per_call = {"draft": draft_step_bytes(alg), "draft_last": alg["draft"][-1],
                       "accept": alg["accept"],
                       "attention": alg["attention"]}.get(dominant, 0.0)
     achieved = bytes_per_call / (avg_us[dominant] * 1e-6) / 1e9
@@ -459,19 +472,21 @@ class Bench:
         host's launch rate.  The D draft steps of a cycle sit between one
         pair of events."""
         torch, w, plan, stream = self.torch, self.w, self.plan, self.stream
-        names = ["draft", "rerank_mask", "attention", "accept"]
+        names = (["draft"] if w.depth > 1 else []) + ["draft_last", "attention", "accept"]
         acc = {n: 0.0 for n in names}
         cnt = {n: 0 for n in names}
 
         def enqueue_cycle(ds, row):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for step in range(1, w.depth + 1):
-                plan.draft_step(step, ds["roots"], ds["draft"][:, step - 1], stream)
-            e1.record(stream)
-            row.append(("draft", e0, e1))
-            for n, fn in (("rerank_mask", lambda: plan.rerank_mask(ds["prefix"], stream)),
+            if w.depth > 1:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for step in range(1, w.depth):
+                    plan.draft_step(step, ds["roots"], ds["draft"][:, step - 1], stream)
+                e1.record(stream)
+                row.append(("draft", e0, e1))
+            for n, fn in (("draft_last", lambda: plan.draft_step_last(
+                              ds["roots"], ds["draft"][:, w.depth - 1], ds["prefix"], stream)),
                           ("attention", lambda: plan.tree_attention(
                               ds["attn"]["q"], ds["attn"]["k_cache"],
                               ds["attn"]["v_cache"], ds["attn"]["k_tree"],
@@ -509,7 +524,7 @@ class Bench:
             for row in rows:
                 for n, e0, e1 in row:
                     acc[n] += e0.elapsed_time(e1) * 1e3  # us
-                    cnt[n] += w.depth if n == "draft" else 1
+                    cnt[n] += w.depth - 1 if n == "draft" else 1
             done += nb
         avg_us = {n: acc[n] / cnt[n] for n in names}
         per_cycle_us = {n: acc[n] / K for n in names}

@@ -12,6 +12,6 @@ from .binding import (EXPORTS, EtError, Plan, et_accept,  # noqa: F401
                       et_draft_step, et_kv_commit, et_plan_create,
                       et_plan_destroy,
                       et_pool_capacity, et_pool_export, et_rerank,
-                      et_rerank_mask,
+                      et_rerank_mask, et_draft_step_last,
                       et_tree_attention, et_tree_mask, et_workspace_bytes,
                       et_workspace_init, lib, make_config)

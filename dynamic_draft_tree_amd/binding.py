@@ -22,7 +22,8 @@ _STATUS = {ET_EINVAL: "ET_EINVAL", ET_EUNSUPPORTED: "ET_EUNSUPPORTED",
 
 EXPORTS = ("et_plan_create", "et_plan_destroy", "et_workspace_bytes",
            "et_pool_capacity", "et_workspace_init", "et_draft_step",
-           "et_rerank", "et_tree_mask", "et_rerank_mask", "et_tree_attention", "et_accept",
+           "et_rerank", "et_tree_mask", "et_rerank_mask", "et_draft_step_last",
+           "et_tree_attention", "et_accept",
            "et_accept_sample", "et_kv_commit", "et_pool_export",
            "et_set_static_shape", "et_draft_step_static", "et_static_tree",
            "et_draft_step_hidden", "et_accept_noalloc", "et_check_tree",
@@ -70,6 +71,7 @@ def lib():
             "et_rerank": ([vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "et_tree_mask": ([vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "et_rerank_mask": ([vp] * 12, ctypes.c_int),
+            "et_draft_step_last": ([vp, vp, vp, vp, i64, i64] + [vp] * 12, ctypes.c_int),
             "et_tree_attention": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp],
                                   ctypes.c_int),
             "et_accept": ([vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
@@ -213,6 +215,17 @@ def et_rerank(plan, ws, tokens, parent_slot, conf, value, n_kept,
     _check(lib().et_rerank(plan, _ptr(ws), _ptr(tokens), _ptr(parent_slot),
                            _ptr(conf), _ptr(value), _ptr(n_kept),
                            _stream(stream)))
+
+
+def et_draft_step_last(plan, ws, root_tokens, logits, next_tokens, next_count,
+                       prefix_len, tokens, parent_slot, conf, value, n_kept, mask,
+                       depth, pos_ids, stream=None):
+    bs, rs = _rows(logits)
+    _check(lib().et_draft_step_last(plan, _ptr(ws), _ptr(root_tokens), _ptr(logits), bs, rs,
+                                    _ptr(next_tokens), _ptr(next_count),
+                                    _ptr(prefix_len), _ptr(tokens), _ptr(parent_slot),
+                                    _ptr(conf), _ptr(value), _ptr(n_kept), _ptr(mask),
+                                    _ptr(depth), _ptr(pos_ids), _stream(stream)))
 
 
 def et_rerank_mask(plan, ws, tokens, parent_slot, conf, value, n_kept,
@@ -387,6 +400,13 @@ class Plan:
         et_tree_mask(self.handle, self.parent_slot, self.n_kept, prefix_len,
                      self.mask, self.depth, self.pos_ids, stream)
 
+    def draft_step_last(self, root_tokens, logits, prefix_len, stream=None):
+        """draft_step(D) and rerank_mask, the rerank in the step's merge."""
+        et_draft_step_last(self.handle, self.ws, root_tokens, logits, self.next_tokens,
+                           self.next_count, prefix_len, self.tokens, self.parent_slot,
+                           self.conf, self.value, self.n_kept, self.mask, self.depth,
+                           self.pos_ids, stream)
+
     def rerank_mask(self, prefix_len, stream=None):
         """rerank and tree_mask in one launch (same outputs)."""
         et_rerank_mask(self.handle, self.ws, self.tokens, self.parent_slot,
@@ -427,9 +447,9 @@ class Plan:
     def cycle(self, root_tokens, draft, prefix_len, attn, target,
               stream=None):
         """One whole cycle; draft is [B][D][k][V], draft[:, l] feeds step l+1."""
-        for step in range(1, self.w.depth + 1):
+        for step in range(1, self.w.depth):
             self.draft_step(step, root_tokens, draft[:, step - 1], stream)
-        self.rerank_mask(prefix_len, stream)
+        self.draft_step_last(root_tokens, draft[:, self.w.depth - 1], prefix_len, stream)
         self.tree_attention(attn["q"], attn["k_cache"], attn["v_cache"],
                             attn["k_tree"], attn["v_tree"], prefix_len,
                             stream=stream)

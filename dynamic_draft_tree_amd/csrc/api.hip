@@ -407,7 +407,8 @@ namespace {
 int draft_step(const char* fn, et_plan_t plan, void* ws, int32_t step,
                const int32_t* root_tokens, const void* logits,
                int64_t batch_stride, int64_t row_stride, int32_t* next_tokens,
-               int32_t* next_count, et_stream_t stream, bool fixed) {
+               int32_t* next_count, et_stream_t stream, bool fixed,
+               const et::RerankOut* last = nullptr) {
   CHECK_PTR(plan);
   CHECK_PTR(ws);
   CHECK_PTR(logits);
@@ -440,10 +441,12 @@ int draft_step(const char* fn, et_plan_t plan, void* ws, int32_t step,
   int rc = hip_status(
       et::launch_draft_step(p, et::draft_ws(p, ws), step, root_tokens, logits,
                             batch_stride, row_stride, vec, fixed ? &ff : nullptr,
-                            next_tokens, next_count, (hipStream_t)stream),
+                            next_tokens, next_count, (hipStream_t)stream, last),
       fn);
   if (rc == ET_OK && p.debug)
     rc = debug_frontier(p, fn, next_tokens, next_count, (hipStream_t)stream);
+  if (rc == ET_OK && p.debug && last)
+    rc = debug_tree(p, fn, last->tokens, last->parent_slot, last->n_kept, (hipStream_t)stream);
   if (rc == ET_OK) {
     p.last_ws = ws;
     p.last_step = step;
@@ -462,6 +465,49 @@ int et_draft_step(et_plan_t plan, void* ws, int32_t step,
   return draft_step("et_draft_step", plan, ws, step, root_tokens, logits,
                     batch_stride, row_stride, next_tokens, next_count, stream,
                     false);
+}
+
+int et_draft_step_last(et_plan_t plan, void* ws, const int32_t* root_tokens,
+                       const void* logits, int64_t batch_stride, int64_t row_stride,
+                       int32_t* next_tokens, int32_t* next_count,
+                       const int32_t* prefix_len, int32_t* tokens, int32_t* parent_slot,
+                       float* conf, float* value, int32_t* n_kept, uint64_t* mask,
+                       int32_t* depth, int32_t* pos_ids, et_stream_t stream) {
+  const char* fn = "et_draft_step_last";
+  CHECK_PTR(plan);
+  CHECK_PTR(prefix_len);
+  CHECK_PTR(tokens);
+  CHECK_PTR(parent_slot);
+  CHECK_PTR(conf);
+  CHECK_PTR(value);
+  CHECK_PTR(n_kept);
+  CHECK_PTR(mask);
+  CHECK_PTR(depth);
+  CHECK_PTR(pos_ids);
+  et::Plan& p = *as_plan(plan);
+  // the merge block (64 k threads) holds at most kRerankPer pool nodes per
+  // thread; every valid configuration fits (capacity <= 1 + k + 14 k^2)
+  if (p.cap > 4 * 64 * p.k)
+    return fail(ET_EUNSUPPORTED, "%s: pool capacity %d above %d", fn, p.cap, 4 * 64 * p.k);
+  if (p.debug) {
+    const int rc = debug_prefix(p, fn, prefix_len, (hipStream_t)stream);
+    if (rc != ET_OK) return rc;
+  }
+  et::RerankOut o;
+  o.tokens = tokens;
+  o.parent_slot = parent_slot;
+  o.conf = conf;
+  o.value = value;
+  o.n_kept = n_kept;
+  o.prefix_len = prefix_len;
+  o.mask = mask;
+  o.depth = depth;
+  o.pos = pos_ids;
+  o.N = p.N;
+  o.T = p.T;
+  o.W = p.W;
+  return draft_step(fn, plan, ws, p.D, root_tokens, logits, batch_stride, row_stride,
+                    next_tokens, next_count, stream, false, &o);
 }
 
 int et_draft_step_static(et_plan_t plan, void* ws, int32_t step,

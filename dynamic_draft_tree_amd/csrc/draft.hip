@@ -22,6 +22,7 @@
 
 #include "device.h"
 #include "internal.h"
+#include "rerank.h"
 
 namespace et {
 
@@ -358,8 +359,19 @@ __device__ __forceinline__ void empty_frontier(const DraftArgs& a, int b) {
 // across the whole block.
 // FIXED: the next frontier comes from a fixed shape (fx) instead of the
 // children's values.
-template <bool BF16, int KST, bool FIXED>
-__device__ __forceinline__ void merge_rows(const DraftArgs& a, const FixedFrontier* fx, int b) {
+// What the last step's merge leaves for the rerank in the same block: the
+// pool size before the step, the children appended, and the children's
+// pool keys, parent pool indexes and conf in LDS (child c at index c).
+struct LastChildren {
+  int P0, n_new;
+  const uint64_t* key;
+  const int* par;
+  const float* conf;
+};
+
+template <bool BF16, int KST, bool FIXED, bool LAST = false>
+__device__ __forceinline__ void merge_rows(const DraftArgs& a, const FixedFrontier* fx, int b,
+                                           LastChildren* lc = nullptr) {
   constexpr float kLog2e = 1.4426950408889634f;
   const int tid = threadIdx.x, lane = tid & 63, jr = tid >> 6;  // jr: this wave's row
   const int k = a.k, S = a.parts;  // partial lists per row (<= 64)
@@ -368,6 +380,8 @@ __device__ __forceinline__ void merge_rows(const DraftArgs& a, const FixedFronti
   __shared__ uint64_t s_rk[kMaxTopk * kMaxTopk];  // row top-k keys
   // children's pool keys; the padding covers count_greater's last reads
   __shared__ __attribute__((aligned(16))) uint64_t s_aux[kMaxTopk * kMaxTopk + 32];
+  __shared__ int s_cpar[LAST ? kMaxTopk * kMaxTopk : 1];    // children's parents (LAST)
+  __shared__ float s_cconf[LAST ? kMaxTopk * kMaxTopk : 1];  // and conf (LAST)
   __shared__ int s_nf;
   // Every load is issued before the frontier count F arrives: rows j < k
   // of the workspace are always readable, rows j >= F are dropped.
@@ -384,6 +398,7 @@ __device__ __forceinline__ void merge_rows(const DraftArgs& a, const FixedFronti
     pk[r] = a.ws.part_keys[(rowid * kMaxTopk + min(r, k - 1)) * S + li];
   const int P0 = a.step == 1 ? 0 : a.ws.pool_count[b];
   const int F = a.step == 1 ? 1 : a.ws.frontier_count[prev * a.B + b];
+  if constexpr (LAST) *lc = LastChildren{P0, 0, s_aux, s_cpar, s_cconf};
   if (F == 0) {
     empty_frontier(a, b);
     return;
@@ -488,8 +503,13 @@ __device__ __forceinline__ void merge_rows(const DraftArgs& a, const FixedFronti
     const int ci = jr * k + crank;
     c_pi = P0 + ci;
     s_aux[ci] = pool_key(c_val, a.step, c_tok, c_pi);
+    if constexpr (LAST) {
+      s_cpar[ci] = par;
+      s_cconf[ci] = c_conf;
+    }
   }
   const int n_new = F * k;  // <= k * k: four threads per child fit the k waves
+  if constexpr (LAST) lc->n_new = n_new;
   lds_barrier();
   // phase: children appended
   const int fb = (cur * a.B + b) * k;
@@ -598,6 +618,62 @@ __global__ __launch_bounds__(1024) void draft_merge_fixed_kernel(DraftArgs a, Fi
   merge_rows<BF16, KST, true>(a, &fx, blockIdx.x);
 }
 
+// Merge of the last step, then the rerank and flatten of the finished tree
+// by the same block (one launch fewer per cycle than et_rerank_mask after
+// the step).  The pool nodes of the earlier steps are loaded first, with
+// the merge's own loads (clamped to the readable capacity, dropped past
+// the pool size once it is known); the step's children come from LDS.
+template <bool BF16, int KST>
+__global__ __launch_bounds__(1024) void draft_merge_last_kernel(DraftArgs a, RerankOut o) {
+  const int b = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+  __shared__ RerankLds L;
+  const int64_t pb = (int64_t)b * a.cap;
+  const int rounds = (a.cap + nt - 1) / nt;  // <= kRerankPer (checked by the host)
+  int par[kRerankPer], dep[kRerankPer], tok[kRerankPer];
+  float cnf[kRerankPer], val[kRerankPer];
+#pragma unroll
+  for (int i = 0; i < kRerankPer; ++i) {
+    val[i] = cnf[i] = 0.f;
+    par[i] = dep[i] = tok[i] = -1;
+    if (i < rounds) {  // uniform
+      const int64_t g = pb + min(tid + nt * i, a.cap - 1);
+      val[i] = a.ws.pool_value[g];
+      dep[i] = a.ws.pool_depth[g];
+      tok[i] = a.ws.pool_token[g];
+      par[i] = a.ws.pool_parent[g];
+      cnf[i] = a.ws.pool_conf[g];
+    }
+  }
+  const int pre = o.prefix_len[b];
+  // (step 1 is also the last when D = 1: the root token is then the
+  // input's, the workspace copy being written by this same launch)
+  const int root = a.step == 1 ? a.root_tokens[b] : a.ws.root_token[b];
+  LastChildren lc;
+  merge_rows<BF16, KST, false, true>(a, nullptr, b, &lc);
+  // the pool values become opaque only here, so that nothing computed
+  // from them is scheduled before the merge (each such use a wait for the
+  // memory round trip ahead of the merge's own loads)
+#pragma unroll
+  for (int i = 0; i < kRerankPer; ++i)
+    asm volatile("" : "+v"(val[i]), "+v"(dep[i]), "+v"(tok[i]), "+v"(par[i]), "+v"(cnf[i]));
+  uint64_t key[kRerankPer];
+#pragma unroll
+  for (int i = 0; i < kRerankPer; ++i) {
+    const int idx = tid + nt * i;
+    key[i] = 0;
+    if (idx < lc.P0) {
+      key[i] = pool_key(val[i], dep[i], tok[i], idx);
+    } else if (idx < lc.P0 + lc.n_new) {
+      const int c = idx - lc.P0;
+      key[i] = lc.key[c];
+      par[i] = lc.par[c];
+      cnf[i] = lc.conf[c];
+    }
+  }
+  const int P = lc.P0 + lc.n_new;
+  rerank_block<true>(o, L, b, nt, key, par, cnf, P < o.N ? P : o.N, root, pre);
+}
+
 // Keys staged per list: four when a row has many lists (its top k then
 // almost always lie within the first four of each), eight with few.
 constexpr int merge_stage(int parts) { return parts > 16 ? 4 : 8; }
@@ -631,7 +707,7 @@ hipError_t launch_draft_step(const Plan& p, const DraftWs& w, int step,
                              const int32_t* root_tokens, const void* logits,
                              int64_t bstride, int64_t rstride, bool vec,
                              const FixedFrontier* fixed, int32_t* next_tokens,
-                             int32_t* next_count, hipStream_t s) {
+                             int32_t* next_count, hipStream_t s, const RerankOut* last) {
   DraftArgs a;
   a.ws = w;
   a.logits = logits;
@@ -672,6 +748,7 @@ hipError_t launch_draft_step(const Plan& p, const DraftWs& w, int step,
 #define ET_MERGE(BF, K)                                                                  \
   do {                                                                                   \
     if (fixed) draft_merge_fixed_kernel<BF, K><<<p.B, 64 * p.k, 0, s>>>(a, *fixed);      \
+    else if (last) draft_merge_last_kernel<BF, K><<<p.B, 64 * p.k, 0, s>>>(a, *last);    \
     else draft_merge_kernel<BF, K><<<p.B, 64 * p.k, 0, s>>>(a);                          \
   } while (0)
   const int kst = merge_stage(a.parts);

@@ -153,11 +153,29 @@ AcceptWs accept_ws(const Plan& p, void* ws);
 AttnWs attn_ws(const Plan& p, void* ws);
 
 // Launchers (return hipError_t of the launch).
+// Where a rerank writes: the et_rerank outputs, and with the flatten the
+// et_tree_mask outputs too.
+struct RerankOut {
+  int32_t* tokens;
+  int32_t* parent_slot;
+  float* conf;
+  float* value;
+  int32_t* n_kept;
+  const int32_t* prefix_len;
+  uint64_t* mask;
+  int32_t* depth;
+  int32_t* pos;
+  int N, T, W;
+};
+
+// last: the step is the last one and its merge also reranks and flattens
+// the tree into these outputs (et_draft_step_last); else null.
 hipError_t launch_draft_step(const Plan& p, const DraftWs& w, int step,
                              const int32_t* root_tokens, const void* logits,
                              int64_t bstride, int64_t rstride, bool vec,
                              const FixedFrontier* fixed, int32_t* next_tokens,
-                             int32_t* next_count, hipStream_t s);
+                             int32_t* next_count, hipStream_t s,
+                             const RerankOut* last = nullptr);
 // The draft step's merge alone, over `parts` partial lists per row already
 // in the workspace (fp32 logit keys).
 hipError_t launch_draft_merge(const Plan& p, const DraftWs& w, int step,

@@ -24,6 +24,9 @@
  *     et_accept                      -- greedy longest accepted path
  *       (or et_accept_sample           -- ratio tests at temperature > 0)
  *     et_kv_commit                   -- append the accepted path's K/V
+ * Fused forms with the same outputs: et_rerank_mask (rerank and mask in
+ * one launch) and et_draft_step_last (the last draft step, whose merge
+ * also reranks and flattens the tree).
  * A fixed-shape baseline replaces the first two with et_draft_step_static
  * x D and et_static_tree (after et_set_static_shape).
  * Between draft steps the caller runs its draft model on `next_tokens`
@@ -199,6 +202,24 @@ int et_rerank_mask(et_plan_t plan, void* ws, int32_t* tokens, int32_t* parent_sl
                    float* conf, float* value, int32_t* n_kept,
                    const int32_t* prefix_len, uint64_t* mask, int32_t* depth,
                    int32_t* pos_ids, et_stream_t stream);
+
+/* The last draft step, reranked and flattened in its own launches ([P1]
+ * s4.1 then s4.2): et_draft_step(D) (same arguments, same pool and
+ * frontier outputs: the frontier of the last step is empty) whose merge
+ * then writes every output of et_rerank_mask for the finished tree, with
+ * the same values.  One launch fewer per cycle than et_draft_step(D)
+ * followed by et_rerank_mask: the rerank runs in the merge's block, on the
+ * step's children still in on-chip memory and the earlier nodes loaded
+ * with the merge's inputs.  Requirements and errors are those of
+ * et_draft_step at step D and of et_rerank_mask; ET_EUNSUPPORTED if the
+ * pool capacity exceeds 256 nodes per draft row (no valid configuration
+ * does). */
+int et_draft_step_last(et_plan_t plan, void* ws, const int32_t* root_tokens,
+                       const void* logits, int64_t batch_stride, int64_t row_stride,
+                       int32_t* next_tokens, int32_t* next_count,
+                       const int32_t* prefix_len, int32_t* tokens, int32_t* parent_slot,
+                       float* conf, float* value, int32_t* n_kept, uint64_t* mask,
+                       int32_t* depth, int32_t* pos_ids, et_stream_t stream);
 
 /* Tree attention, the verify pass ([P1] s4.2; [P2]: the tree is checked
  * in one tree-attention pass; [P3]: Medusa-style tree attention).

@@ -258,6 +258,35 @@ def _check_rerank_mask(r):
         if a.dtype == torch.float32:
             a, b = a.view(torch.int32), b.view(torch.int32)
         assert torch.equal(a, b), f"et_rerank_mask {f} differs from the pair of calls"
+    # the last draft step with the rerank and flatten in its merge, after a
+    # rerun of steps 1..D-1: the same pool, frontier and tree, bit for bit
+    dev = r["dev"]
+    pool = plan.export_pool()
+    nxt = (plan.next_tokens.clone(), plan.next_count.clone())
+    for step in range(1, w.depth):
+        plan.draft_step(step, dev["root_tokens"], dev["draft"][:, step - 1])
+    for f in fields:
+        getattr(plan, f).fill_(-7)
+    plan.next_tokens.fill_(-7)
+    plan.next_count.fill_(-7)
+    plan.draft_step_last(dev["root_tokens"], dev["draft"][:, w.depth - 1],
+                         dev["prefix_len"])
+    torch.cuda.synchronize()
+    pool2 = plan.export_pool()
+    for f in pool:
+        a, b = pool2[f], pool[f]
+        if a.dtype == torch.float32:
+            a, b = a.view(torch.int32), b.view(torch.int32)
+        if f in ("token", "parent", "depth", "conf", "value"):  # the used part
+            n = int(pool["pool_count"].max())
+            a, b = a[:, :n], b[:, :n]
+        assert torch.equal(a, b), f"et_draft_step_last pool {f} differs"
+    assert torch.equal(plan.next_tokens, nxt[0]) and torch.equal(plan.next_count, nxt[1])
+    for f in fields:
+        a, b = getattr(plan, f), pair[f]
+        if a.dtype == torch.float32:
+            a, b = a.view(torch.int32), b.view(torch.int32)
+        assert torch.equal(a, b), f"et_draft_step_last {f} differs from the separate calls"
 
 
 # Attention outputs compared in full against the oracle (OpenMP over
