@@ -99,6 +99,21 @@ def test_calls_validate_before_launch():
                            nul) == binding.ET_ESTATE
     assert L.et_rerank(h, fake, fake, fake, fake, fake, fake,
                        nul) == binding.ET_ESTATE
+    # rerank and mask in one launch: the tree must be complete; every
+    # output pointer is checked
+    assert L.et_rerank_mask(h, fake, fake, fake, fake, fake, fake, fake, fake,
+                            fake, fake, nul) == binding.ET_ESTATE
+    assert L.et_rerank_mask(h, fake, fake, fake, fake, fake, fake, nul, fake,
+                            fake, fake, nul) == binding.ET_EINVAL
+    assert b"prefix_len" in L.et_last_error()
+    # the last step (D = 3 for tiny) must follow step D - 1
+    last = [h, fake, fake, fake, 1024, 1024, fake, fake, fake, fake, fake, fake,
+            fake, fake, fake, fake, fake, nul]
+    assert L.et_draft_step_last(*last) == binding.ET_ESTATE
+    for i in (8, 13, 16):  # prefix_len, n_kept, pos_ids
+        args = list(last)
+        args[i] = nul
+        assert L.et_draft_step_last(*args) == binding.ET_EINVAL, i
     assert L.et_draft_step(h, ctypes.c_void_p((1 << 20) + 8), 1, fake, fake,
                            1024, 1024, fake, fake, nul) == binding.ET_EINVAL
     assert L.et_tree_attention(h, fake, fake, fake, fake, fake, fake, fake,
