@@ -135,15 +135,22 @@ def summarize_pmc(args):
     print(json.dumps(out))
 
 
-def trace_durations_us(db):
-    """Mean duration (us) per kernel name in a rocprofv3 kernel-trace
-    database (rocpd SQLite, table kernels)."""
-    import sqlite3
-    con = sqlite3.connect(db)
+def trace_durations_us(path):
+    """Mean duration (us) per kernel name in a rocprofv3 kernel trace: its
+    rocpd SQLite database (table kernels) or its kernel_trace.csv (-f csv)."""
     out = {}
-    for name, dur in con.execute("select name, duration from kernels"):
-        out.setdefault(name, []).append(float(dur))
-    con.close()
+    if path.endswith(".csv"):
+        import csv
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                out.setdefault(r["Kernel_Name"], []).append(
+                    float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+    else:
+        import sqlite3
+        con = sqlite3.connect(path)
+        for name, dur in con.execute("select name, duration from kernels"):
+            out.setdefault(name, []).append(float(dur))
+        con.close()
     return {k: float(np.mean(v)) / 1e3 for k, v in out.items()}
 
 

@@ -21,6 +21,25 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+PROBES = os.path.join(HERE, "probes")
+
+
+def build_probes(verbose: bool = False) -> list:
+    """Measurement programs (probes/*.hip, one executable each beside its
+    source): not part of the library."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
+    out = []
+    for src in sorted(glob.glob(os.path.join(PROBES, "*.hip"))):
+        exe = src[:-len(".hip")]
+        cmd = [hipcc, *flags, src, "-o", exe]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True, capture_output=not verbose)
+        out.append(exe)
+    return out
+
+
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"
@@ -42,3 +61,4 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_probes(verbose=True))
