@@ -928,9 +928,25 @@ def test_tree_stops_when_all_below_threshold():
         assert int(plan.next_count[0]) == 0
     ex = plan.export_pool()
     assert int(ex["pool_count"][0]) == w.topk
-    plan.rerank()
+    plan.rerank_mask(dev["prefix_len"])
     torch.cuda.synchronize()
     assert int(plan.n_kept[0]) == w.topk
+    fields = ("tokens", "parent_slot", "conf", "value", "n_kept", "mask", "depth",
+              "pos_ids")
+    want = {f: getattr(plan, f).clone() for f in fields}
+    # the last step's merge with an empty frontier still reranks the pool
+    for step in range(1, w.depth):
+        plan.draft_step(step, dev["root_tokens"], dev["draft"][:, step - 1])
+    for f in fields:
+        getattr(plan, f).fill_(-7)
+    plan.draft_step_last(dev["root_tokens"], dev["draft"][:, w.depth - 1], dev["prefix_len"])
+    torch.cuda.synchronize()
+    assert int(plan.next_count[0]) == 0
+    for f in fields:
+        a, b = getattr(plan, f), want[f]
+        if a.dtype == torch.float32:
+            a, b = a.view(torch.int32), b.view(torch.int32)
+        assert torch.equal(a, b), f
 
 
 def test_attention_empty_prefix():
