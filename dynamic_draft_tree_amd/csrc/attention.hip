@@ -275,16 +275,24 @@ void tree_attn_bf16_kernel(AttnArgs a) {
     const uint16_t* Kg_ = tr_ ? ktb : kcb;                                    \
     const uint16_t* Vg_ = tr_ ? vtb : vcb;                                    \
     _Pragma("unroll") for (int c_ = 0; c_ < CH; ++c_) {                       \
-      const int slab = c_ * 8 + wave;                                         \
-      const int q = slab * 64 + lane;                                         \
-      const int row = q / CPR, phys = q % CPR;                                \
-      const int64_t go = (int64_t)min(k0_ + row, klast_) * HD +               \
-                         ((phys ^ (row & (CPR - 1))) * 8);                    \
+      const int slab = c_ * 8 + wave_u;                                       \
+      const int64_t go = (int64_t)min(k0_ + trow[c_], klast_) * HD + tcol[c_]; \
       load_lds16(Kg_ + go, &sKV[(BUF_)][0][slab * 512]);                      \
       load_lds16(Vg_ + go, &sKV[(BUF_)][1][slab * 512]);                      \
     }                                                                         \
   } while (0)
 
+  // Per lane and slab, the tile row it loads and its swizzled column,
+  // computed once (the wave index made uniform, so each slab's LDS address
+  // is scalar arithmetic).
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  int trow[CH], tcol[CH];
+#pragma unroll
+  for (int c_ = 0; c_ < CH; ++c_) {
+    const int q = (c_ * 8 + wave_u) * 64 + lane;
+    trow[c_] = q / CPR;
+    tcol[c_] = ((q % CPR) ^ (trow[c_] & (CPR - 1))) * 8;
+  }
   if (cnt > 0) ET_ISSUE_TILE(t_begin, 0);
   if (PD > 1 && cnt > 1) ET_ISSUE_TILE(t_begin + 1, 1);
   // Q, the mask word and tile 0 have landed; tile 1 may still be in flight
