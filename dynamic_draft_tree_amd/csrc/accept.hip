@@ -94,35 +94,70 @@ __global__ __launch_bounds__(256) void accept_scan_kernel(AcceptArgs a) {
 
 // Walk: rows are reduced by segments of SP lanes (SP = the power of two
 // >= the row's key count, at most 64; a lane takes every SP-th key), 16
-// waves at a time, into LDS; then wave 0 walks.
+// waves at a time, into LDS; then wave 0 walks.  NR (a power of two) is
+// at least the number of such rounds that cover the T rows.
 constexpr int kWalkWaves = 16;
+template <int NR>
 __global__ __launch_bounds__(kWalkWaves * 64) void accept_walk_kernel(AcceptArgs a) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ int s_am[kMaxBudget + 1];
-  const int n = a.n_kept[b];
   const int P = a.S * kAccWaves;  // keys per row
   int SP = 1;
   while (SP < P && SP < 64) SP <<= 1;
   const int RW = 64 / SP;  // rows per wave
   const int seg = lane / SP, q = lane - seg * SP;
-  for (int r0 = 0; r0 <= n; r0 += kWalkWaves * RW) {
-    const int s = r0 + wave * RW + seg;
-    uint64_t m = 0;
-    if (s <= n) {
-      const uint64_t* pk = a.ws.part + ((int64_t)b * a.T + s) * P;
-      for (int i = q; i < P; i += SP) {
-        const uint64_t v = pk[i];
-        m = v > m ? v : m;
-      }
+  // Nothing waits for n_kept before it is needed: every slot row below T
+  // is reduced (its partials and the tree's token and parent arrays are
+  // readable for all T slots; rows past n_kept are never used), and wave
+  // 0 loads the tree before the barrier.
+  const int32_t* tk = a.tokens + (int64_t)b * a.T;
+  const int32_t* ps = a.parent_slot + (int64_t)b * a.T;
+  int r_tok[4], r_par[4];
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = min(lane + 64 * i, a.T - 1);
+      r_tok[i] = tk[s];
+      r_par[i] = ps[s];
     }
+  }
+  const int n_kept = a.n_kept[b];
+  // Every partial key of every round is loaded before the first is used,
+  // with no branch between the loads (rows are clamped to T - 1, keys to
+  // P - 1, and the surplus zeroed after): a lane holds keys q and q + SP
+  // of its row (P <= 128 at the largest vocabulary).
+  constexpr int kKeys = 2;
+  static_assert(kMaxVocab / accept_chunk_elems(ET_F32) * kAccWaves <= kKeys * 64,
+                "a row's keys exceed two per lane");
+  const int per_round = kWalkWaves * RW;
+  const uint64_t* pb = a.ws.part + (int64_t)b * a.T * P;
+  const int i0 = min(q, P - 1), i1 = min(q + SP, P - 1);
+  uint64_t v[NR][kKeys];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int o = min(r * per_round + wave * RW + seg, a.T - 1) * P;
+    v[r][0] = pb[o + i0];
+    v[r][1] = pb[o + i1];
+  }
+  // keeps each load where it is (not sunk into the code that uses it)
+#pragma unroll
+  for (int r = 0; r < NR; ++r) asm volatile("" : "+v"(v[r][0]), "+v"(v[r][1]));
+  int n = n_kept;
+  asm volatile("" : "+s"(n));  // n_kept read beside the keys, not after the barrier
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int s = r * per_round + wave * RW + seg;
+    const uint64_t v0 = s < a.T && q < P ? v[r][0] : 0;
+    const uint64_t v1 = s < a.T && q + SP < P ? v[r][1] : 0;
+    uint64_t m = v0 > v1 ? v0 : v1;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1)
       if (d < SP) {
         const uint64_t o = xor_lane_rt(m, d);
         m = o > m ? o : m;
       }
-    if (q == 0 && s <= n) s_am[s] = (int)id_of(m);
+    if (q == 0 && s < a.T) s_am[s] = (int)id_of(m);
   }
   __syncthreads();
   // phase: rows merged
@@ -131,15 +166,11 @@ __global__ __launch_bounds__(kWalkWaves * 64) void accept_walk_kernel(AcceptArgs
   // Greedy walk from the root (one wave).  Lane l holds slots l, l+64, ...
   // (T <= 256); siblings carry distinct tokens, so at most one child of the
   // current slot matches.
-  const int32_t* tk = a.tokens + (int64_t)b * a.T;
-  const int32_t* ps = a.parent_slot + (int64_t)b * a.T;
-  int r_tok[4], r_par[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int s = lane + 64 * i;
-    const bool ok = s <= n;
-    r_tok[i] = ok ? tk[s] : -1;
-    r_par[i] = ok ? ps[s] : -2;
+    const bool ok = lane + 64 * i <= n;
+    r_tok[i] = ok ? r_tok[i] : -1;
+    r_par[i] = ok ? r_par[i] : -2;
   }
   int32_t* path = a.path_slots + (int64_t)b * (a.D + 1);
   int32_t* outt = a.out_tokens + (int64_t)b * (a.D + 1);
@@ -203,7 +234,16 @@ hipError_t launch_accept(const Plan& p, const AcceptWs& w, const void* target,
   else if (bf) accept_scan_kernel<true, false, kAccElemsBf16><<<grid, kScanThreads, 0, s>>>(a);
   else if (vec) accept_scan_kernel<false, true, kAccElemsF32><<<grid, kScanThreads, 0, s>>>(a);
   else accept_scan_kernel<false, false, kAccElemsF32><<<grid, kScanThreads, 0, s>>>(a);
-  accept_walk_kernel<<<p.B, kWalkWaves * 64, 0, s>>>(a);
+  // rounds of the row reduction, as the walk kernel counts them
+  const int P = p.s_accept * kAccWaves;
+  int SP = 1;
+  while (SP < P && SP < 64) SP <<= 1;
+  const int rounds = (p.T + kWalkWaves * (64 / SP) - 1) / (kWalkWaves * (64 / SP));
+  if (rounds <= 1) accept_walk_kernel<1><<<p.B, kWalkWaves * 64, 0, s>>>(a);
+  else if (rounds <= 2) accept_walk_kernel<2><<<p.B, kWalkWaves * 64, 0, s>>>(a);
+  else if (rounds <= 4) accept_walk_kernel<4><<<p.B, kWalkWaves * 64, 0, s>>>(a);
+  else if (rounds <= 8) accept_walk_kernel<8><<<p.B, kWalkWaves * 64, 0, s>>>(a);
+  else accept_walk_kernel<(kMaxBudget + 1) / kWalkWaves><<<p.B, kWalkWaves * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
