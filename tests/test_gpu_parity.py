@@ -98,6 +98,19 @@ VARIANTS = {
                           threshold=0.0, sharpness=(2.0, 1.0), n_q_heads=4,
                           n_kv_heads=2, head_dim=128, prefix_cap=100,
                           prefix_range=(0, 100), seed=11),
+    # the accept walk's row reduction: 100 partial keys per slot row (two
+    # per lane) over 201 slots, sixteen rounds of 16 rows
+    "accept_rows_f32": TINY.with_(batch=1, vocab=200000, topk=8, depth=4,
+                                  budget_n=200, threshold=0.0, sharpness=(1.5,),
+                                  n_q_heads=2, n_kv_heads=1, head_dim=64,
+                                  prefix_cap=64, prefix_range=(1, 64), seed=18),
+    # 40 keys per slot row over 121 slots: eight rounds
+    "accept_rows_bf16": TINY.with_(batch=1, vocab=150000, topk=6, depth=5,
+                                   budget_n=120, threshold=0.0,
+                                   logits_dtype="bf16", sharpness=(2.0,),
+                                   n_q_heads=2, n_kv_heads=1, head_dim=64,
+                                   prefix_cap=64, prefix_range=(1, 64),
+                                   qkv_dtype="bf16", seed=19),
 }
 FULL = ["vicuna7b_flat", "vicuna7b_sharp", "llama8b", "llama8b_b64",
         "llama70b_b8"]
