@@ -674,9 +674,13 @@ __global__ __launch_bounds__(1024) void draft_merge_last_kernel(DraftArgs a, Rer
   rerank_block<true>(o, L, b, nt, key, par, cnf, P < o.N ? P : o.N, root, pre);
 }
 
-// Keys staged per list: four when a row has many lists (its top k then
-// almost always lie within the first four of each), eight with few.
-constexpr int merge_stage(int parts) { return parts > 16 ? 4 : 8; }
+// Keys staged per list: four when a row has 64 lists (its top k then
+// almost always lie within the first four of each), eight with up to 32.
+// A launch lasts as long as its slowest block, so a few rows on the exact
+// path set the step's time: at 64 sequences of 128256 bf16 ids (32 lists
+// per row, half the rows from flat softmaxes) about 1% of the rows needed
+// more than four keys of some list, and with eight none did.
+constexpr int merge_stage(int parts) { return parts > 32 ? 4 : 8; }
 
 hipError_t launch_draft_merge(const Plan& p, const DraftWs& w, int step,
                               const int32_t* root_tokens, int parts,
