@@ -45,7 +45,7 @@ enum {
   R_POOL_TOKEN, R_POOL_PARENT, R_POOL_DEPTH, R_POOL_CONF, R_POOL_VALUE,
   R_POOL_COUNT, R_ROOT, R_FRONTIER, R_FRONTIER_VAL, R_FRONTIER_COUNT, R_PART_M, R_PART_S,
   R_PART_KEYS, R_LM_M, R_LM_S, R_LM_KEYS, R_ACC_PART,
-  R_ATT_O, R_ATT_M, R_ATT_L, R_COUNT
+  R_ATT_O, R_ATT_M, R_ATT_L, R_ATT_ORDER, R_COUNT
 };
 
 void layout(et::Plan& p) {
@@ -72,6 +72,7 @@ void layout(et::Plan& p) {
   sz[R_ACC_PART] = B * T * p.s_accept * W4 * 16;
   sz[R_ATT_O] = att_rows * p.HD * 4;
   sz[R_ATT_M] = sz[R_ATT_L] = att_rows * 4;
+  sz[R_ATT_ORDER] = B * 4;
   size_t off = 0;
   for (int r = 0; r < R_COUNT; ++r) {
     p.off[r] = off;
@@ -247,6 +248,7 @@ AttnWs attn_ws(const Plan& p, void* ws) {
   w.o = at<float>(ws, p, R_ATT_O);
   w.m = at<float>(ws, p, R_ATT_M);
   w.l = at<float>(ws, p, R_ATT_L);
+  w.order = at<int32_t>(ws, p, R_ATT_ORDER);
   return w;
 }
 

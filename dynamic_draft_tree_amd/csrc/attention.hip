@@ -49,6 +49,7 @@ struct AttnArgs {
   const int32_t* prefix_len;
   const uint64_t* mask;
   const int32_t* n_kept;
+  const int32_t* order;  // sequence of unit-sequence b0, or null (b = b0)
   void* out;
   float* po;
   float* pm;
@@ -180,7 +181,8 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   int unit, rem;
   if (!attn_block_coords(blockIdx.x, a.B * a.Hkv, a.nqb * a.S, &unit, &rem)) return;
   const int qb = rem / a.S, split = rem - qb * a.S;
-  const int b = unit / a.Hkv, kvh = unit - b * a.Hkv;
+  const int b0 = unit / a.Hkv, kvh = unit - b0 * a.Hkv;
+  const int b = a.order ? a.order[b0] : b0;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int rg = wave & 3, kh = wave >> 2;  // row group, key half of a tile
   const int r16 = lane & 15, g = lane >> 4;
@@ -511,6 +513,28 @@ void tree_attn_bf16_kernel(AttnArgs a) {
 
 #undef ET_ISSUE_TILE
 
+// The batch's sequences ranked by descending prefix length (ties by
+// index): order[r] is the sequence of rank r.  The attention grid then
+// walks the longest sequences first, so that when a launch has more blocks
+// than the chip holds at once the last blocks to start are short ones
+// (longest-processing-time-first list scheduling).  One block; B is at
+// most kAttnOrderMaxB.
+__global__ __launch_bounds__(1024) void attn_order_kernel(const int32_t* prefix_len, int B,
+                                                          int32_t* order) {
+  __shared__ int s_len[kAttnOrderMaxB];
+  for (int i = threadIdx.x; i < B; i += blockDim.x) s_len[i] = prefix_len[i];
+  __syncthreads();
+  for (int t = threadIdx.x; t < B; t += blockDim.x) {
+    const int mine = s_len[t];
+    int r = 0;
+    for (int q = 0; q < B; ++q) {
+      const int o = s_len[q];
+      r += (o > mine || (o == mine && q < t)) ? 1 : 0;
+    }
+    order[r] = t;
+  }
+}
+
 // Combine the S split partials: o = sum_i O_i 2^(m_i - m) / l.  A block
 // covers RPB rows of one (unit, row block); thread = (row, 4 columns).
 // Blocks map to XCDs like the main kernel, so the partials are read from
@@ -670,6 +694,7 @@ hipError_t launch_tree_attention(const Plan& p, const AttnWs& w,
   a.prefix_len = prefix_len;
   a.mask = mask;
   a.n_kept = n_kept;
+  a.order = nullptr;
   a.out = out;
   a.po = w.o;
   a.pm = w.m;
@@ -691,6 +716,18 @@ hipError_t launch_tree_attention(const Plan& p, const AttnWs& w,
   }
   const int units8 = (p.B * p.Hkv + 7) / 8 * 8;  // whole units per XCD
   const int blocks = units8 * p.attn_nqb * p.attn_splits;
+  // More blocks than the chip holds at once (two per compute unit with two
+  // tile buffers, one with three) and ragged prefixes: dispatch the
+  // longest sequences first.  (Only without key splits: the split merge
+  // maps units to sequences directly.)
+  const int resident = 256 * (ET_ATTN_NB(p.attn_wr) == 2 ? 2 : 1);
+  if (p.B > 1 && p.B <= kAttnOrderMaxB && p.attn_splits == 1 && blocks > resident) {
+    const int nt = p.B < 1024 ? (p.B + 63) / 64 * 64 : 1024;
+    attn_order_kernel<<<1, nt, 0, s>>>(prefix_len, p.B, w.order);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.order = w.order;
+  }
 #define ET_ATTN(HD, WR)                                                          \
   do {                                                                           \
     tree_attn_bf16_kernel<HD, WR, ET_ATTN_NB(WR)><<<blocks, 512, 0, s>>>(a);     \

@@ -61,6 +61,9 @@ constexpr int kScanTargetBlocks = ET_SCAN_TARGET_BLOCKS;
 constexpr int kScanWideBlocks = ET_SCAN_WIDE_BLOCKS;
 constexpr int kAttnTile = 64;            // keys per staged K/V tile
 constexpr int kAttnMaxSplits = 32;       // key splits per (kv head, row block)
+// Batches up to this size may have their attention blocks dispatched
+// longest sequence first (one block ranks the prefix lengths).
+constexpr int kAttnOrderMaxB = 1024;
 #ifndef ET_ATTN_TARGET_BLOCKS
 #define ET_ATTN_TARGET_BLOCKS 256
 #endif
@@ -105,6 +108,7 @@ struct AttnWs {
   float* o;               // [B*Hkv][nqb][S][rows per block][d]
   float* m;               // [B*Hkv][nqb][S][rows per block]
   float* l;
+  int32_t* order;         // [B] sequences by descending prefix length
 };
 
 struct Plan {
