@@ -50,7 +50,8 @@ CALLS = {
                         ["draft.hip", "rerank.h", "device.h", "internal.h"]),
     "accept": (["accept_scan_kernel", "accept_walk_kernel"],
                ["accept.hip", "device.h", "internal.h"]),
-    "tree_attention": (["tree_attn_bf16_kernel", "tree_attn_merge_kernel"],
+    "tree_attention": (["tree_attn_bf16_kernel", "tree_attn_merge_kernel",
+                        "tree_attn_order_kernel"],
                        ["attention.hip", "device.h", "internal.h"]),
 }
 

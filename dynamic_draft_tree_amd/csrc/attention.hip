@@ -519,7 +519,7 @@ void tree_attn_bf16_kernel(AttnArgs a) {
 // than the chip holds at once the last blocks to start are short ones
 // (longest-processing-time-first list scheduling).  One block; B is at
 // most kAttnOrderMaxB.
-__global__ __launch_bounds__(1024) void attn_order_kernel(const int32_t* prefix_len, int B,
+__global__ __launch_bounds__(1024) void tree_attn_order_kernel(const int32_t* prefix_len, int B,
                                                           int32_t* order) {
   __shared__ int s_len[kAttnOrderMaxB];
   for (int i = threadIdx.x; i < B; i += blockDim.x) s_len[i] = prefix_len[i];
@@ -723,7 +723,7 @@ hipError_t launch_tree_attention(const Plan& p, const AttnWs& w,
   const int resident = 256 * (ET_ATTN_NB(p.attn_wr) == 2 ? 2 : 1);
   if (p.B > 1 && p.B <= kAttnOrderMaxB && p.attn_splits == 1 && blocks > resident) {
     const int nt = p.B < 1024 ? (p.B + 63) / 64 * 64 : 1024;
-    attn_order_kernel<<<1, nt, 0, s>>>(prefix_len, p.B, w.order);
+    tree_attn_order_kernel<<<1, nt, 0, s>>>(prefix_len, p.B, w.order);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.order = w.order;
