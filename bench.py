@@ -653,7 +653,9 @@ def extra_workload(name, args, torch, d, gen, WORKLOADS, copy_gbs, spin_per_ms):
     w = WORKLOADS[name]
     b = Bench(w, 1, torch, d, gen)
     b.capture()
-    ms = b.timed(min(args.steps, 50), 5)
+    # (20 warm-up cycles: the extras follow the CPU leg, which leaves the
+    # GPU idle for seconds)
+    ms = b.timed(min(args.steps, 100), 20)
     avg_us, per_cycle_us, _ = b.per_call(10, spin_per_ms)
     alg = b.algorithmic()
     out = {"cycles_per_s": round(1e3 / ms, 2), "ms_per_cycle": round(ms, 5),
