@@ -14,7 +14,10 @@
 //   each) and the unit's key tiles (prefix tiles, then tree tiles) into S
 //   contiguous splits; one block per (unit, row block, split).  Block i
 //   runs on XCD i % 8, so the launch maps every block of a unit to one XCD
-//   and the unit's K/V and split partials stay in that XCD's L2.
+//   and the unit's K/V and split partials stay in that XCD's L2.  When the
+//   grid is larger than the chip holds at once, units are taken in order
+//   of their sequence's prefix length, longest first (a one-block kernel
+//   ranks the batch), so that the blocks left for the end are short.
 //   Scores are computed transposed, S^T = K . Q^T, which leaves each lane
 //   holding one query row (lane % 16) and 4 consecutive keys per 16-key
 //   sub-tile; that register layout is directly the B operand of
