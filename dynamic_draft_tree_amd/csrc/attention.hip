@@ -58,6 +58,7 @@ struct AttnArgs {
   float* pm;
   float* pl;
   int B, T, Hq, Hkv, G, Pcap, W, nqb, S;
+  int interleave;  // block qb holds row groups qb, qb + nqb, ... (WR = 1, S = 1)
   float scale, scale_log2;
 };
 
@@ -193,13 +194,22 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   const int R = (n + 1) * a.G;
   const int RT = a.T * a.G;
   const int row0 = qb * BR;
+  // The unit row of the block's row rr (rr < BR).  Interleaved (64-row
+  // blocks without key splits), block qb holds the 16-row groups qb,
+  // qb + nqb, ...: the kept rows then spread evenly over a unit's blocks,
+  // which walk its tiles at one pace and share them through the L2
+  // (contiguous, a last block with few kept rows ran ahead of the others).
+  const bool inter = a.interleave;
+  auto row_of = [&](int rr) {
+    return inter ? 16 * (qb + a.nqb * (rr >> 4)) + (rr & 15) : row0 + rr;
+  };
   uint16_t* out = (uint16_t*)a.out;
 
-  if (row0 >= R) {
+  if (row_of(0) >= R) {
     // rows of unkept slots: zero output (the merge does it when S > 1)
     if (a.S == 1) {
       for (int e = tid; e < BR * (HD / 4); e += 512) {
-        const int r = row0 + e / (HD / 4);
+        const int r = row_of(e / (HD / 4));
         if (r >= RT) break;
         const int slot = r / a.G, gg = r - slot * a.G;
         *(uint2*)(out + (((int64_t)b * a.T + slot) * a.Hq + kvh * a.G + gg) * HD +
@@ -223,13 +233,13 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   const int me = min(tid, 4 * BR - 1);  // mask word staged by this thread
   uint64_t mword;
   {
-    const int rc = min(row0 + me % BR, R - 1);
+    const int rc = min(row_of(me % BR), R - 1);
     mword = a.mask[((int64_t)b * a.T + rc / a.G) * a.W + min(me / BR, a.W - 1)];
   }
   bf16x8_t qf[WR][KSTEPS];
 #pragma unroll
   for (int w = 0; w < WR; ++w) {
-    const int rc = min(row0 + rg * 16 * WR + w * 16 + r16, R - 1);
+    const int rc = min(row_of(rg * 16 * WR + w * 16 + r16), R - 1);
     const int slot = rc / a.G, gg = rc - slot * a.G;
     const uint16_t* qr = (const uint16_t*)a.q +
                          (((int64_t)b * a.T + slot) * a.Hq + kvh * a.G + gg) * HD;
@@ -305,16 +315,16 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   if (tid < 4 * BR) {
     const int rr = me % BR, q = me / BR;
-    sMask[q][rr] = (row0 + rr < R && q < a.W) ? mword : 0ull;
+    sMask[q][rr] = (row_of(rr) < R && q < a.W) ? mword : 0ull;
   }
   __syncthreads();
 
   const int sw = r16 & (CPR - 1);  // swizzle of the K rows this lane reads
-  // A row group whose rows all lie past the kept slots' rows (the last
-  // block of a unit whose row count is not a multiple of the block's) only
-  // helps stage the tiles: its accumulators stay zero, which writes the
-  // zero output (or empty partial) such rows get.
-  const bool active = row0 + rg * 16 * WR < R;  // wave-uniform
+  // A row group whose rows all lie past the kept slots' rows (when the
+  // unit's row count is not a multiple of the blocks') only helps stage the
+  // tiles: its accumulators stay zero, which writes the zero output (or
+  // empty partial) such rows get.
+  const bool active = row_of(rg * 16 * WR) < R;  // wave-uniform
   for (int it = 0; it < cnt; ++it) {
     const int cur = it % NB;
     // buffer (it+PD) % NB was last read in iteration it-1, before its barrier
@@ -487,7 +497,7 @@ void tree_attn_bf16_kernel(AttnArgs a) {
       o[dt] = oacc[w][dt] * f0 +
               *(const f32x4_t*)&xo[(((rg * WR + w) * DT + dt) * 64 + lane) * 4] * f1;
     const int rr = rg * 16 * WR + w * 16 + r16;
-    const int r = row0 + rr;
+    const int r = row_of(rr);
     if (r >= RT) continue;
     if (a.S == 1) {
       const int slot = r / a.G, gg = r - slot * a.G;
@@ -711,6 +721,7 @@ hipError_t launch_tree_attention(const Plan& p, const AttnWs& w,
   a.W = p.W;
   a.nqb = p.attn_nqb;
   a.S = p.attn_splits;
+  a.interleave = p.attn_wr == 1 && p.attn_splits == 1 && p.attn_nqb > 1;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   if (p.qdt == ET_F32) {
