@@ -16,8 +16,9 @@
 //   runs on XCD i % 8, so the launch maps every block of a unit to one XCD
 //   and the unit's K/V and split partials stay in that XCD's L2.  When the
 //   grid is larger than the chip holds at once, units are taken in order
-//   of their sequence's prefix length, longest first (a one-block kernel
-//   ranks the batch), so that the blocks left for the end are short.
+//   of their sequence's prefix length, longest first (up to 64 sequences
+//   each wave ranks the batch itself, above that a one-block kernel does),
+//   so that the blocks left for the end are short.
 //   Scores are computed transposed, S^T = K . Q^T, which leaves each lane
 //   holding one query row (lane % 16) and 4 consecutive keys per 16-key
 //   sub-tile; that register layout is directly the B operand of
@@ -53,6 +54,7 @@ struct AttnArgs {
   const uint64_t* mask;
   const int32_t* n_kept;
   const int32_t* order;  // sequence of unit-sequence b0, or null (b = b0)
+  int rank_inline;       // no order array: each wave ranks the batch (B <= 64)
   void* out;
   float* po;
   float* pm;
@@ -157,6 +159,25 @@ __device__ __forceinline__ bool attn_block_coords(int i, int units, int per_unit
   return u < units;
 }
 
+// The sequence of rank r (0-based) when a batch of B <= 64 sequences, one
+// per lane, is ordered by prefix length, longest first, ties by index: the
+// (r + 1)-th largest of the distinct keys length * 64 + 63 - index, found
+// bit by bit from the top with one ballot per bit (lengths below 2^26 keep
+// the order exact; whatever the lengths, the result is a lane below B,
+// since for r < B the (r + 1)-th largest key is one of theirs: unused
+// lanes hold 0 and the batch's keys end in 63 - index > 0 when B < 64).
+__device__ __forceinline__ int sequence_of_rank(const int32_t* prefix_len, int B, int r) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t key = lane < B ? ((uint32_t)prefix_len[lane] << 6) | (uint32_t)(63 - lane) : 0u;
+  uint32_t t = 0;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    if (__popcll(__ballot(key >= cand)) > r) t = cand;
+  }
+  return 63 - (int)(t & 63u);
+}
+
 __device__ __forceinline__ void barrier_no_fence() {
   // s_barrier alone: the direct loads still in flight into another buffer
   // need no fence here (each wave waits for its own loads with an explicit
@@ -186,7 +207,7 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   if (!attn_block_coords(blockIdx.x, a.B * a.Hkv, a.nqb * a.S, &unit, &rem)) return;
   const int qb = rem / a.S, split = rem - qb * a.S;
   const int b0 = unit / a.Hkv, kvh = unit - b0 * a.Hkv;
-  const int b = a.order ? a.order[b0] : b0;
+  const int b = a.order ? a.order[b0] : a.rank_inline ? sequence_of_rank(a.prefix_len, a.B, b0) : b0;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int rg = wave & 3, kh = wave >> 2;  // row group, key half of a tile
   const int r16 = lane & 15, g = lane >> 4;
@@ -708,6 +729,7 @@ hipError_t launch_tree_attention(const Plan& p, const AttnWs& w,
   a.mask = mask;
   a.n_kept = n_kept;
   a.order = nullptr;
+  a.rank_inline = 0;
   a.out = out;
   a.po = w.o;
   a.pm = w.m;
@@ -735,7 +757,11 @@ hipError_t launch_tree_attention(const Plan& p, const AttnWs& w,
   // longest sequences first.  (Only without key splits: the split merge
   // maps units to sequences directly.)
   const int resident = 256 * (ET_ATTN_NB(p.attn_wr) == 2 ? 2 : 1);
-  if (p.B > 1 && p.B <= kAttnOrderMaxB && p.attn_splits == 1 && blocks > resident) {
+  // Up to 64 sequences (lengths below 2^26) each wave ranks the batch
+  // itself, one sequence per lane, instead of a launch of its own.
+  if (p.B > 1 && p.B <= 64 && p.Pcap < (1 << 26) && p.attn_splits == 1 && blocks > resident) {
+    a.rank_inline = 1;
+  } else if (p.B > 1 && p.B <= kAttnOrderMaxB && p.attn_splits == 1 && blocks > resident) {
     const int nt = p.B < 1024 ? (p.B + 63) / 64 * 64 : 1024;
     tree_attn_order_kernel<<<1, nt, 0, s>>>(prefix_len, p.B, w.order);
     hipError_t e = hipGetLastError();
