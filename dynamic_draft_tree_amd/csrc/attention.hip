@@ -64,6 +64,13 @@ struct AttnArgs {
   float scale, scale_log2;
 };
 
+// Global-memory (address space 1) element types.
+typedef __attribute__((address_space(1))) int32_t gmem_i32;
+typedef __attribute__((address_space(1))) float gmem_f32;
+typedef __attribute__((address_space(1))) f32x4_t gmem_f32x4;
+typedef __attribute__((address_space(1))) uint16_t gmem_u16;
+typedef __attribute__((address_space(1))) u32x2_t gmem_u32x2;
+
 // Growth of a row's max (log2 units) tolerated before O is rescaled.
 constexpr float kSlack = 8.0f;
 
@@ -203,15 +210,26 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sKV[NB][2][TE];
   __shared__ uint64_t sMask[4][BR];  // [tree tile][row of the block]
 
+  // The arguments that pick the block's sequence in one round of scalar
+  // loads, then its kept count and prefix length in one round (pointers
+  // pass the asm as integers and come back as global-memory pointers).
+  int nB = a.B, nHkv = a.Hkv, nqbs = a.nqb, nS = a.S, rank_inline = a.rank_inline;
+  uint64_t u_order = (uint64_t)a.order, u_nk = (uint64_t)a.n_kept, u_pl = (uint64_t)a.prefix_len;
+  asm volatile("" : "+s"(nB), "+s"(nHkv), "+s"(nqbs), "+s"(nS), "+s"(rank_inline), "+s"(u_order),
+               "+s"(u_nk), "+s"(u_pl));
   int unit, rem;
-  if (!attn_block_coords(blockIdx.x, a.B * a.Hkv, a.nqb * a.S, &unit, &rem)) return;
-  const int qb = rem / a.S, split = rem - qb * a.S;
-  const int b0 = unit / a.Hkv, kvh = unit - b0 * a.Hkv;
-  const int b = a.order ? a.order[b0] : a.rank_inline ? sequence_of_rank(a.prefix_len, a.B, b0) : b0;
+  if (!attn_block_coords(blockIdx.x, nB * nHkv, nqbs * nS, &unit, &rem)) return;
+  const int qb = rem / nS, split = rem - qb * nS;
+  const int b0 = unit / nHkv, kvh = unit - b0 * nHkv;
+  const int b = __builtin_amdgcn_readfirstlane(
+      u_order ? ((const gmem_i32*)u_order)[b0]
+              : rank_inline ? sequence_of_rank(a.prefix_len, nB, b0) : b0);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int rg = wave & 3, kh = wave >> 2;  // row group, key half of a tile
   const int r16 = lane & 15, g = lane >> 4;
-  const int n = a.n_kept[b];
+  int n = __builtin_amdgcn_readfirstlane(((const gmem_i32*)u_nk)[b]);
+  int P = __builtin_amdgcn_readfirstlane(((const gmem_i32*)u_pl)[b]);
+  asm volatile("" : "+s"(n), "+s"(P));
   const int R = (n + 1) * a.G;
   const int RT = a.T * a.G;
   const int row0 = qb * BR;
@@ -240,7 +258,6 @@ void tree_attn_bf16_kernel(AttnArgs a) {
     return;
   }
 
-  const int P = a.prefix_len[b];
   const int tp = (P + kAttnTile - 1) / kAttnTile;
   const int tt = (n + 1 + kAttnTile - 1) / kAttnTile;
   const int tot = tp + tt;
@@ -580,24 +597,32 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a) {
   constexpr int RPB = 256 / TPR;  // rows per block
   constexpr int BR = 64 * WR;
   constexpr int MB = BR / RPB;    // merge blocks per (unit, row block)
+  // The arguments in one round of scalar loads, then the kept count and
+  // the split partials in one round of loads: the partials are read
+  // whatever the count (rows past it hold unused workspace, replaced by
+  // zeros at the end), so no load waits for another.
+  // (Pointers pass the asm as integers and come back as global-memory
+  // pointers, which keeps their loads global rather than flat.)
+  int B = a.B, Hkv = a.Hkv, nqb = a.nqb, S = a.S, T = a.T, G = a.G, Hq = a.Hq;
+  uint64_t u_nk = (uint64_t)a.n_kept, u_po = (uint64_t)a.po, u_pm = (uint64_t)a.pm,
+           u_pl = (uint64_t)a.pl, u_out = (uint64_t)a.out;
+  asm volatile("" : "+s"(B), "+s"(Hkv), "+s"(nqb), "+s"(S), "+s"(T), "+s"(G), "+s"(Hq),
+               "+s"(u_nk), "+s"(u_po), "+s"(u_pm), "+s"(u_pl), "+s"(u_out));
+  const gmem_i32* n_kept = (const gmem_i32*)u_nk;
+  const gmem_f32 *po = (const gmem_f32*)u_po, *pm = (const gmem_f32*)u_pm,
+                 *pl = (const gmem_f32*)u_pl;
   int unit, rem;
-  if (!attn_block_coords(blockIdx.x, a.B * a.Hkv, a.nqb * MB, &unit, &rem)) return;
+  if (!attn_block_coords(blockIdx.x, B * Hkv, nqb * MB, &unit, &rem)) return;
   const int qb = rem / MB, mb = rem - qb * MB;
   const int rr = mb * RPB + threadIdx.x / TPR;
   const int col = (threadIdx.x % TPR) * 4;
-  const int b = unit / a.Hkv, kvh = unit - b * a.Hkv;
+  const int b = unit / Hkv, kvh = unit - b * Hkv;
   const int r = qb * BR + rr;
-  const int RT = a.T * a.G;
-  if (r >= RT) return;
-  const int R = (a.n_kept[b] + 1) * a.G;
-  const int slot = r / a.G, gg = r - slot * a.G;
-  uint16_t* orow = (uint16_t*)a.out +
-                   (((int64_t)b * a.T + slot) * a.Hq + kvh * a.G + gg) * HD + col;
-  if (r >= R) {
-    *(uint2*)orow = make_uint2(0u, 0u);
-    return;
-  }
-  const int64_t base = (int64_t)(unit * a.nqb + qb) * a.S;
+  if (r >= T * G) return;
+  const int R = (n_kept[b] + 1) * G;
+  const int slot = r / G, gg = r - slot * G;
+  gmem_u16* orow = (gmem_u16*)u_out + (((int64_t)b * T + slot) * Hq + kvh * G + gg) * HD + col;
+  const int64_t base = (int64_t)(unit * nqb + qb) * S;
   float mi[kAttnMaxSplits], li[kAttnMaxSplits];
   float4 oi[kAttnMaxSplits];
 #pragma unroll
@@ -605,11 +630,12 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a) {
     mi[i] = -INFINITY;
     li[i] = 0.f;
     oi[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (i < a.S) {
+    if (i < S) {
       const int64_t pr = (base + i) * BR + rr;
-      mi[i] = a.pm[pr];
-      li[i] = a.pl[pr];
-      oi[i] = *(const float4*)(a.po + pr * HD + col);
+      mi[i] = pm[pr];
+      li[i] = pl[pr];
+      const f32x4_t v = *(const gmem_f32x4*)(po + pr * HD + col);
+      oi[i] = make_float4(v.x, v.y, v.z, v.w);
     }
   }
   float m = -INFINITY;
@@ -630,7 +656,8 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a) {
   uint2 w;
   w.x = (uint32_t)f32_to_bf16_rne(acc.x * inv) | ((uint32_t)f32_to_bf16_rne(acc.y * inv) << 16);
   w.y = (uint32_t)f32_to_bf16_rne(acc.z * inv) | ((uint32_t)f32_to_bf16_rne(acc.w * inv) << 16);
-  *(uint2*)orow = w;
+  if (r >= R) w = make_uint2(0u, 0u);  // rows of unkept slots
+  *(gmem_u32x2*)orow = u32x2_t{w.x, w.y};
 }
 
 // fp32 inputs: one block per (slot, q head, sequence), keys in chunks of
