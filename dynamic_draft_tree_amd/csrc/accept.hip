@@ -44,9 +44,17 @@ __global__ __launch_bounds__(256) void accept_scan_kernel(AcceptArgs a) {
   const int nch = min(a.cpb, a.S - c0);
   float x[E];
   u32x4_t raw[VEC ? chunk_vectors<BF16, E>() : 1];
+  // n_kept's address with the arguments the loads need, in one round
+  uint64_t u_nk = (uint64_t)a.n_kept;
+  asm volatile("" : "+s"(u_nk));
+  int nkv = ((const gmem_i32*)u_nk)[b];
   if constexpr (VEC) issue_chunk<BF16, E>(row, c0 * kChunkE, a.V, tid, raw);
   else load_chunk<BF16, false, E>(row, c0 * kChunkE, a.V, tid, x);
-  if (srow > a.n_kept[b]) return;
+  // The pins keep the loads ahead of the test (the compiler otherwise
+  // moves the test, and its wait for n_kept, in front of them).
+  pin_loaded<VEC, E>(raw, x);
+  asm volatile("" : "+v"(nkv));
+  if (srow > __builtin_amdgcn_readfirstlane(nkv)) return;
   const int64_t rowid = (int64_t)b * a.T + srow;
   for (int ci = 0; ci < nch; ++ci) {
     const int c = c0 + ci;

@@ -64,11 +64,8 @@ struct AttnArgs {
   float scale, scale_log2;
 };
 
-// Global-memory (address space 1) element types.
-typedef __attribute__((address_space(1))) int32_t gmem_i32;
-typedef __attribute__((address_space(1))) float gmem_f32;
+// Global-memory (address space 1) vector types.
 typedef __attribute__((address_space(1))) f32x4_t gmem_f32x4;
-typedef __attribute__((address_space(1))) uint16_t gmem_u16;
 typedef __attribute__((address_space(1))) u32x2_t gmem_u32x2;
 
 // Growth of a row's max (log2 units) tolerated before O is rescaled.

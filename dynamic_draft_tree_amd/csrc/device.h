@@ -195,10 +195,31 @@ __device__ __forceinline__ int elem_off(int e, int tid) {
   return ((e / per) * kLoadThreads + tid) * per + (e % per);
 }
 
+// Global-memory (address space 1) element types, for pointers that come
+// back from an asm statement as integers: loads through them stay global
+// loads rather than flat ones.
+typedef __attribute__((address_space(1))) int32_t gmem_i32;
+typedef __attribute__((address_space(1))) float gmem_f32;
+typedef __attribute__((address_space(1))) uint16_t gmem_u16;
+
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // 16-byte vectors a thread holds for E elements of a chunk
 template <bool BF16, int E>
 constexpr int chunk_vectors() { return E / (BF16 ? 8 : 4); }
+
+// Holds the values of a chunk's loads (raw on the vector path, x on the
+// element path) in registers at this point, so a test that follows cannot
+// be moved by the compiler in front of the loads' issue.
+template <bool VEC, int E, int NV>
+__device__ __forceinline__ void pin_loaded(u32x4_t (&raw)[NV], float (&x)[E]) {
+  if constexpr (VEC) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) asm volatile("" : "+v"(raw[i]));
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) asm volatile("" : "+v"(x[e]));
+  }
+}
 
 // Vector path, first half: issue the thread's 16-byte loads of the chunk
 // at `base`.  A vector that runs past the row end loads the row's first

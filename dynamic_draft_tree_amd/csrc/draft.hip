@@ -595,8 +595,7 @@ __device__ __forceinline__ void merge_rows(const DraftArgs& a, const FixedFronti
 template <bool BF16, bool VEC, int E, bool WAVE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VEC ? (E > 32 ? 4 : 3) : 1))) void draft_scan_kernel(DraftArgs a) {
   constexpr int kChunkE = kScanThreads * E;
-  const int j = blockIdx.y, b = blockIdx.z;
-  if (a.step == 1 && j > 0) return;  // the root is the only row of step 1
+  const int j = blockIdx.y, b = blockIdx.z;  // (step 1 launches row 0 only)
   const char* row = (const char*)a.logits + (b * a.bstride + j * a.rstride) * (BF16 ? 2 : 4);
   const int c0 = blockIdx.x * a.cpb;
   float x[E];
@@ -730,7 +729,8 @@ hipError_t launch_draft_step(const Plan& p, const DraftWs& w, int step,
   a.cap = p.cap;
   a.thr = p.cfg.expand_threshold;
   const bool bf = p.ldt == ET_BF16;
-  const dim3 grid((p.s_draft + p.draft_cpb - 1) / p.draft_cpb, p.k, p.B);
+  // step 1 scans the root row only: one row of blocks per sequence
+  const dim3 grid((p.s_draft + p.draft_cpb - 1) / p.draft_cpb, step == 1 ? 1 : p.k, p.B);
   const bool wv = p.s_draft * kWaves <= 64;
   a.parts = wv ? p.s_draft * kWaves : p.s_draft;
 #define ET_SCAN(W, X)                                                                                   \

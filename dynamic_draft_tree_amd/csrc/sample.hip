@@ -146,9 +146,16 @@ __global__ __launch_bounds__(256) void sample_scan_kernel(SampleArgs a) {
   // the first range is in flight before n_kept arrives (all T rows are
   // readable memory by contract; rows past n_kept are dropped)
   const int j0 = c0 * kSegsPerChunk + wave;
+  // n_kept's address with the arguments the loads need, in one round
+  uint64_t u_nk = (uint64_t)a.n_kept;
+  asm volatile("" : "+s"(u_nk));
+  int nkv = ((const gmem_i32*)u_nk)[b];
   if constexpr (VEC) issue_range<BF16, E>(row, j0 * kSeg, a.V, lane, raw);
   else load_range_elems<BF16, E>(row, j0 * kSeg, a.V, lane, x);
-  if (srow > a.n_kept[b]) return;
+  // (the pins keep the loads ahead of the test and its wait for n_kept)
+  pin_loaded<VEC, E>(raw, x);
+  asm volatile("" : "+v"(nkv));
+  if (srow > __builtin_amdgcn_readfirstlane(nkv)) return;
   double2* out = a.part + ((int64_t)b * a.T + srow) * (a.S * kSegsPerChunk);
   for (int ci = 0; ci < nch; ++ci) {
     const int j = j0 + ci * kSegsPerChunk;
