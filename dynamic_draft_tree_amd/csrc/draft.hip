@@ -624,7 +624,14 @@ __global__ __launch_bounds__(1024) void draft_merge_fixed_kernel(DraftArgs a, Fi
 // the pool size once it is known); the step's children come from LDS.
 template <bool BF16, int KST>
 __global__ __launch_bounds__(1024) void draft_merge_last_kernel(DraftArgs a, RerankOut o) {
-  const int b = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+  // The arguments of the merge's first loads, read with the pool's in one
+  // round of scalar loads (the compiler would otherwise read them in two
+  // more rounds, between the pool loads and the merge's).
+  asm volatile("" ::"s"(a.ws.frontier), "s"(a.ws.frontier_val), "s"(a.ws.frontier_count),
+               "s"(a.ws.part_m), "s"(a.ws.part_s), "s"(a.ws.part_keys), "s"(a.ws.pool_count),
+               "s"(a.ws.root_token), "s"(a.root_tokens), "s"(o.prefix_len), "s"(a.k), "s"(a.B),
+               "s"(a.parts), "s"(a.step), "s"(a.cap));
+  const int b = blockIdx.x, tid = threadIdx.x, nt = 64 * a.k;  // (the launch has 64 k threads)
   __shared__ RerankLds L;
   const int64_t pb = (int64_t)b * a.cap;
   const int rounds = (a.cap + nt - 1) / nt;  // <= kRerankPer (checked by the host)
