@@ -34,6 +34,8 @@
 //   tile is tested per key in registers.  With S > 1 each split writes
 //   (O, m, l) partials and a merge kernel combines them.
 // fp32 path: plain per-row kernel (vector ALU), for fp32 inputs.
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
@@ -86,22 +88,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// ds_read_b64_tr_b16 at an LDS byte address, plus a fixed byte offset.
-// Plain (non-template) device functions: the host pass never sees the
-// assembly inside a kernel body.
-__device__ __forceinline__ u32x2_t ds_read_tr16(uint32_t addr) {
+// ds_read_b64_tr_b16 at an LDS byte address plus an immediate offset.
+template <int OFF>
+__device__ __forceinline__ u32x2_t ds_read_tr16_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "16-bit LDS offset");
   u32x2_t v;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
-  return v;
-}
-__device__ __forceinline__ u32x2_t ds_read_tr16_off2k(uint32_t addr) {
-  u32x2_t v;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:2048" : "=v"(v) : "v"(addr));
-  return v;
-}
-__device__ __forceinline__ u32x2_t ds_read_tr16_off4k(uint32_t addr) {
-  u32x2_t v;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:4096" : "=v"(v) : "v"(addr));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
   return v;
 }
 
@@ -125,6 +117,7 @@ __device__ __forceinline__ void lds_wait_all(u32x2_t (&x)[4], u32x2_t (&y)[4]) {
 // direct loads still filling another buffer).
 template <int OFF>
 __device__ __forceinline__ bf16x8_t ds_read_b128_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "16-bit LDS offset");
   bf16x8_t v;
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
   return v;
@@ -204,7 +197,9 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   constexpr int CH = kAttnTile * CPR / 64 / 8;  // 1 KB slabs per wave per tile
   constexpr int PD = NB - 1;       // prefetch distance
   constexpr int BR = 64 * WR;      // query rows per block
-  __shared__ __attribute__((aligned(16))) uint16_t sKV[NB][2][TE];
+  // [K or V][buffer][tile]: the K tiles, then the V tiles, so that every
+  // read of a buffer is one per-lane address plus an immediate offset
+  __shared__ __attribute__((aligned(16))) uint16_t sKV[2][NB][TE];
   __shared__ uint64_t sMask[4][BR];  // [tree tile][row of the block]
 
   // The arguments that pick the block's sequence in one round of scalar
@@ -324,25 +319,34 @@ void tree_attn_bf16_kernel(AttnArgs a) {
     const int klast_ = (tr_ ? n + 1 : P) - 1;                                 \
     const uint16_t* Kg_ = tr_ ? ktb : kcb;                                    \
     const uint16_t* Vg_ = tr_ ? vtb : vcb;                                    \
-    _Pragma("unroll") for (int c_ = 0; c_ < CH; ++c_) {                       \
-      const int slab = c_ * 8 + wave_u;                                       \
-      const int64_t go = (int64_t)min(k0_ + trow[c_], klast_) * HD + tcol[c_]; \
-      load_lds16(Kg_ + go, &sKV[(BUF_)][0][slab * 512]);                      \
-      load_lds16(Vg_ + go, &sKV[(BUF_)][1][slab * 512]);                      \
+    if (k0_ + kAttnTile <= klast_ + 1) {                                      \
+      const char* Kt_ = (const char*)(Kg_ + (int64_t)k0_ * HD);               \
+      const char* Vt_ = (const char*)(Vg_ + (int64_t)k0_ * HD);               \
+      _Pragma("unroll") for (int c_ = 0; c_ < CH; ++c_) {                     \
+        const int slab = c_ * 8 + wave_u;                                     \
+        const uint32_t bo_ = c_ * (512 / CPR) * HD * 2;                       \
+        load_lds16(Kt_ + bo_ + tboff, &sKV[0][(BUF_)][slab * 512]);           \
+        load_lds16(Vt_ + bo_ + tboff, &sKV[1][(BUF_)][slab * 512]);           \
+      }                                                                       \
+    } else {                                                                  \
+      _Pragma("unroll") for (int c_ = 0; c_ < CH; ++c_) {                     \
+        const int slab = c_ * 8 + wave_u;                                     \
+        const int64_t go = (int64_t)min(k0_ + trow + c_ * (512 / CPR), klast_) * HD + tcol; \
+        load_lds16(Kg_ + go, &sKV[0][(BUF_)][slab * 512]);                    \
+        load_lds16(Vg_ + go, &sKV[1][(BUF_)][slab * 512]);                    \
+      }                                                                       \
     }                                                                         \
   } while (0)
 
-  // Per lane and slab, the tile row it loads and its swizzled column,
-  // computed once (the wave index made uniform, so each slab's LDS address
-  // is scalar arithmetic).
+  // Per lane, the tile row it loads in its first slab and the swizzled
+  // column, computed once (the wave index made uniform, so each slab's LDS
+  // address is scalar arithmetic).  Slab c_ lies 512 / CPR rows further on,
+  // with the same column (a multiple of CPR rows leaves the swizzle as is).
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  int trow[CH], tcol[CH];
-#pragma unroll
-  for (int c_ = 0; c_ < CH; ++c_) {
-    const int q = (c_ * 8 + wave_u) * 64 + lane;
-    trow[c_] = q / CPR;
-    tcol[c_] = ((q % CPR) ^ (trow[c_] & (CPR - 1))) * 8;
-  }
+  const int trow = (wave_u * 64 + lane) / CPR;
+  const int tcol = (((wave_u * 64 + lane) % CPR) ^ (trow & (CPR - 1))) * 8;
+  const uint32_t tboff = (uint32_t)(trow * HD + tcol) * 2u;  // bytes, in a tile whose rows all exist
+  static_assert((512 / CPR) % CPR == 0, "slabs keep the swizzle");
   if (cnt > 0) ET_ISSUE_TILE(t_begin, 0);
   if (PD > 1 && cnt > 1) ET_ISSUE_TILE(t_begin + 1, 1);
   // Q, the mask word and tile 0 have landed; tile 1 may still be in flight
@@ -360,17 +364,33 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   // tiles: its accumulators stay zero, which writes the zero output (or
   // empty partial) such rows get.
   const bool active = row_of(rg * 16 * WR) < R;  // wave-uniform
-  for (int it = 0; it < cnt; ++it) {
-    const int cur = it % NB;
-    // buffer (it+PD) % NB was last read in iteration it-1, before its barrier
-    if (it + PD < cnt) ET_ISSUE_TILE(t_begin + it + PD, (it + PD) % NB);
+  // Per-lane LDS addresses of the K fragments and V transpose reads in
+  // buffer 0; buffer `cur` adds cur * TE * 2 bytes (K) as an immediate
+  // offset, and the V tiles lie NB * TE * 2 bytes further on.
+  uint32_t ka0[KSTEPS], va0[DT];
+  {
+    const uint32_t kb = lds_addr(&sKV[0][0][0]) + (kh * 32 + r16) * (HD * 2);
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) ka0[kk] = kb + (((kk * 4 + g) ^ sw) * 16);
+    const int vrow = kh * 32 + g * 4 + (r16 >> 2);
+    const uint32_t vbase = lds_addr(&sKV[1][0][vrow * HD]) + (r16 & 1) * 8;
+    const int vsw = vrow & (CPR - 1);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) va0[dt] = vbase + (((dt * 2 + ((r16 >> 1) & 1)) ^ vsw) * 16);
+  }
+  // One tile step on buffer CUR (a compile-time index: the loop below runs
+  // NB steps per trip, so every LDS address is a fixed register plus an
+  // immediate and no address is recomputed per tile).
+  auto tile_step = [&](auto CUR_, const int it) {
+    constexpr int cur = decltype(CUR_)::value;
+    constexpr int kofs = cur * TE * 2;  // byte offset of buffer cur
+    // buffer (cur+PD) % NB was last read in step it-1, before its barrier
+    if (it + PD < cnt) ET_ISSUE_TILE(t_begin + it + PD, (cur + PD) % NB);
 
     if (active) {
     const int t = t_begin + it;
     const bool tree = t >= tp;
     const int key0 = (tree ? t - tp : t) * kAttnTile;
-    const uint16_t* Ks = sKV[cur][0];
-    const uint16_t* Vs = sKV[cur][1];
 
     // S^T = K . Q^T over this wave's 32 keys: lane holds row r16 and keys
     // kh*32 + s2*16 + 4g + e.  Every K fragment of the tile is read before
@@ -383,12 +403,10 @@ void tree_attn_bf16_kernel(AttnArgs a) {
       for (int w = 0; w < WR; ++w) sacc[w][s2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     {
       bf16x8_t af[KSTEPS][2];
-      const uint32_t kb = lds_addr(Ks) + (kh * 32 + r16) * (HD * 2);
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
-        const uint32_t ka = kb + (((kk * 4 + g) ^ sw) * 16);
-        af[kk][0] = ds_read_b128_at<0>(ka);
-        af[kk][1] = ds_read_b128_at<16 * HD * 2>(ka);  // 16 key rows below
+        af[kk][0] = ds_read_b128_at<kofs>(ka0[kk]);
+        af[kk][1] = ds_read_b128_at<kofs + 16 * HD * 2>(ka0[kk]);  // 16 key rows below
       }
       lds_wait_k(af);
 #pragma unroll
@@ -409,16 +427,12 @@ void tree_attn_bf16_kernel(AttnArgs a) {
     // vector work then hides their latency; 64-row blocks issue them after
     // it, keeping four waves per SIMD within the register budget.
     u32x2_t vlo[DT], vhi[DT];
-    const int vrow = kh * 32 + g * 4 + (r16 >> 2);
-    const uint32_t vbase = lds_addr(Vs + vrow * HD) + (r16 & 1) * 8;
-    const int vsw = vrow & (CPR - 1);
     auto issue_v = [&]() {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         // this lane's source word: key row vrow (+16), d = dt*16 + 4*(r16%4)
-        const uint32_t va = vbase + (((dt * 2 + ((r16 >> 1) & 1)) ^ vsw) * 16);
-        vlo[dt] = ds_read_tr16(va);
-        vhi[dt] = HD == 128 ? ds_read_tr16_off4k(va) : ds_read_tr16_off2k(va);
+        vlo[dt] = ds_read_tr16_at<kofs>(va0[dt]);
+        vhi[dt] = ds_read_tr16_at<kofs + 16 * HD * 2>(va0[dt]);  // 16 key rows below
       }
     };
     if constexpr (NB == 3) issue_v();
@@ -492,6 +506,12 @@ void tree_attn_bf16_kernel(AttnArgs a) {
     if (PD > 1 && it + 2 < cnt) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * CH));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     barrier_no_fence();
+  };
+  for (int it = 0; it < cnt; it += NB) {
+    tile_step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < cnt) tile_step(std::integral_constant<int, 1>{}, it + 1);
+    if constexpr (NB == 3)
+      if (it + 2 < cnt) tile_step(std::integral_constant<int, NB - 1>{}, it + 2);
   }
 
   // Combine the two key halves of every row group: the kh = 1 waves
