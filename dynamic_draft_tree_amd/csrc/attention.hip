@@ -465,8 +465,7 @@ void tree_attn_bf16_kernel(AttnArgs a) {
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sv[s2][e]);
-      tmax = fmaxf(tmax, xor_lane<16>(tmax));
-      tmax = fmaxf(tmax, xor_lane<32>(tmax));
+      tmax = max_xor_rows<32>(max_xor_rows<16>(tmax));
       const float tm = tmax * c;
       if (__ballot(tm > m_run[w] + kSlack) != 0ull) {
         const float m_new = fmaxf(m_run[w], tm);

@@ -1,6 +1,7 @@
 // device.h -- wave64 primitives and ordering keys shared by the kernels.
 #pragma once
 
+#include <cfloat>
 #include <cstdint>
 
 #include <hip/hip_runtime.h>
@@ -113,27 +114,76 @@ __device__ __forceinline__ T xor_lane_rt(T v, int m) {
 }
 
 // Butterfly reductions: every lane ends with the same result.
+// Reductions with lane l ^ 16 (M = 16) or l ^ 32 (M = 32): a row (half)
+// swap of v with itself leaves, in its two result registers, v and the
+// partner's value in an order that depends on the lane, so a symmetric
+// combination of the two needs no select.  The maximum is taken as the
+// median of the two and FLT_MAX, which needs no canonicalising of its
+// operands (values are finite or -inf: no NaN, no +inf).  Results equal
+// those of combining v with xor_lane<M>(v).
+template <int M>
+__device__ __forceinline__ void xor_rows_pair(uint32_t v, uint32_t* a, uint32_t* b) {
+  static_assert(M == 16 || M == 32, "row distance");
+  if constexpr (M == 16) {
+    auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    *a = (uint32_t)r[0];
+    *b = (uint32_t)r[1];
+  } else {
+    auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    *a = (uint32_t)r[0];
+    *b = (uint32_t)r[1];
+  }
+}
+template <int M>
+__device__ __forceinline__ float max_xor_rows(float v) {
+  uint32_t a, b;
+  xor_rows_pair<M>(__float_as_uint(v), &a, &b);
+  return __builtin_amdgcn_fmed3f(__uint_as_float(a), __uint_as_float(b), FLT_MAX);
+}
+template <int M>
+__device__ __forceinline__ float sum_xor_rows(float v) {
+  uint32_t a, b;
+  xor_rows_pair<M>(__float_as_uint(v), &a, &b);
+  return __uint_as_float(a) + __uint_as_float(b);
+}
 __device__ __forceinline__ float wave_max_f32(float v) {
+  v = max_xor_rows<32>(v);
+  v = max_xor_rows<16>(v);
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, xor_lane_rt(v, m));
+  for (int m = 8; m >= 1; m >>= 1) v = fmaxf(v, xor_lane_rt(v, m));
   return v;
 }
 __device__ __forceinline__ float wave_sum_f32(float v) {
+  v = sum_xor_rows<32>(v);
+  v = sum_xor_rows<16>(v);
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += xor_lane_rt(v, m);
+  for (int m = 8; m >= 1; m >>= 1) v += xor_lane_rt(v, m);
   return v;
 }
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-  v = min(v, xor_lane<32>(v));
-  v = min(v, xor_lane<16>(v));
+  uint32_t a, b;
+  xor_rows_pair<32>(v, &a, &b);
+  v = min(a, b);
+  xor_rows_pair<16>(v, &a, &b);
+  v = min(a, b);
   v = min(v, xor_lane<8>(v));
   v = min(v, xor_lane<4>(v));
   v = min(v, xor_lane<2>(v));
   return min(v, xor_lane<1>(v));
 }
+template <int M>
+__device__ __forceinline__ uint64_t max_xor_rows(uint64_t v) {
+  uint32_t alo, blo, ahi, bhi;
+  xor_rows_pair<M>((uint32_t)v, &alo, &blo);
+  xor_rows_pair<M>((uint32_t)(v >> 32), &ahi, &bhi);
+  const uint64_t a = ((uint64_t)ahi << 32) | alo, b = ((uint64_t)bhi << 32) | blo;
+  return a > b ? a : b;
+}
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = max_xor_rows<32>(v);
+  v = max_xor_rows<16>(v);
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
+  for (int m = 8; m >= 1; m >>= 1) {
     const uint64_t o = xor_lane_rt(v, m);
     v = o > v ? o : v;
   }
