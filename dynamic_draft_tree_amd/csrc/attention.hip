@@ -284,12 +284,17 @@ void tree_attn_bf16_kernel(AttnArgs a) {
     for (int dt = 0; dt < DT; ++dt) oacc[w][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // Row sums l ride on the matrix cores as well: ones . P^T adds the bf16
   // weights exactly as V^T . P^T uses them, replicated over the 16 d rows.
+  // Per row: the running max m (scaled, log2 units), the exponent offset
+  // -m (0 while m = -inf) and the raw tile max above which m is raised,
+  // (m + kSlack) / c, all updated only when m is.
   f32x4_t lacc[WR];
-  float m_run[WR];
+  float m_run[WR], nmu[WR], raise_at[WR];
 #pragma unroll
   for (int w = 0; w < WR; ++w) {
     lacc[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     m_run[w] = -INFINITY;
+    nmu[w] = 0.f;
+    raise_at[w] = -INFINITY;
   }
   bf16x8_t ones;
 #pragma unroll
@@ -466,22 +471,22 @@ void tree_attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sv[s2][e]);
       tmax = max_xor_rows<32>(max_xor_rows<16>(tmax));
-      const float tm = tmax * c;
-      if (__ballot(tm > m_run[w] + kSlack) != 0ull) {
-        const float m_new = fmaxf(m_run[w], tm);
+      if (__ballot(tmax > raise_at[w]) != 0ull) {
+        const float m_new = fmaxf(m_run[w], tmax * c);
         const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[w] - m_new);
         m_run[w] = m_new;
+        // a row that has seen no visible key keeps m = -inf and gets p = 0
+        nmu[w] = m_new == -INFINITY ? 0.f : -m_new;
+        raise_at[w] = (m_new + kSlack) / c;
         lacc[w] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[w][dt] *= alpha;
       }
-      // a row that has seen no visible key keeps m = -inf and gets p = 0
-      const float mu = m_run[w] == -INFINITY ? 0.f : m_run[w];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          pf[w][s2 * 4 + e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sv[s2][e], c, -mu));
+          pf[w][s2 * 4 + e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sv[s2][e], c, nmu[w]));
     }
 
     if constexpr (NB != 3) issue_v();
