@@ -187,7 +187,9 @@ __device__ __forceinline__ void barrier_no_fence() {
 // NB LDS tile buffers, prefetch distance NB - 1.  NB = 2 halves the LDS
 // so that two blocks share a compute unit (four waves per SIMD, which hide
 // each other's LDS and matrix latencies) when the registers allow it.
-template <int HD, int WR, int NB>
+// FP: the steps whose tiles are whole prefix tiles run in a loop of their
+// own, without the mask, clamping and tree-or-prefix selects.
+template <int HD, int WR, int NB, bool FP>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NB == 2 ? 4 : 2)))
 void tree_attn_bf16_kernel(AttnArgs a) {
   constexpr int KSTEPS = HD / 32;  // 32-wide d steps of K . Q^T
@@ -316,6 +318,18 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   // slot, load the last valid row instead: finite values whose scores are
   // masked, so they add p = 0 times a finite V (tree rows past n_kept are
   // the caller's unwritten memory and are never read).
+// A tile whose 64 rows all exist, from its first K and V rows.
+#define ET_ISSUE_WHOLE(KT_, VT_, BUF_)                                        \
+  do {                                                                        \
+    const char* Kt_ = (const char*)(KT_);                                     \
+    const char* Vt_ = (const char*)(VT_);                                     \
+    _Pragma("unroll") for (int c_ = 0; c_ < CH; ++c_) {                       \
+      const int slab = c_ * 8 + wave_u;                                       \
+      const uint32_t bo_ = c_ * (512 / CPR) * HD * 2;                         \
+      load_lds16(Kt_ + bo_ + tboff, &sKV[0][(BUF_)][slab * 512]);             \
+      load_lds16(Vt_ + bo_ + tboff, &sKV[1][(BUF_)][slab * 512]);             \
+    }                                                                         \
+  } while (0)
 #define ET_ISSUE_TILE(T_, BUF_)                                               \
   do {                                                                        \
     const int t_ = (T_);                                                      \
@@ -325,14 +339,7 @@ void tree_attn_bf16_kernel(AttnArgs a) {
     const uint16_t* Kg_ = tr_ ? ktb : kcb;                                    \
     const uint16_t* Vg_ = tr_ ? vtb : vcb;                                    \
     if (k0_ + kAttnTile <= klast_ + 1) {                                      \
-      const char* Kt_ = (const char*)(Kg_ + (int64_t)k0_ * HD);               \
-      const char* Vt_ = (const char*)(Vg_ + (int64_t)k0_ * HD);               \
-      _Pragma("unroll") for (int c_ = 0; c_ < CH; ++c_) {                     \
-        const int slab = c_ * 8 + wave_u;                                     \
-        const uint32_t bo_ = c_ * (512 / CPR) * HD * 2;                       \
-        load_lds16(Kt_ + bo_ + tboff, &sKV[0][(BUF_)][slab * 512]);           \
-        load_lds16(Vt_ + bo_ + tboff, &sKV[1][(BUF_)][slab * 512]);           \
-      }                                                                       \
+      ET_ISSUE_WHOLE(Kg_ + (int64_t)k0_ * HD, Vg_ + (int64_t)k0_ * HD, (BUF_));  \
     } else {                                                                  \
       _Pragma("unroll") for (int c_ = 0; c_ < CH; ++c_) {                     \
         const int slab = c_ * 8 + wave_u;                                     \
@@ -386,15 +393,23 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   // One tile step on buffer CUR (a compile-time index: the loop below runs
   // NB steps per trip, so every LDS address is a fixed register plus an
   // immediate and no address is recomputed per tile).
-  auto tile_step = [&](auto CUR_, const int it) {
+  // FAST: the step's tile and the tile it issues are whole prefix tiles
+  // (no clamped rows, no mask), which the caller has checked.
+  auto tile_step = [&](auto CUR_, auto FAST_, const int it) {
     constexpr int cur = decltype(CUR_)::value;
+    constexpr bool fast = decltype(FAST_)::value;
     constexpr int kofs = cur * TE * 2;  // byte offset of buffer cur
     // buffer (cur+PD) % NB was last read in step it-1, before its barrier
-    if (it + PD < cnt) ET_ISSUE_TILE(t_begin + it + PD, (cur + PD) % NB);
+    if constexpr (fast) {
+      const int64_t e0 = (int64_t)(t_begin + it + PD) * (kAttnTile * HD);
+      ET_ISSUE_WHOLE(kcb + e0, vcb + e0, (cur + PD) % NB);
+    } else if (it + PD < cnt) {
+      ET_ISSUE_TILE(t_begin + it + PD, (cur + PD) % NB);
+    }
 
     if (active) {
     const int t = t_begin + it;
-    const bool tree = t >= tp;
+    const bool tree = !fast && t >= tp;
     const int key0 = (tree ? t - tp : t) * kAttnTile;
 
     // S^T = K . Q^T over this wave's 32 keys: lane holds row r16 and keys
@@ -446,7 +461,7 @@ void tree_attn_bf16_kernel(AttnArgs a) {
     // max m is raised only when some row's tile max exceeds it by more
     // than kSlack (a wave-uniform branch), so the O rescale is rare; the
     // weights are then bounded by 2^kSlack, harmless in fp32 and bf16.
-    const bool full = !tree && key0 + kAttnTile <= P;
+    const bool full = fast || (!tree && key0 + kAttnTile <= P);
     bf16x8_t pf[WR];
 #pragma unroll
     for (int w = 0; w < WR; ++w) {
@@ -507,15 +522,27 @@ void tree_attn_bf16_kernel(AttnArgs a) {
       lacc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[w], lacc[w], 0, 0, 0);
     }  // active
     // tile it+1 must have landed before the barrier; tile it+2 may fly on
-    if (PD > 1 && it + 2 < cnt) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * CH));
+    if (PD > 1 && (fast || it + 2 < cnt)) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * CH));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     barrier_no_fence();
   };
-  for (int it = 0; it < cnt; it += NB) {
-    tile_step(std::integral_constant<int, 0>{}, it);
-    if (it + 1 < cnt) tile_step(std::integral_constant<int, 1>{}, it + 1);
+  using fast_t = std::true_type;
+  using gen_t = std::false_type;
+  // Steps it < n_fast issue tile t_begin + it + PD below floor(P / 64):
+  // it and every tile before it are whole prefix tiles.
+  const int n_fast = FP ? max(0, min(cnt - PD, P / kAttnTile - t_begin - PD)) : 0;
+  int it = 0;
+  if constexpr (FP)
+  for (; it + NB <= n_fast; it += NB) {
+    tile_step(std::integral_constant<int, 0>{}, fast_t{}, it);
+    tile_step(std::integral_constant<int, 1>{}, fast_t{}, it + 1);
+    if constexpr (NB == 3) tile_step(std::integral_constant<int, NB - 1>{}, fast_t{}, it + 2);
+  }
+  for (; it < cnt; it += NB) {
+    tile_step(std::integral_constant<int, 0>{}, gen_t{}, it);
+    if (it + 1 < cnt) tile_step(std::integral_constant<int, 1>{}, gen_t{}, it + 1);
     if constexpr (NB == 3)
-      if (it + 2 < cnt) tile_step(std::integral_constant<int, NB - 1>{}, it + 2);
+      if (it + 2 < cnt) tile_step(std::integral_constant<int, NB - 1>{}, gen_t{}, it + 2);
   }
 
   // Combine the two key halves of every row group: the kh = 1 waves
@@ -816,20 +843,28 @@ hipError_t launch_tree_attention(const Plan& p, const AttnWs& w,
     if (e != hipSuccess) return e;
     a.order = w.order;
   }
-#define ET_ATTN(HD, WR)                                                          \
+  // FP (the separate loop for whole prefix tiles) when the keys are not
+  // split: a block then walks every tile of its unit.  Split blocks walk a
+  // few tiles each, and the smaller kernel leaves more of the instruction
+  // cache to the latency-bound kernels around it (batch 1: the last draft
+  // step's merge ran 0.4 us slower beside the larger code).
+#define ET_ATTN(HD, WR, FP)                                                      \
   do {                                                                           \
-    tree_attn_bf16_kernel<HD, WR, ET_ATTN_NB(WR)><<<blocks, 512, 0, s>>>(a);     \
+    tree_attn_bf16_kernel<HD, WR, ET_ATTN_NB(WR), FP><<<blocks, 512, 0, s>>>(a); \
     hipError_t e = hipGetLastError();                                            \
     if (e != hipSuccess || p.attn_splits == 1) return e;                         \
     tree_attn_merge_kernel<HD, WR>                                               \
         <<<units8 * p.attn_nqb * (64 * WR / (256 / (HD / 4))), 256, 0, s>>>(a);  \
   } while (0)
+  // (64 * 2-row blocks are planned only without key splits)
   if (p.HD == 128) {
-    if (p.attn_wr == 2) ET_ATTN(128, 2);
-    else ET_ATTN(128, 1);
+    if (p.attn_wr == 2) ET_ATTN(128, 2, true);
+    else if (p.attn_splits == 1) ET_ATTN(128, 1, true);
+    else ET_ATTN(128, 1, false);
   } else {
-    if (p.attn_wr == 2) ET_ATTN(64, 2);
-    else ET_ATTN(64, 1);
+    if (p.attn_wr == 2) ET_ATTN(64, 2, true);
+    else if (p.attn_splits == 1) ET_ATTN(64, 1, true);
+    else ET_ATTN(64, 1, false);
   }
 #undef ET_ATTN
   return hipGetLastError();
