@@ -636,11 +636,12 @@ __global__ __launch_bounds__(1024) void tree_attn_order_kernel(const int32_t* pr
 
 // Combine the S split partials: o = sum_i O_i 2^(m_i - m) / l.  A block
 // covers RPB rows of one (unit, row block); thread = (row, 4 columns).
-// Blocks map to XCDs like the main kernel, so the partials are read from
-// the L2 they were written to.  Every load of a thread is independent and
-// issued up front.
-template <int HD, int WR>
+// Blocks map to XCDs like the main kernel.  Every load of a thread is
+// independent and issued up front, for MS >= S splits (the smallest of 8,
+// 16 and 32 that holds S: a short kernel for the common split counts).
+template <int HD, int WR, int MS>
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a) {
+  static_assert(MS <= kAttnMaxSplits, "split bound");
   constexpr int TPR = HD / 4;     // threads per row
   constexpr int RPB = 256 / TPR;  // rows per block
   constexpr int BR = 64 * WR;
@@ -671,10 +672,10 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a) {
   const int slot = r / G, gg = r - slot * G;
   gmem_u16* orow = (gmem_u16*)u_out + (((int64_t)b * T + slot) * Hq + kvh * G + gg) * HD + col;
   const int64_t base = (int64_t)(unit * nqb + qb) * S;
-  float mi[kAttnMaxSplits], li[kAttnMaxSplits];
-  float4 oi[kAttnMaxSplits];
+  float mi[MS], li[MS];
+  float4 oi[MS];
 #pragma unroll
-  for (int i = 0; i < kAttnMaxSplits; ++i) {
+  for (int i = 0; i < MS; ++i) {
     mi[i] = -INFINITY;
     li[i] = 0.f;
     oi[i] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -688,11 +689,11 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a) {
   }
   float m = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kAttnMaxSplits; ++i) m = fmaxf(m, mi[i]);
+  for (int i = 0; i < MS; ++i) m = fmaxf(m, mi[i]);
   float l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int i = 0; i < kAttnMaxSplits; ++i) {
+  for (int i = 0; i < MS; ++i) {
     const float f = mi[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi[i] - m);
     l += li[i] * f;
     acc.x += oi[i].x * f;
@@ -853,8 +854,10 @@ hipError_t launch_tree_attention(const Plan& p, const AttnWs& w,
     tree_attn_bf16_kernel<HD, WR, ET_ATTN_NB(WR), FP><<<blocks, 512, 0, s>>>(a); \
     hipError_t e = hipGetLastError();                                            \
     if (e != hipSuccess || p.attn_splits == 1) return e;                         \
-    tree_attn_merge_kernel<HD, WR>                                               \
-        <<<units8 * p.attn_nqb * (64 * WR / (256 / (HD / 4))), 256, 0, s>>>(a);  \
+    const dim3 mg(units8 * p.attn_nqb * (64 * WR / (256 / (HD / 4))));           \
+    if (p.attn_splits <= 8) tree_attn_merge_kernel<HD, WR, 8><<<mg, 256, 0, s>>>(a);        \
+    else if (p.attn_splits <= 16) tree_attn_merge_kernel<HD, WR, 16><<<mg, 256, 0, s>>>(a); \
+    else tree_attn_merge_kernel<HD, WR, 32><<<mg, 256, 0, s>>>(a);               \
   } while (0)
   // (64 * 2-row blocks are planned only without key splits)
   if (p.HD == 128) {
