@@ -622,7 +622,7 @@ __global__ __launch_bounds__(1024) void draft_merge_fixed_kernel(DraftArgs a, Fi
 // the step).  The pool nodes of the earlier steps are loaded first, with
 // the merge's own loads (clamped to the readable capacity, dropped past
 // the pool size once it is known); the step's children come from LDS.
-template <bool BF16, int KST>
+template <bool BF16, int KST, int RP>
 __global__ __launch_bounds__(1024) void draft_merge_last_kernel(DraftArgs a, RerankOut o) {
   // The arguments of the merge's first loads, read with the pool's in one
   // round of scalar loads (the compiler would otherwise read them in two
@@ -634,11 +634,11 @@ __global__ __launch_bounds__(1024) void draft_merge_last_kernel(DraftArgs a, Rer
   const int b = blockIdx.x, tid = threadIdx.x, nt = 64 * a.k;  // (the launch has 64 k threads)
   __shared__ RerankLds L;
   const int64_t pb = (int64_t)b * a.cap;
-  const int rounds = (a.cap + nt - 1) / nt;  // <= kRerankPer (checked by the host)
-  int par[kRerankPer], dep[kRerankPer], tok[kRerankPer];
-  float cnf[kRerankPer], val[kRerankPer];
+  const int rounds = (a.cap + nt - 1) / nt;  // <= RP (chosen by the host)
+  int par[RP], dep[RP], tok[RP];
+  float cnf[RP], val[RP];
 #pragma unroll
-  for (int i = 0; i < kRerankPer; ++i) {
+  for (int i = 0; i < RP; ++i) {
     val[i] = cnf[i] = 0.f;
     par[i] = dep[i] = tok[i] = -1;
     if (i < rounds) {  // uniform
@@ -660,11 +660,11 @@ __global__ __launch_bounds__(1024) void draft_merge_last_kernel(DraftArgs a, Rer
   // from them is scheduled before the merge (each such use a wait for the
   // memory round trip ahead of the merge's own loads)
 #pragma unroll
-  for (int i = 0; i < kRerankPer; ++i)
+  for (int i = 0; i < RP; ++i)
     asm volatile("" : "+v"(val[i]), "+v"(dep[i]), "+v"(tok[i]), "+v"(par[i]), "+v"(cnf[i]));
-  uint64_t key[kRerankPer];
+  uint64_t key[RP];
 #pragma unroll
-  for (int i = 0; i < kRerankPer; ++i) {
+  for (int i = 0; i < RP; ++i) {
     const int idx = tid + nt * i;
     key[i] = 0;
     if (idx < lc.P0) {
@@ -677,7 +677,7 @@ __global__ __launch_bounds__(1024) void draft_merge_last_kernel(DraftArgs a, Rer
     }
   }
   const int P = lc.P0 + lc.n_new;
-  rerank_block<true>(o, L, b, nt, key, par, cnf, P < o.N ? P : o.N, root, pre);
+  rerank_block<true, RP>(o, L, b, nt, key, par, cnf, P < o.N ? P : o.N, root, pre);
 }
 
 // Keys staged per list: four when a row has 64 lists (its top k then
@@ -759,10 +759,16 @@ hipError_t launch_draft_step(const Plan& p, const DraftWs& w, int step,
 #define ET_MERGE(BF, K)                                                                  \
   do {                                                                                   \
     if (fixed) draft_merge_fixed_kernel<BF, K><<<p.B, 64 * p.k, 0, s>>>(a, *fixed);      \
-    else if (last) draft_merge_last_kernel<BF, K><<<p.B, 64 * p.k, 0, s>>>(a, *last);    \
+    else if (last && rp == 1) draft_merge_last_kernel<BF, K, 1><<<p.B, 64 * p.k, 0, s>>>(a, *last); \
+    else if (last && rp == 2) draft_merge_last_kernel<BF, K, 2><<<p.B, 64 * p.k, 0, s>>>(a, *last); \
+    else if (last) draft_merge_last_kernel<BF, K, 4><<<p.B, 64 * p.k, 0, s>>>(a, *last); \
     else draft_merge_kernel<BF, K><<<p.B, 64 * p.k, 0, s>>>(a);                          \
   } while (0)
   const int kst = merge_stage(a.parts);
+  // pool nodes per thread of the last merge (64 k threads): the fewest
+  // of 1, 2 and 4 that cover the capacity, which keeps its code short
+  const int rounds = (p.cap + 64 * p.k - 1) / (64 * p.k);
+  const int rp = rounds <= 1 ? 1 : rounds <= 2 ? 2 : 4;
   if (bf && kst == 4) ET_MERGE(true, 4);
   else if (bf) ET_MERGE(true, 8);
   else if (kst == 4) ET_MERGE(false, 4);

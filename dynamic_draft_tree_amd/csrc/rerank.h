@@ -75,7 +75,7 @@ __device__ __forceinline__ void suffix_pick(const uint32_t* hist, int need,
 }
 
 // The rerank of sequence b by a block of nt threads (nt a multiple of 64,
-// nt * kRerankPer >= every pool index).  Thread tid holds pool nodes
+// nt * RP >= every pool index, RP <= kRerankPer).  Thread tid holds pool nodes
 // tid + nt * i: their keys (0 for no node), parent pool indexes and conf.
 // Writes the kept tree (slot 0 the root token, slots 1..n in rank order,
 // pads) and, with MASK, each slot's ancestor mask, depth and position id
@@ -83,15 +83,15 @@ __device__ __forceinline__ void suffix_pick(const uint32_t* hist, int need,
 // LDS data only (lds_barrier: no wait for the block's global stores, such
 // as a merge's pool stores before it or the output stores before the
 // flatten).
-template <bool MASK>
+template <bool MASK, int RP>
 __device__ __forceinline__ void rerank_block(const RerankOut& o, RerankLds& L, int b, int nt,
-                                             const uint64_t (&key)[kRerankPer],
-                                             const int (&par)[kRerankPer],
-                                             const float (&cnf)[kRerankPer], int n, int root,
+                                             const uint64_t (&key)[RP], const int (&par)[RP],
+                                             const float (&cnf)[RP], int n, int root,
                                              int pre) {
+  static_assert(RP >= 1 && RP <= kRerankPer, "pool nodes per thread");
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < kRerankPer; ++i)
+  for (int i = 0; i < RP; ++i)
     if (tid + nt * i < kRerankMaxPool) L.slot[tid + nt * i] = -1;
   if (tid == 0) L.count = 0;
   uint64_t prefix = 0;  // chosen high key bits, right-aligned
@@ -103,7 +103,7 @@ __device__ __forceinline__ void rerank_block(const RerankOut& o, RerankLds& L, i
     lds_barrier();
     const int sh = shift - 8;
 #pragma unroll
-    for (int i = 0; i < kRerankPer; ++i) {
+    for (int i = 0; i < RP; ++i) {
       const bool in = key[i] != 0 && (level == 0 || (key[i] >> shift) == prefix);
       if (in) atomicAdd(&L.hist[(key[i] >> sh) & 0xFFu], 1u);
     }
@@ -129,7 +129,7 @@ __device__ __forceinline__ void rerank_block(const RerankOut& o, RerankLds& L, i
   const int64_t ob = (int64_t)b * o.T;
   if (n > 0) {
 #pragma unroll
-    for (int i = 0; i < kRerankPer; ++i)
+    for (int i = 0; i < RP; ++i)
       if (key[i] != 0 && key[i] >= T) L.cand[atomicAdd(&L.count, 1)] = key[i];
     lds_barrier();
     // g consecutive lanes rank one candidate, each counting every g-th key
@@ -149,7 +149,7 @@ __device__ __forceinline__ void rerank_block(const RerankOut& o, RerankLds& L, i
   // kept nodes: slot = rank + 1, written by the thread that holds the node
   // (token and value come back out of the key, which holds both exactly)
 #pragma unroll
-  for (int i = 0; i < kRerankPer; ++i) {
+  for (int i = 0; i < RP; ++i) {
     const int s = key[i] != 0 ? L.slot[tid + nt * i] : -1;
     if (s > 0) {
       const int ps = par[i] < 0 ? 0 : L.slot[par[i]];

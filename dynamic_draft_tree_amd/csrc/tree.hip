@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(RerankArgs a, Re
     const int idx = tid + kRerankThreads * i;
     key[i] = idx < P ? pool_key(val[i], dep[i], tok[i], idx) : 0;
   }
-  rerank_block<MASK>(o, L, b, kRerankThreads, key, par, cnf, n, root, pre);
+  rerank_block<MASK, kRerankPer>(o, L, b, kRerankThreads, key, par, cnf, n, root, pre);
 }
 
 RerankOut rerank_out(const Plan& p, int32_t* tokens, int32_t* parent_slot, float* conf,
