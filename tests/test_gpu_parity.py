@@ -112,6 +112,18 @@ VARIANTS = {
                               sharpness=tuple([2.5, 0.8] * 100), n_q_heads=8,
                               n_kv_heads=2, head_dim=128, prefix_cap=300,
                               prefix_range=(1, 300), qkv_dtype="bf16", seed=20),
+    # 64 sequences, four kv heads of 132 query rows: 768 blocks of 64 rows
+    # without key splits (more than the chip holds at once), so the
+    # attention kernel's waves rank the ragged prefixes themselves and the
+    # whole prefix tiles take their own loop (head_dim 64); prefixes 1..300
+    # cross every tile boundary case
+    "ragged_b64_hd64": TINY.with_(batch=64, vocab=3000, topk=4, depth=3,
+                                  budget_n=32, threshold=0.0,
+                                  logits_dtype="bf16",
+                                  sharpness=tuple([2.5, 0.8] * 32),
+                                  n_q_heads=16, n_kv_heads=4, head_dim=64,
+                                  prefix_cap=300, prefix_range=(1, 300),
+                                  qkv_dtype="bf16", seed=21),
     # 40 keys per slot row over 121 slots: eight rounds
     "accept_rows_bf16": TINY.with_(batch=1, vocab=150000, topk=6, depth=5,
                                    budget_n=120, threshold=0.0,
