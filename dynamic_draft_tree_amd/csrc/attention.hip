@@ -56,7 +56,8 @@ struct AttnArgs {
   const uint64_t* mask;
   const int32_t* n_kept;
   const int32_t* order;  // sequence of unit-sequence b0, or null (b = b0)
-  int rank_inline;       // no order array: each wave ranks the batch (B <= 64)
+  int rank_inline;       // no order array: each wave ranks the batch (B <= 64);
+                         // 1: keys below 2^20, 2: any keys, 0: off
   void* out;
   float* po;
   float* pm;
@@ -159,20 +160,20 @@ __device__ __forceinline__ bool attn_block_coords(int i, int units, int per_unit
 // The sequence of rank r (0-based) when a batch of B <= 64 sequences, one
 // per lane, is ordered by prefix length, longest first, ties by index: the
 // (r + 1)-th largest of the distinct keys length * 64 + 63 - index, found
-// bit by bit from the top with one ballot per bit (lengths below 2^26 keep
-// the order exact; whatever the lengths, the result is a lane below B,
-// since for r < B the (r + 1)-th largest key is one of theirs: unused
-// lanes hold 0 and the batch's keys end in 63 - index > 0 when B < 64).
+// bit by bit from the top with one ballot per bit.  NBITS: the keys'
+// width (20 when every prefix length is below 2^14, else 32).  Whatever
+// the lengths, the result is clamped to a lane below B.
+template <int NBITS>
 __device__ __forceinline__ int sequence_of_rank(const int32_t* prefix_len, int B, int r) {
   const int lane = threadIdx.x & 63;
   const uint32_t key = lane < B ? ((uint32_t)prefix_len[lane] << 6) | (uint32_t)(63 - lane) : 0u;
   uint32_t t = 0;
 #pragma unroll
-  for (int bit = 31; bit >= 0; --bit) {
+  for (int bit = NBITS - 1; bit >= 0; --bit) {
     const uint32_t cand = t | (1u << bit);
     if (__popcll(__ballot(key >= cand)) > r) t = cand;
   }
-  return 63 - (int)(t & 63u);
+  return min(63 - (int)(t & 63u), B - 1);
 }
 
 __device__ __forceinline__ void barrier_no_fence() {
@@ -217,7 +218,8 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   const int b0 = unit / nHkv, kvh = unit - b0 * nHkv;
   const int b = __builtin_amdgcn_readfirstlane(
       u_order ? ((const gmem_i32*)u_order)[b0]
-              : rank_inline ? sequence_of_rank(a.prefix_len, nB, b0) : b0);
+              : rank_inline == 1 ? sequence_of_rank<20>(a.prefix_len, nB, b0)
+              : rank_inline ? sequence_of_rank<32>(a.prefix_len, nB, b0) : b0);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int rg = wave & 3, kh = wave >> 2;  // row group, key half of a tile
   const int r16 = lane & 15, g = lane >> 4;
@@ -834,9 +836,10 @@ hipError_t launch_tree_attention(const Plan& p, const AttnWs& w,
   // maps units to sequences directly.)
   const int resident = 256 * (ET_ATTN_NB(p.attn_wr) == 2 ? 2 : 1);
   // Up to 64 sequences (lengths below 2^26) each wave ranks the batch
-  // itself, one sequence per lane, instead of a launch of its own.
+  // itself, one sequence per lane, instead of a launch of its own (over
+  // 20-bit keys when the lengths are below 2^14).
   if (p.B > 1 && p.B <= 64 && p.Pcap < (1 << 26) && p.attn_splits == 1 && blocks > resident) {
-    a.rank_inline = 1;
+    a.rank_inline = p.Pcap < (1 << 14) ? 1 : 2;
   } else if (p.B > 1 && p.B <= kAttnOrderMaxB && p.attn_splits == 1 && blocks > resident) {
     const int nt = p.B < 1024 ? (p.B + 63) / 64 * 64 : 1024;
     tree_attn_order_kernel<<<1, nt, 0, s>>>(prefix_len, p.B, w.order);
