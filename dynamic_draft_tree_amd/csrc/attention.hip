@@ -14,7 +14,9 @@
 //   each) and the unit's key tiles (prefix tiles, then tree tiles) into S
 //   contiguous splits; one block per (unit, row block, split).  Block i
 //   runs on XCD i % 8, so the launch maps every block of a unit to one XCD
-//   and the unit's K/V and split partials stay in that XCD's L2.  When the
+//   and the unit's row blocks share its K/V tiles through that XCD's L2
+//   (split partials do not stay there: the end of the launch writes them
+//   back, and the merge reads them from beyond the L2).  When the
 //   grid is larger than the chip holds at once, units are taken in order
 //   of their sequence's prefix length, longest first (up to 64 sequences
 //   each wave ranks the batch itself, above that a one-block kernel does),
@@ -27,9 +29,13 @@
 //   row-major V tile with the LDS transpose read (ds_read_b64_tr_b16: in
 //   each 16-lane group, lane j receives element j % 4 of the 8-byte words
 //   addressed by lanes j/4, 4+j/4, 8+j/4, 12+j/4), so no transposed copy
-//   of V is ever written.  K/V tiles are double-buffered in LDS with one
-//   barrier per tile; the next tile's global loads are in flight while the
-//   current one is computed.  Online softmax in fp32 registers with exp2
+//   of V is ever written.  K/V tiles are double- (128-row blocks: triple-)
+//   buffered in LDS with one barrier per tile; the next tiles' global loads
+//   are in flight while the current one is computed.  The tile loop runs
+//   one step per buffer per trip, so every LDS read is a fixed register
+//   plus an immediate offset, and without key splits the whole prefix
+//   tiles take a loop of their own, without masks or row clamping.
+//   Online softmax in fp32 registers with exp2
 //   and a pre-multiplied log2(e) scale; the ancestor bitmask word of a tree
 //   tile is tested per key in registers.  With S > 1 each split writes
 //   (O, m, l) partials and a merge kernel combines them.
