@@ -112,6 +112,20 @@ VARIANTS = {
                               sharpness=tuple([2.5, 0.8] * 100), n_q_heads=8,
                               n_kv_heads=2, head_dim=128, prefix_cap=300,
                               prefix_range=(1, 300), qkv_dtype="bf16", seed=20),
+    # one kv head of 68 query rows at batch 1: the keys are split up to the
+    # tile count, 24 splits (the merge built for 32) and 15 (for 16)
+    "split24_hd128": TINY.with_(batch=1, vocab=3000, topk=4, depth=3,
+                                budget_n=16, threshold=0.0, logits_dtype="bf16",
+                                sharpness=(2.5,), n_q_heads=4, n_kv_heads=1,
+                                head_dim=128, prefix_cap=1500,
+                                prefix_range=(1500, 1500), qkv_dtype="bf16",
+                                seed=22),
+    "split15_hd64": TINY.with_(batch=2, vocab=3000, topk=4, depth=3,
+                               budget_n=16, threshold=0.0, logits_dtype="bf16",
+                               sharpness=(2.5, 0.8), n_q_heads=4, n_kv_heads=1,
+                               head_dim=64, prefix_cap=900,
+                               prefix_range=(400, 900), qkv_dtype="bf16",
+                               seed=23),
     # 64 sequences, four kv heads of 132 query rows: 768 blocks of 64 rows
     # without key splits (more than the chip holds at once), so the
     # attention kernel's waves rank the ragged prefixes themselves and the
