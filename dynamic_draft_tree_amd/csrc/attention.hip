@@ -33,8 +33,8 @@
 //   buffered in LDS with one barrier per tile; the next tiles' global loads
 //   are in flight while the current one is computed.  The tile loop runs
 //   one step per buffer per trip, so every LDS read is a fixed register
-//   plus an immediate offset, and without key splits the whole prefix
-//   tiles take a loop of their own, without masks or row clamping.
+//   plus an immediate offset, and the whole prefix tiles take a loop of
+//   their own, without masks or row clamping.
 //   Online softmax in fp32 registers with exp2
 //   and a pre-multiplied log2(e) scale; the ancestor bitmask word of a tree
 //   tile is tested per key in registers.  With S > 1 each split writes
@@ -194,9 +194,7 @@ __device__ __forceinline__ void barrier_no_fence() {
 // NB LDS tile buffers, prefetch distance NB - 1.  NB = 2 halves the LDS
 // so that two blocks share a compute unit (four waves per SIMD, which hide
 // each other's LDS and matrix latencies) when the registers allow it.
-// FP: the steps whose tiles are whole prefix tiles run in a loop of their
-// own, without the mask, clamping and tree-or-prefix selects.
-template <int HD, int WR, int NB, bool FP>
+template <int HD, int WR, int NB>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NB == 2 ? 4 : 2)))
 void tree_attn_bf16_kernel(AttnArgs a) {
   constexpr int KSTEPS = HD / 32;  // 32-wide d steps of K . Q^T
@@ -538,9 +536,8 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   using gen_t = std::false_type;
   // Steps it < n_fast issue tile t_begin + it + PD below floor(P / 64):
   // it and every tile before it are whole prefix tiles.
-  const int n_fast = FP ? max(0, min(cnt - PD, P / kAttnTile - t_begin - PD)) : 0;
+  const int n_fast = max(0, min(cnt - PD, P / kAttnTile - t_begin - PD));
   int it = 0;
-  if constexpr (FP)
   for (; it + NB <= n_fast; it += NB) {
     tile_step(std::integral_constant<int, 0>{}, fast_t{}, it);
     tile_step(std::integral_constant<int, 1>{}, fast_t{}, it + 1);
@@ -853,14 +850,9 @@ hipError_t launch_tree_attention(const Plan& p, const AttnWs& w,
     if (e != hipSuccess) return e;
     a.order = w.order;
   }
-  // FP (the separate loop for whole prefix tiles) when the keys are not
-  // split: a block then walks every tile of its unit.  Split blocks walk a
-  // few tiles each, and the smaller kernel leaves more of the instruction
-  // cache to the latency-bound kernels around it (batch 1: the last draft
-  // step's merge ran 0.4 us slower beside the larger code).
-#define ET_ATTN(HD, WR, FP)                                                      \
+#define ET_ATTN(HD, WR)                                                          \
   do {                                                                           \
-    tree_attn_bf16_kernel<HD, WR, ET_ATTN_NB(WR), FP><<<blocks, 512, 0, s>>>(a); \
+    tree_attn_bf16_kernel<HD, WR, ET_ATTN_NB(WR)><<<blocks, 512, 0, s>>>(a);     \
     hipError_t e = hipGetLastError();                                            \
     if (e != hipSuccess || p.attn_splits == 1) return e;                         \
     const dim3 mg(units8 * p.attn_nqb * (64 * WR / (256 / (HD / 4))));           \
@@ -868,15 +860,12 @@ hipError_t launch_tree_attention(const Plan& p, const AttnWs& w,
     else if (p.attn_splits <= 16) tree_attn_merge_kernel<HD, WR, 16><<<mg, 256, 0, s>>>(a); \
     else tree_attn_merge_kernel<HD, WR, 32><<<mg, 256, 0, s>>>(a);               \
   } while (0)
-  // (64 * 2-row blocks are planned only without key splits)
   if (p.HD == 128) {
-    if (p.attn_wr == 2) ET_ATTN(128, 2, true);
-    else if (p.attn_splits == 1) ET_ATTN(128, 1, true);
-    else ET_ATTN(128, 1, false);
+    if (p.attn_wr == 2) ET_ATTN(128, 2);
+    else ET_ATTN(128, 1);
   } else {
-    if (p.attn_wr == 2) ET_ATTN(64, 2, true);
-    else if (p.attn_splits == 1) ET_ATTN(64, 1, true);
-    else ET_ATTN(64, 1, false);
+    if (p.attn_wr == 2) ET_ATTN(64, 2);
+    else ET_ATTN(64, 1);
   }
 #undef ET_ATTN
   return hipGetLastError();
